@@ -1,0 +1,174 @@
+"""Benchmark of the TDT loss forward+backward on one MI355X.
+
+One step = one call of the C ABI (row statistics, node weights, lattice, coefficients,
+gradient pass) over one batch of the Parakeet-size workload: B=4, T=200, U=40,
+V=8193 (blank 8192), durations {0..4}, bf16 logits read in place as the slice
+[..., :8193] of a [4, 200, 41, 8198] joint output, sigma 0.05, reduction mean_batch.
+Inputs are seeded synthetic data resident in HBM; several input/gradient buffer sets are
+rotated so that a step never finds the previous step's data in the 256 MB last-level
+cache.
+
+Prints one JSON line: value = algorithmic GB/s of the whole step (two reads of every
+valid lattice row and one write of every gradient row, V + D elements each), the
+roofline of the dominant kernel (the gradient pass, timed with HIP events recorded by
+the library between its kernels over the timed region), and the float64 CPU oracle
+timed on the host on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "TDT loss fwd+bwd ms and achieved HBM GB/s, B4 T200 U40 V8193 bf16"
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload id in tdt_inputs.CONFIGS")
+    ap.add_argument("--rotate", type=int, default=3, help="input/gradient buffer sets cycled over the steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", type=str, default=None,
+                    help="JSON with measured HBM bytes per launch of the gradient kernel (from rocprofv3 --pmc)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the loss shards by utterance with no exchange but a scalar all-reduce, not built here.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import tdt_transducer_loss_amd as tdt
+    from tdt_transducer_loss_amd import _native
+    from tdt_inputs import CONFIGS, algorithmic_bytes, config_case
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = config_case(args.config, device=dev)
+    cfg = CONFIGS[args.config]
+    B, Tm, U1, _ = case.joint.shape
+    V, D = case.V, case.D
+    elt = case.joint.element_size()
+    dtype_code = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[case.joint.dtype]
+    red = tdt.REDUCTIONS[case.reduction]
+
+    sets = []
+    for r in range(max(1, args.rotate)):
+        joint = case.joint if r == 0 else case.joint.clone()
+        tok, dur = joint[..., :V], joint[..., V:V + D]
+        g, gd = tdt.alloc_grads_like(tok, dur)
+        sets.append((joint, tok, dur, g, gd))
+    loss = torch.empty(B if red == 0 else 1, dtype=torch.float32, device=dev)
+    ws_bytes = tdt.workspace_size(B, Tm, U1, case.durations)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    labels, tl, ul = case.labels.contiguous(), case.logit_lengths.contiguous(), case.label_lengths.contiguous()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None):
+        _, tok, dur, g, gd = sets[i % len(sets)]
+        rc = _native.fwd_bwd_raw(
+            dtype_code, B, Tm, U1, V, tok.data_ptr(), list(tok.stride()[:3]), dur.data_ptr(),
+            list(dur.stride()[:3]), D, labels.data_ptr(), labels.stride(0), tl.data_ptr(), ul.data_ptr(),
+            case.durations, case.blank, case.sigma, red, loss.data_ptr(), g.data_ptr(), list(g.stride()[:3]),
+            gd.data_ptr(), list(gd.stride()[:3]), None, ws.data_ptr(), ws_bytes, stream.cuda_stream,
+            events=events)
+        if rc != 0:
+            raise RuntimeError(f"tdt_loss_fwd_bwd: {_native.status_string(rc)}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    for row in evs:  # materialise the HIP events on this stream before the timed region
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    handles = [[e.cuda_event for e in row] for row in evs]
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, handles[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    names = ["row_stats", "node_weights", "lattice", "coef", "grad"]
+    phase_ms = {n: 0.0 for n in names}
+    for row in evs:
+        for j, n in enumerate(names):
+            phase_ms[n] += row[j].elapsed_time(row[j + 1]) / K
+    kernel_sum_ms = sum(phase_ms.values())
+
+    alg = algorithmic_bytes(case)
+    value = alg / (ms_per_step * 1e-3) / 1e9
+    # dominant kernel: the gradient pass reads every valid row once and writes every row once
+    row_bytes = (V + D) * elt
+    valid = int((case.logit_lengths.cpu() * (case.label_lengths.cpu() + 1)).sum())
+    grad_bytes = valid * row_bytes + B * Tm * U1 * row_bytes
+    grad_ms = phase_ms["grad"]
+    achieved = grad_bytes / (grad_ms * 1e-3) / 1e9
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("grad_bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        c = case.to("cpu")
+        t = time.perf_counter()
+        oracle.run(c.tok, c.dur, c.labels, c.logit_lengths, c.label_lengths, c.durations, c.blank, c.sigma,
+                   c.reduction)
+        dt = time.perf_counter() - t
+        cpu = {"value": round(alg / dt / 1e9, 4), "unit": "GB/s", "ms": round(dt * 1e3, 1),
+               "cores": oracle.max_threads(), "kind": "oracle",
+               "sample": f"the full workload (B={B}) once, float64 loss and gradient, OpenMP"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {0: "f32", 1: "f16", 2: "bf16"}[dtype_code],
+        "data": "synthetic",
+        "config": {"workload": f"{cfg['name']}: B{B} T{Tm} U{U1 - 1} V{V} D{D} {case.joint.dtype} joint "
+                               f"[{B},{Tm},{U1},{case.joint.shape[3]}] read as slices, sigma {case.sigma}, "
+                               f"{case.reduction}",
+                   "global_batch": B, "seq_len": Tm, "labels": U1 - 1, "vocab": V,
+                   "algorithmic_bytes": alg, "buffer_sets": len(sets)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": "k_grad (gradient pass)", "kernel_ms": round(grad_ms, 4),
+                     "bytes_per_launch": grad_bytes},
+        "kernel_ms": {k: round(v, 4) for k, v in phase_ms.items()},
+        "kernel_sum_ms": round(kernel_sum_ms, 4),
+        "frac_of_peak_whole_step": round(value / PEAK_HBM_GBS, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,163 @@
+/*
+ * tdt_loss.h — C ABI of the MI355X (gfx950) Token-and-Duration Transducer loss.
+ *
+ * One call computes the TDT loss and its gradient with respect to the token logits and
+ * the duration logits of a joint network output, as described on the page
+ * "tdt-loss: add TDT loss kernel" (huggingface/kernels-community PR #882, comment
+ * "What's in it"): a log-softmax over the vocabulary of every lattice node, float64
+ * alpha/beta passes over the lattice with no limit of 1024 labels, one fused gradient
+ * pass for token and duration logits, fp32/fp16/bf16 logits read in place (slices of
+ * the joint output such as logits[..., :V] are not copied), and the reductions
+ * mean_volume, mean_batch, mean, sum and none.  Labels use -100 padding (page
+ * "Add TDT loss kernel", huggingface/transformers PR #46048, commit summary "Use -100
+ * label padding for training").  sigma is the logit under-normalisation of that page's
+ * review thread ("Should we also test for sigma != 0?").
+ *
+ * Definitions, for utterance b with T = logit_lengths[b] frames, U = label_lengths[b]
+ * labels y_1..y_U and lattice nodes n = (t, u), 0 <= t < T, 0 <= u <= U:
+ *   - a blank with duration d > 0 moves (t,u) -> (t+d,u) when t+d < T, and ends the
+ *     alignment when u == U and t+d == T;
+ *   - label y_{u+1} with any duration d (0 allowed) moves (t,u) -> (t+d,u+1) when
+ *     u < U and t+d < T;
+ *   - each move weighs log_softmax(h(n))[token] - sigma + log_softmax(g(n))[d's index],
+ *     where h(n) are the V token logits (blank included) and g(n) the D duration logits;
+ *   - loss_b = -log of the sum over alignments of exp(sum of move weights).
+ * Reductions with per-utterance gradient weights w_b:
+ *   none -> loss[b] = loss_b (w_b = 1);  sum -> sum_b loss_b (w_b = 1);
+ *   mean_batch -> sum_b loss_b / B;  mean -> (1/B) sum_b loss_b / max(U_b, 1);
+ *   mean_volume -> sum_b loss_b / max(sum_b U_b, 1).
+ * The gradient written is d(reduced loss)/d(logits) (for 'none': of sum_b loss_b),
+ * exactly 0 at padded nodes (t >= T or u > U), in the dtype of the logits, rounded to
+ * nearest even.
+ */
+#ifndef TDT_LOSS_H
+#define TDT_LOSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of the logits (and of the gradients, which use the same type). */
+typedef enum { TDT_DTYPE_F32 = 0, TDT_DTYPE_F16 = 1, TDT_DTYPE_BF16 = 2 } tdt_dtype_t;
+
+typedef enum {
+  TDT_REDUCTION_NONE = 0,
+  TDT_REDUCTION_SUM = 1,
+  TDT_REDUCTION_MEAN = 2,
+  TDT_REDUCTION_MEAN_BATCH = 3,
+  TDT_REDUCTION_MEAN_VOLUME = 4
+} tdt_reduction_t;
+
+/* Return codes (host-detectable errors; nothing is launched when one is returned). */
+#define TDT_OK 0
+#define TDT_ERR_INVALID_ARGUMENT (-1)  /* null pointer, bad size, bad enum, bad durations, bad blank, non-finite sigma */
+#define TDT_ERR_UNSUPPORTED_DTYPE (-2) /* dtype not one of tdt_dtype_t */
+#define TDT_ERR_BAD_STRIDE (-3)        /* pointer not aligned to the element size */
+#define TDT_ERR_WORKSPACE_TOO_SMALL (-4)
+#define TDT_ERR_UNSUPPORTED (-5)       /* a size beyond this library's limits (see below) */
+#define TDT_ERR_HIP (-6)               /* a HIP launch failed */
+
+/* Per-utterance status bits written to utt_status[b] (device memory, may be NULL).
+ * A data error makes that utterance's loss NaN and its gradient 0; other utterances
+ * are unaffected (the reduced loss becomes NaN).  An utterance with no alignment
+ * (e.g. T == 0, or durations {2} and odd T) gets loss +inf, gradient 0. */
+#define TDT_UTT_BAD_LOGIT_LENGTH 1 /* logit_lengths[b] outside [0, T_max] */
+#define TDT_UTT_BAD_LABEL_LENGTH 2 /* label_lengths[b] outside [0, U1_max - 1] */
+#define TDT_UTT_BAD_LABEL 4        /* a label y_1..y_U outside [0, V) */
+#define TDT_UTT_INFEASIBLE 8       /* no alignment exists */
+
+/* Limits of this build: 1 <= num_durations <= 16, duration values in [0, 16] with at
+ * least one > 0, U1_max <= 8192. */
+#define TDT_MAX_DURATIONS 16
+#define TDT_MAX_DURATION_VALUE 16
+#define TDT_MAX_U1 8192
+
+/*
+ * Workspace bytes needed by tdt_loss_fwd_bwd for these sizes.
+ *   B, T_max, U1_max: padded batch shape of the logits [B, T_max, U1_max, *].
+ *   durations[num_durations]: host array of the duration values.
+ * Writes the size to *bytes and returns TDT_OK, or a negative code for invalid sizes.
+ */
+int tdt_loss_workspace_size(int64_t B, int64_t T_max, int64_t U1_max, const int32_t* durations,
+                            int32_t num_durations, size_t* bytes);
+
+/*
+ * TDT loss forward and backward, stream-ordered on `stream` (a hipStream_t; NULL =
+ * the default stream).  The call only validates arguments on the host and enqueues
+ * kernels: it never synchronises, never allocates and keeps no pointer after it
+ * returns.  All pointers except `durations` and the three stride arrays are device
+ * pointers owned by the caller.
+ *
+ *   dtype            element type of logits, dur_logits, grad_logits, grad_dur_logits.
+ *   B, T_max, U1_max padded shape; U1_max = (maximum label count) + 1.
+ *   V                number of token classes, blank included.
+ *   logits           token logits [B, T_max, U1_max, V], element strides
+ *                    logits_strides[0..2] for the first three dims, unit stride in the
+ *                    last one (e.g. joint[..., :V] of a [B, T_max, U1_max, V + D] joint).
+ *   dur_logits       duration logits [B, T_max, U1_max, D], strides dur_strides[0..2],
+ *                    unit last stride (e.g. joint[..., V:]).  May alias `logits`' buffer.
+ *   labels           int64 [B, >= U1_max - 1], row stride labels_stride elements;
+ *                    entries at index >= label_lengths[b] (-100 padding) are never read.
+ *   logit_lengths    int64 [B] frames per utterance.
+ *   label_lengths    int64 [B] labels per utterance.
+ *   durations        host int32 [num_durations]: distinct duration values (see limits).
+ *   blank            blank id in [0, V).
+ *   sigma            logit under-normalisation, subtracted once per emission (finite).
+ *   reduction        tdt_reduction_t.
+ *   loss_out         float [B] for TDT_REDUCTION_NONE, else float [1].
+ *   grad_logits      gradient w.r.t. logits, same shape, strides grad_strides[0..2];
+ *                    NULL together with grad_dur_logits for a forward-only call.  Every
+ *                    element of the [B, T_max, U1_max, V] view is written (zeros in
+ *                    padding), so it may start uninitialised.  May share a buffer with
+ *                    grad_dur_logits (e.g. two slices of one joint gradient) but must
+ *                    not overlap the logits.
+ *   grad_dur_logits  gradient w.r.t. dur_logits [B, T_max, U1_max, D], strides
+ *                    grad_dur_strides[0..2].
+ *   utt_status       int32 [B] status bits, or NULL.
+ *   workspace        device scratch of at least tdt_loss_workspace_size() bytes,
+ *                    256-byte aligned; its contents need no initialisation and are
+ *                    overwritten.  Calls that share a workspace must not overlap.
+ * Returns TDT_OK or a negative TDT_ERR_* code.
+ */
+int tdt_loss_fwd_bwd(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,
+                     const void* logits, const int64_t* logits_strides, const void* dur_logits,
+                     const int64_t* dur_strides, int32_t num_durations, const int64_t* labels,
+                     int64_t labels_stride, const int64_t* logit_lengths, const int64_t* label_lengths,
+                     const int32_t* durations, int32_t blank, double sigma, int32_t reduction, float* loss_out,
+                     void* grad_logits, const int64_t* grad_strides, void* grad_dur_logits,
+                     const int64_t* grad_dur_strides, int32_t* utt_status, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * Same as tdt_loss_fwd_bwd, and additionally records caller-created events (hipEvent_t
+ * handles) on `stream` at the kernel boundaries, for profiling:
+ *   events[0] before the row-statistics kernel, events[1] after it, events[2] after the
+ *   node-weight kernel, events[3] after the lattice kernel, events[4] after the
+ *   coefficient kernel (or the loss reduction of a forward-only call), events[5] after
+ *   the gradient kernel.
+ * num_events must be 6; a NULL entry is skipped.  Intended for benchmarks and tools
+ * that attribute time per kernel (the events themselves cost a few microseconds).
+ */
+int tdt_loss_fwd_bwd_timed(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,
+                           const void* logits, const int64_t* logits_strides, const void* dur_logits,
+                           const int64_t* dur_strides, int32_t num_durations, const int64_t* labels,
+                           int64_t labels_stride, const int64_t* logit_lengths, const int64_t* label_lengths,
+                           const int32_t* durations, int32_t blank, double sigma, int32_t reduction,
+                           float* loss_out, void* grad_logits, const int64_t* grad_strides, void* grad_dur_logits,
+                           const int64_t* grad_dur_strides, int32_t* utt_status, void* workspace,
+                           size_t workspace_bytes, void* stream, void* const* events, int32_t num_events);
+
+/* Static string naming a return code. */
+const char* tdt_loss_status_string(int status);
+
+/* ABI version of this library (incremented on incompatible changes). */
+int tdt_loss_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TDT_LOSS_H */

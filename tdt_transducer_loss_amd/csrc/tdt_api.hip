@@ -1,0 +1,275 @@
+// Host side of the C ABI declared in include/tdt_loss.h: argument validation, workspace
+// layout and the stream-ordered launch sequence
+//   row statistics -> node weights -> lattice (alpha || beta) -> coefficients -> gradient.
+#include <math.h>
+#include <string.h>
+
+#include "tdt_kernels.h"
+#include "tdt_loss.h"
+
+namespace {
+
+using tdt::Params;
+
+struct Layout {
+  int KD, WP, DM, NW, NPR, RS;
+  size_t off_rstat, off_lse, off_pr, off_wm, off_we, off_am, off_ae, off_bm, off_be, off_rec;
+  size_t off_logp, off_logpa, off_wts, off_pm, off_pe, off_uok;
+  size_t total;
+};
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int pick_dm(int maxd) { return maxd <= 4 ? 4 : (maxd <= 8 ? 8 : 16); }
+
+// Validate the duration list and return its largest value (or a negative code).
+int check_durations(const int32_t* durations, int32_t D) {
+  if (!durations || D < 1) return TDT_ERR_INVALID_ARGUMENT;
+  if (D > TDT_MAX_DURATIONS) return TDT_ERR_UNSUPPORTED;
+  int maxd = -1;
+  bool any_pos = false;
+  for (int i = 0; i < D; ++i) {
+    const int d = durations[i];
+    if (d < 0) return TDT_ERR_INVALID_ARGUMENT;
+    if (d > TDT_MAX_DURATION_VALUE) return TDT_ERR_UNSUPPORTED;
+    for (int j = 0; j < i; ++j)
+      if (durations[j] == d) return TDT_ERR_INVALID_ARGUMENT;
+    any_pos |= d > 0;
+    maxd = d > maxd ? d : maxd;
+  }
+  return any_pos ? maxd : TDT_ERR_INVALID_ARGUMENT;
+}
+
+int make_layout(int64_t B, int64_t Tmax, int64_t U1max, int32_t D, int maxd, Layout* L) {
+  if (B < 1 || Tmax < 1 || U1max < 1) return TDT_ERR_INVALID_ARGUMENT;
+  if (U1max > TDT_MAX_U1) return TDT_ERR_UNSUPPORTED;
+  if (Tmax > (1 << 24)) return TDT_ERR_UNSUPPORTED;
+  L->KD = (int)(Tmax + U1max - 1);
+  L->WP = (int)(Tmax < U1max ? Tmax : U1max);
+  L->DM = pick_dm(maxd);
+  L->NW = 2 * L->DM + 1;
+  L->NPR = L->DM + 3;
+  L->RS = 5 + D;
+  const size_t NP = (size_t)B * (size_t)L->KD * (size_t)L->WP;
+  if (NP > ((size_t)1 << 40)) return TDT_ERR_UNSUPPORTED;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L->off_rstat = take(NP * 16);
+  L->off_lse = take(NP * 8);
+  L->off_pr = take(NP * (size_t)L->NPR * 8);
+  L->off_wm = take(NP * (size_t)L->NW * 8);
+  L->off_we = take(NP * (size_t)L->NW * 4);
+  L->off_am = take(NP * 8);
+  L->off_ae = take(NP * 4);
+  L->off_bm = take(NP * 8);
+  L->off_be = take(NP * 4);
+  L->off_rec = take(NP * (size_t)L->RS * 4);
+  L->off_logp = take((size_t)B * 8);
+  L->off_logpa = take((size_t)B * 8);
+  L->off_wts = take((size_t)B * 8);
+  L->off_pm = take((size_t)B * 8);
+  L->off_pe = take((size_t)B * 4);
+  L->off_uok = take((size_t)B * 4);
+  L->total = o;
+  return TDT_OK;
+}
+
+bool aligned_to(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+}  // namespace
+
+extern "C" int tdt_loss_abi_version(void) { return 1; }
+
+extern "C" const char* tdt_loss_status_string(int status) {
+  switch (status) {
+    case TDT_OK: return "ok";
+    case TDT_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case TDT_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case TDT_ERR_BAD_STRIDE: return "bad stride or misaligned pointer";
+    case TDT_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case TDT_ERR_UNSUPPORTED: return "size beyond the limits of this library";
+    case TDT_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int tdt_loss_workspace_size(int64_t B, int64_t T_max, int64_t U1_max, const int32_t* durations,
+                                       int32_t num_durations, size_t* bytes) {
+  if (!bytes) return TDT_ERR_INVALID_ARGUMENT;
+  const int maxd = check_durations(durations, num_durations);
+  if (maxd < 0) return maxd;
+  Layout L;
+  const int rc = make_layout(B, T_max, U1_max, num_durations, maxd, &L);
+  if (rc != TDT_OK) return rc;
+  *bytes = L.total;
+  return TDT_OK;
+}
+
+namespace {
+
+int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, const void* logits,
+                 const int64_t* logits_strides, const void* dur_logits, const int64_t* dur_strides,
+                 int32_t num_durations, const int64_t* labels, int64_t labels_stride, const int64_t* logit_lengths,
+                 const int64_t* label_lengths, const int32_t* durations, int32_t blank, double sigma,
+                 int32_t reduction, float* loss_out, void* grad_logits, const int64_t* grad_strides,
+                 void* grad_dur_logits, const int64_t* grad_dur_strides, int32_t* utt_status, void* workspace,
+                 size_t workspace_bytes, void* stream, void* const* events) {
+  if (dtype < 0 || dtype > 2) return TDT_ERR_UNSUPPORTED_DTYPE;
+  if (reduction < 0 || reduction > 4) return TDT_ERR_INVALID_ARGUMENT;
+  if (!logits || !logits_strides || !dur_logits || !dur_strides || !labels || !logit_lengths || !label_lengths ||
+      !loss_out || !workspace)
+    return TDT_ERR_INVALID_ARGUMENT;
+  if (V < 1 || V > (int64_t)1 << 30 || B > (int64_t)1 << 24) return V < 1 ? TDT_ERR_INVALID_ARGUMENT : TDT_ERR_UNSUPPORTED;
+  if (blank < 0 || blank >= V) return TDT_ERR_INVALID_ARGUMENT;
+  if (!isfinite(sigma)) return TDT_ERR_INVALID_ARGUMENT;
+  if (labels_stride < U1_max - 1) return TDT_ERR_BAD_STRIDE;
+  const bool grads = grad_logits != nullptr || grad_dur_logits != nullptr;
+  if (grads && (!grad_logits || !grad_dur_logits || !grad_strides || !grad_dur_strides))
+    return TDT_ERR_INVALID_ARGUMENT;
+  const int maxd = check_durations(durations, num_durations);
+  if (maxd < 0) return maxd;
+  Layout L;
+  int rc = make_layout(B, T_max, U1_max, num_durations, maxd, &L);
+  if (rc != TDT_OK) return rc;
+  if (workspace_bytes < L.total) return TDT_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned_to(workspace, 256)) return TDT_ERR_BAD_STRIDE;
+  const size_t elt = dtype == 0 ? 4 : 2;
+  if (!aligned_to(logits, elt) || !aligned_to(dur_logits, elt)) return TDT_ERR_BAD_STRIDE;
+  if (grads && (!aligned_to(grad_logits, elt) || !aligned_to(grad_dur_logits, elt))) return TDT_ERR_BAD_STRIDE;
+
+  Params p;
+  memset(&p, 0, sizeof p);
+  p.B = (int)B;
+  p.Tmax = (int)T_max;
+  p.U1max = (int)U1_max;
+  p.V = (int)V;
+  p.D = num_durations;
+  p.blank = blank;
+  p.red = reduction;
+  p.dtype = dtype;
+  p.KD = L.KD;
+  p.WP = L.WP;
+  p.DM = L.DM;
+  p.NW = L.NW;
+  p.NPR = L.NPR;
+  p.RS = L.RS;
+  p.sigma = sigma;
+  for (int d = 0; d <= tdt::kMaxDval; ++d) p.didx[d] = -1;
+  for (int i = 0; i < num_durations; ++i) {
+    p.dval[i] = durations[i];
+    p.didx[durations[i]] = i;
+  }
+  p.tok = logits;
+  p.ts0 = logits_strides[0];
+  p.ts1 = logits_strides[1];
+  p.ts2 = logits_strides[2];
+  p.dur = dur_logits;
+  p.ds0 = dur_strides[0];
+  p.ds1 = dur_strides[1];
+  p.ds2 = dur_strides[2];
+  p.labels = labels;
+  p.lab_stride = labels_stride;
+  p.Tlen = logit_lengths;
+  p.Ulen = label_lengths;
+  p.loss = loss_out;
+  p.ustatus = utt_status;
+  if (grads) {
+    p.gtok = grad_logits;
+    p.gs0 = grad_strides[0];
+    p.gs1 = grad_strides[1];
+    p.gs2 = grad_strides[2];
+    p.gdur = grad_dur_logits;
+    p.gds0 = grad_dur_strides[0];
+    p.gds1 = grad_dur_strides[1];
+    p.gds2 = grad_dur_strides[2];
+  }
+  char* ws = (char*)workspace;
+  p.rstat = (float4*)(ws + L.off_rstat);
+  p.lse = (double*)(ws + L.off_lse);
+  p.pr = (double*)(ws + L.off_pr);
+  p.wm = (double*)(ws + L.off_wm);
+  p.we = (int*)(ws + L.off_we);
+  p.am = (double*)(ws + L.off_am);
+  p.ae = (int*)(ws + L.off_ae);
+  p.bm = (double*)(ws + L.off_bm);
+  p.be = (int*)(ws + L.off_be);
+  p.rec = (float*)(ws + L.off_rec);
+  p.logp = (double*)(ws + L.off_logp);
+  p.logpa = (double*)(ws + L.off_logpa);
+  p.wts = (double*)(ws + L.off_wts);
+  p.pm = (double*)(ws + L.off_pm);
+  p.pe = (int*)(ws + L.off_pe);
+  p.uok = (int*)(ws + L.off_uok);
+
+  // Row and gradient chunks coincide when the logits and gradient rows share their
+  // address modulo 16 bytes for every node.
+  bool aligned = false;
+  if (grads) {
+    const int64_t e = (int64_t)elt;
+    aligned = ((uintptr_t)logits % 16) == ((uintptr_t)grad_logits % 16);
+    for (int d = 0; d < 3; ++d) aligned = aligned && (((logits_strides[d] - grad_strides[d]) * e) % 16 == 0);
+  }
+
+  hipStream_t st = (hipStream_t)stream;
+  auto mark = [&](int i) {
+    if (events && events[i]) (void)hipEventRecord((hipEvent_t)events[i], st);
+  };
+  auto rows = [&](int which) {
+    return dtype == 0 ? tdt::launch_rows_f32(p, aligned, st, which)
+                      : (dtype == 1 ? tdt::launch_rows_f16(p, aligned, st, which) : tdt::launch_rows_bf16(p, aligned, st, which));
+  };
+  mark(0);
+  if (rows(0) != hipSuccess) return TDT_ERR_HIP;
+  mark(1);
+  if (tdt::launch_lattice_side(p, 0, st) != hipSuccess) return TDT_ERR_HIP;
+  mark(2);
+  if (tdt::launch_lattice_side(p, 1, st) != hipSuccess) return TDT_ERR_HIP;
+  mark(3);
+  if (grads) {
+    if (tdt::launch_lattice_side(p, 2, st) != hipSuccess) return TDT_ERR_HIP;
+    mark(4);
+    if (rows(1) != hipSuccess) return TDT_ERR_HIP;
+  } else {
+    if (tdt::launch_lattice_side(p, 3, st) != hipSuccess) return TDT_ERR_HIP;
+    mark(4);
+  }
+  mark(5);
+  return TDT_OK;
+}
+
+}  // namespace
+
+extern "C" int tdt_loss_fwd_bwd(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,
+                                const void* logits, const int64_t* logits_strides, const void* dur_logits,
+                                const int64_t* dur_strides, int32_t num_durations, const int64_t* labels,
+                                int64_t labels_stride, const int64_t* logit_lengths, const int64_t* label_lengths,
+                                const int32_t* durations, int32_t blank, double sigma, int32_t reduction,
+                                float* loss_out, void* grad_logits, const int64_t* grad_strides,
+                                void* grad_dur_logits, const int64_t* grad_dur_strides, int32_t* utt_status,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_bwd_impl(dtype, B, T_max, U1_max, V, logits, logits_strides, dur_logits, dur_strides, num_durations,
+                      labels, labels_stride, logit_lengths, label_lengths, durations, blank, sigma, reduction,
+                      loss_out, grad_logits, grad_strides, grad_dur_logits, grad_dur_strides, utt_status, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
+extern "C" int tdt_loss_fwd_bwd_timed(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,
+                                      const void* logits, const int64_t* logits_strides, const void* dur_logits,
+                                      const int64_t* dur_strides, int32_t num_durations, const int64_t* labels,
+                                      int64_t labels_stride, const int64_t* logit_lengths,
+                                      const int64_t* label_lengths, const int32_t* durations, int32_t blank,
+                                      double sigma, int32_t reduction, float* loss_out, void* grad_logits,
+                                      const int64_t* grad_strides, void* grad_dur_logits,
+                                      const int64_t* grad_dur_strides, int32_t* utt_status, void* workspace,
+                                      size_t workspace_bytes, void* stream, void* const* events,
+                                      int32_t num_events) {
+  if (!events || num_events != 6) return TDT_ERR_INVALID_ARGUMENT;
+  return fwd_bwd_impl(dtype, B, T_max, U1_max, V, logits, logits_strides, dur_logits, dur_strides, num_durations,
+                      labels, labels_stride, logit_lengths, label_lengths, durations, blank, sigma, reduction,
+                      loss_out, grad_logits, grad_strides, grad_dur_logits, grad_dur_strides, utt_status, workspace,
+                      workspace_bytes, stream, events);
+}

@@ -1,0 +1,261 @@
+// Shared definitions of the gfx950 TDT loss kernels: launch parameters, the workspace
+// layout, extended-range float64 arithmetic and element-type traits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tdt {
+
+constexpr int kWave = 64;
+constexpr int kMaxD = 16;      // durations per call
+constexpr int kMaxDval = 16;   // largest duration value
+constexpr int kEZ = -(1 << 28);  // exponent of the extended-range zero
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLn2 = 0.6931471805599453094;
+constexpr double kLn2Hi = 6.93147180369123816490e-01;  // ln2 with 32 trailing zero bits
+constexpr double kLn2Lo = 1.90821492927058770002e-10;
+constexpr double kLog2eD = 1.4426950408889634074;
+
+// Everything the kernels of one call need, passed by value.
+//
+// Workspace layout.  Per utterance b the lattice nodes are stored by anti-diagonal:
+// position (b, k, i) with k = t + u in [0, KD) and i = u - ulo(k) in [0, WP), where
+// ulo(k) = max(0, k - T + 1).  pos = (b*KD + k)*WP + i.  Transition weights use
+// [b][k][slot][i]: slot d-1 (d = 1..DM) is the blank move of duration d, slot DM + d
+// (d = 0..DM) the label move of duration d; absent durations hold the zero value.
+struct Params {
+  int B, Tmax, U1max, V, D, blank, red, dtype;
+  int KD, WP, DM, NW, NPR, RS;
+  double sigma;
+  int dval[kMaxD];          // duration value of index i
+  int didx[kMaxDval + 1];   // index of duration value d, -1 when absent
+  // inputs (element strides of the first three dims; last dim contiguous)
+  const void* tok;
+  int64_t ts0, ts1, ts2;
+  const void* dur;
+  int64_t ds0, ds1, ds2;
+  const int64_t* labels;
+  int64_t lab_stride;
+  const int64_t* Tlen;
+  const int64_t* Ulen;
+  // outputs
+  float* loss;
+  int32_t* ustatus;
+  void* gtok;
+  int64_t gs0, gs1, gs2;
+  void* gdur;
+  int64_t gds0, gds1, gds2;
+  // workspace, per position
+  float4* rstat;  // {mL, K, h_blank, h_label}: mL = f32(rowmax * log2e), K = log2 sum 2^(x log2e - mL)
+  double* lse;    // natural-log normaliser of the token logits
+  double* pr;     // [NPR]: softmax(h)_blank, softmax(h)_label, softmax(g) by duration value 0..DM
+  double* wm;     // transition weight mantissas [B][KD][NW][WP]
+  int* we;        // transition weight exponents
+  double* am;     // alpha (extended range)
+  int* ae;
+  double* bm;     // beta
+  int* be;
+  float* rec;     // [RS] per-node record of the gradient pass
+  // workspace, per utterance
+  double* logp;   // log P from beta(0,0)
+  double* logpa;  // log P from the alpha terminal (diagnostic)
+  double* wts;    // reduction weight w_b
+  double* pm;     // P as mantissa / exponent
+  int* pe;
+  int* uok;       // 1: gradients are written from the lattice, 0: zeros
+};
+
+// ---- extended-range non-negative numbers: value = m * 2^e ----
+struct Ext {
+  double m;
+  int e;
+};
+
+__device__ __forceinline__ Ext ext_zero() { return Ext{0.0, kEZ}; }
+__device__ __forceinline__ Ext ext_one() { return Ext{0.5, 1}; }
+__device__ __forceinline__ Ext ext_mul(Ext a, Ext b) { return Ext{a.m * b.m, a.e + b.e}; }
+
+// Normalise a sum s * 2^E to a mantissa in [0.5, 1).
+__device__ __forceinline__ Ext ext_norm(double s, int E) {
+  if (s == 0.0) return ext_zero();
+  int ex;
+  double m = frexp(s, &ex);  // v_frexp_mant_f64 / v_frexp_exp_i32_f64
+  return Ext{m, E + ex};
+}
+
+// exp(x) in extended range, accurate to a few ulp of float64.
+__device__ __forceinline__ Ext ext_exp(double x) {
+  if (!(x > -1.0e300)) {  // -inf (or a huge negative value): zero; NaN propagates below
+    if (x != x) return Ext{x, 0};
+    return ext_zero();
+  }
+  double kf = floor(x * kLog2eD);
+  if (kf > 1.0e9) return Ext{__builtin_inf(), 0};
+  int k = (int)kf;
+  double r = fma(-kf, kLn2Hi, x);
+  r = fma(-kf, kLn2Lo, r);
+  return Ext{exp(r), k};
+}
+
+__device__ __forceinline__ double ext_log(Ext a) {
+  if (a.m == 0.0) return -__builtin_inf();
+  return log(a.m) + (double)a.e * kLn2;
+}
+
+__device__ __forceinline__ double ext_to_double(Ext a) {
+  if (a.m == 0.0) return 0.0;
+  int e = a.e;
+  e = e < -2100 ? -2100 : (e > 2100 ? 2100 : e);
+  return ldexp(a.m, e);
+}
+
+// Sum of N extended values: align to the largest exponent, add, renormalise.
+template <int N>
+__device__ __forceinline__ Ext ext_sum(const Ext (&t)[N]) {
+  int E = t[0].e;
+#pragma unroll
+  for (int i = 1; i < N; ++i) E = max(E, t[i].e);
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) s += ldexp(t[i].m, t[i].e - E);
+  return ext_norm(s, E);
+}
+
+// ---- lattice layout ----
+__device__ __forceinline__ int diag_ulo(int k, int T) { return max(0, k - T + 1); }
+
+__device__ __forceinline__ int64_t node_pos(const Params& p, int b, int k, int i) {
+  return ((int64_t)b * p.KD + k) * p.WP + i;
+}
+
+__device__ __forceinline__ int64_t w_index(const Params& p, int b, int k, int slot, int i) {
+  return (((int64_t)b * p.KD + k) * p.NW + slot) * p.WP + i;
+}
+
+__device__ __forceinline__ bool utt_dims_ok(const Params& p, int64_t T, int64_t U) {
+  return T >= 0 && T <= p.Tmax && U >= 0 && U <= p.U1max - 1;
+}
+
+// Work-groups are handed to the 8 XCDs round-robin; remap so that consecutive logical
+// blocks (neighbouring lattice positions) share an XCD and its L2.
+__device__ __forceinline__ uint32_t xcd_block(uint32_t g, uint32_t G) {
+  constexpr uint32_t nx = 8;
+  uint32_t q = G / nx, r = G % nx, x = g % nx, idx = g / nx;
+  return x < r ? x * (q + 1) + idx : r * (q + 1) + (x - r) * q + idx;
+}
+
+// ---- element types ----
+struct F32 {
+  using T = float;
+  static constexpr int kEpc = 4;  // elements per 16-byte chunk
+  static constexpr uint32_t kNegInf = 0xff800000u;
+  __device__ static __forceinline__ float load(const void* p, int64_t i) { return ((const float*)p)[i]; }
+  __device__ static __forceinline__ void store(void* p, int64_t i, float v) { ((float*)p)[i] = v; }
+  __device__ static __forceinline__ float get(const uint4& c, int s) {
+    uint32_t w = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
+    return __uint_as_float(w);
+  }
+  // element s of a chunk, s a compile-time constant after unrolling
+  template <int S>
+  __device__ static __forceinline__ float at(const uint4& c) {
+    return __uint_as_float(S == 0 ? c.x : S == 1 ? c.y : S == 2 ? c.z : c.w);
+  }
+  __device__ static __forceinline__ uint32_t bits(float v) { return __float_as_uint(v); }
+  __device__ static __forceinline__ uint4 pack(const float (&v)[4]) {
+    return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+  }
+};
+
+struct BF16 {
+  using T = uint16_t;
+  static constexpr int kEpc = 8;
+  static constexpr uint32_t kNegInf = 0xff80u;
+  __device__ static __forceinline__ float load(const void* p, int64_t i) {
+    return __uint_as_float(((uint32_t)((const uint16_t*)p)[i]) << 16);
+  }
+  __device__ static __forceinline__ uint32_t bits(float v) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);  // round to nearest even
+  }
+  __device__ static __forceinline__ void store(void* p, int64_t i, float v) { ((uint16_t*)p)[i] = (uint16_t)bits(v); }
+  __device__ static __forceinline__ float get(const uint4& c, int s) {
+    uint32_t w = (s >> 1) == 0 ? c.x : (s >> 1) == 1 ? c.y : (s >> 1) == 2 ? c.z : c.w;
+    return __uint_as_float((s & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  template <int S>
+  __device__ static __forceinline__ float at(const uint4& c) {
+    uint32_t w = (S >> 1) == 0 ? c.x : (S >> 1) == 1 ? c.y : (S >> 1) == 2 ? c.z : c.w;
+    return __uint_as_float((S & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    f2 in = {lo, hi};
+    bf2 out = __builtin_convertvector(in, bf2);  // v_cvt_pk_bf16_f32, round to nearest even
+    return __builtin_bit_cast(uint32_t, out);
+  }
+  __device__ static __forceinline__ uint4 pack(const float (&v)[8]) {
+    return make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
+  }
+};
+
+struct F16 {
+  using T = uint16_t;
+  static constexpr int kEpc = 8;
+  static constexpr uint32_t kNegInf = 0xfc00u;
+  __device__ static __forceinline__ float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+  __device__ static __forceinline__ float load(const void* p, int64_t i) { return h2f(((const uint16_t*)p)[i]); }
+  __device__ static __forceinline__ uint32_t bits(float v) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);  // round to nearest even
+  }
+  __device__ static __forceinline__ void store(void* p, int64_t i, float v) { ((uint16_t*)p)[i] = (uint16_t)bits(v); }
+  __device__ static __forceinline__ float get(const uint4& c, int s) {
+    uint32_t w = (s >> 1) == 0 ? c.x : (s >> 1) == 1 ? c.y : (s >> 1) == 2 ? c.z : c.w;
+    return h2f((s & 1) ? (w >> 16) : (w & 0xffffu));
+  }
+  template <int S>
+  __device__ static __forceinline__ float at(const uint4& c) {
+    uint32_t w = (S >> 1) == 0 ? c.x : (S >> 1) == 1 ? c.y : (S >> 1) == 2 ? c.z : c.w;
+    return h2f((S & 1) ? (w >> 16) : (w & 0xffffu));
+  }
+  __device__ static __forceinline__ uint32_t pack2(float lo, float hi) { return bits(lo) | (bits(hi) << 16); }
+  __device__ static __forceinline__ uint4 pack(const float (&v)[8]) {
+    return make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
+  }
+};
+
+// Replace element s of a chunk by the pattern `bitsv` (element width from TI).
+template <typename TI>
+__device__ __forceinline__ void chunk_set(uint4& c, int s, uint32_t bitsv) {
+  if (TI::kEpc == 4) {
+    if (s == 0) c.x = bitsv;
+    else if (s == 1) c.y = bitsv;
+    else if (s == 2) c.z = bitsv;
+    else c.w = bitsv;
+  } else {
+    const int w = s >> 1;
+    const uint32_t sh = (s & 1) ? 16u : 0u;
+    const uint32_t keep = ~(0xffffu << sh);
+    const uint32_t put = (bitsv & 0xffffu) << sh;
+    if (w == 0) c.x = (c.x & keep) | put;
+    else if (w == 1) c.y = (c.y & keep) | put;
+    else if (w == 2) c.z = (c.z & keep) | put;
+    else c.w = (c.w & keep) | put;
+  }
+}
+
+// ---- wave reductions (64 lanes) ----
+__device__ __forceinline__ float wave_max_f32(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+}  // namespace tdt

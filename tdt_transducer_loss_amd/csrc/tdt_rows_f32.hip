@@ -1,0 +1,9 @@
+// Row kernels of the TDT loss instantiated for f32 logits.
+#include "tdt_kernels.h"
+#include "tdt_rows.h"
+
+namespace tdt {
+hipError_t launch_rows_f32(const Params& p, bool aligned, hipStream_t st, int which) {
+  return launch_rows_t<F32>(p, aligned, st, which);
+}
+}  // namespace tdt

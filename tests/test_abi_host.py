@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every
+function include/tdt_loss.h declares, and rejects invalid arguments with the documented
+codes before it launches anything (every call below is invalid on purpose, so nothing
+reaches the device even on a GPU machine)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tdt_transducer_loss_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(tdt_\w+)\s*\(", src, flags=re.M))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"tdt_loss_fwd_bwd", "tdt_loss_workspace_size", "tdt_loss_status_string",
+            "tdt_loss_abi_version", "tdt_loss_fwd_bwd_timed"} <= names
+    lib = _native.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(_native.SIGNATURES) == names
+
+
+def test_status_strings():
+    for code in range(0, -7, -1):
+        assert _native.status_string(code) != "unknown status"
+    assert _native.status_string(-99) == "unknown status"
+    assert _native.lib().tdt_loss_abi_version() == 1
+
+
+def test_workspace_size():
+    small = _native.workspace_size(1, 10, 5, [0, 1, 2])
+    big = _native.workspace_size(4, 200, 41, [0, 1, 2, 3, 4])
+    assert 0 < small < big
+    assert big % 256 == 0
+    for bad in ([], [0], [1, 1], [-1, 1], [0, 17]):
+        with pytest.raises(ValueError):
+            _native.workspace_size(1, 10, 5, bad)
+    with pytest.raises(ValueError):
+        _native.workspace_size(1, 10, 8193, [0, 1])
+    with pytest.raises(ValueError):
+        _native.workspace_size(0, 10, 5, [0, 1])
+
+
+FAKE = 1 << 20  # a 256-aligned non-null address that is never dereferenced
+
+
+def _call(**over):
+    args = dict(dtype=2, B=2, T_max=10, U1_max=5, V=9, logits=FAKE, lstr=[450, 45, 9], dur=FAKE + 4096,
+                dstr=[450, 45, 9], D=3, labels=FAKE, lab_stride=4, tlen=FAKE, ulen=FAKE, durations=[0, 1, 2],
+                blank=8, sigma=0.0, reduction=3, loss=FAKE, glog=None, gstr=None, gdur=None, gdstr=None,
+                status=None, ws=FAKE, ws_bytes=0, stream=None)
+    args.update(over)
+    return _native.fwd_bwd_raw(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=3), _native.TDT_ERR_UNSUPPORTED_DTYPE),
+    (dict(dtype=-1), _native.TDT_ERR_UNSUPPORTED_DTYPE),
+    (dict(reduction=5), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(logits=None), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(loss=None), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(blank=9), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(blank=-1), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(sigma=float("nan")), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(sigma=float("inf")), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(V=0), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(durations=[0, 0, 1]), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(durations=[0], D=1), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(durations=[0, 1, 99]), _native.TDT_ERR_UNSUPPORTED),
+    (dict(U1_max=9000, lab_stride=9000), _native.TDT_ERR_UNSUPPORTED),
+    (dict(lab_stride=2), _native.TDT_ERR_BAD_STRIDE),
+    (dict(glog=FAKE), _native.TDT_ERR_INVALID_ARGUMENT),  # one gradient pointer without the other
+    (dict(), _native.TDT_ERR_WORKSPACE_TOO_SMALL),          # ws_bytes = 0
+    (dict(ws_bytes=1 << 40, logits=FAKE + 1), _native.TDT_ERR_BAD_STRIDE),
+    (dict(ws_bytes=1 << 40, ws=FAKE + 8), _native.TDT_ERR_BAD_STRIDE),
+])
+def test_invalid_arguments_are_rejected(over, code):
+    assert _call(**over) == code
+
+
+def test_timed_entry_needs_six_events():
+    lib = _native.lib()
+    i64 = _native.i64_array
+    rc = lib.tdt_loss_fwd_bwd_timed(2, 2, 10, 5, 9, FAKE, i64([1, 1, 1]), FAKE, i64([1, 1, 1]), 3, FAKE, 4, FAKE,
+                                    FAKE, _native.i32_array([0, 1, 2]), 8, 0.0, 3, FAKE, None, None, None, None,
+                                    None, FAKE, ctypes.c_size_t(1 << 40), None, None, 6)
+    assert rc == _native.TDT_ERR_INVALID_ARGUMENT

@@ -1,0 +1,154 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on identical
+seeded inputs.  Tolerances: fp32 logits loss rel <= 1e-6 and gradient max-abs <= 1e-6;
+fp16/bf16 logits loss rel <= 1e-3 and gradient max-abs <= 2e-3."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import tdt_transducer_loss_amd as tdt
+from parity_util import TOL, check_grads, check_loss, gpu_run, oracle_run, say
+from tdt_inputs import config_case, make_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_parity(case, reduction=None):
+    red = reduction or case.reduction
+    loss, gt, gd, st = gpu_run(case, reduction=red)
+    orc = oracle_run(case.to("cpu"), reduction=red)
+    check_loss(loss, orc, red, case.joint.dtype)
+    check_grads(gt, gd, orc, case.joint.dtype)
+    np.testing.assert_array_equal(st.cpu().numpy(), orc["status"])
+    return loss, gt, gd, orc
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_config_full_parity(cfg):
+    """Workloads 0-3 at their full sizes; every loss and every gradient element."""
+    case = config_case(cfg, device="cuda")
+    _full_parity(case)
+
+
+def test_long_label_config_sampled():
+    """Workload 4 (B=2, T=1000, U=1500, V=1025, durations 0..8, bf16): full loss, and the
+    gradient rows of 1500 sampled nodes plus every corner node, against the oracle."""
+    case = config_case(4, device="cuda")
+    loss, gt, gd, st = gpu_run(case)
+    cpu = case.to("cpu")
+    B, Tm, U1 = case.joint.shape[:3]
+    rng = np.random.default_rng(4)
+    rows = set(int(x) for x in rng.integers(0, B * Tm * U1, 1500))
+    for b in range(B):
+        for t in (0, 1, Tm - 2, Tm - 1):
+            for u in (0, 1, U1 - 2, U1 - 1):
+                rows.add((b * Tm + t) * U1 + u)
+    rows = np.array(sorted(rows), dtype=np.int64)
+    say(f"    oracle on {len(rows)} sampled rows")
+    orc = oracle_run(cpu, grads=False, rows=rows)
+    check_loss(loss, orc, case.reduction, case.joint.dtype)
+    idx = torch.from_numpy(rows).to("cuda")
+    g_rows = gt.reshape(-1, case.V).index_select(0, idx).double().cpu().numpy()
+    gd_rows = gd.reshape(-1, case.D).index_select(0, idx).double().cpu().numpy()
+    _, tg = TOL[case.joint.dtype]
+    e1 = float(np.abs(g_rows - orc["rows_tok"]).max())
+    e2 = float(np.abs(gd_rows - orc["rows_dur"]).max())
+    say(f"    sampled grad max-abs: token {e1:.3e} duration {e2:.3e}")
+    assert e1 <= tg and e2 <= tg
+    # zero-sum rows hold at any size
+    zs = gt.reshape(-1, case.V).index_select(0, idx).double().sum(-1).abs().max().item()
+    assert zs <= 0.05
+
+
+EDGE = {
+    "no_labels": lambda: make_case(3, [7, 5, 9], [0, 0, 0], 11, [0, 1, 2, 3, 4], "f32", seed=41, sigma=0.1,
+                                   reduction="sum", U1max=2),
+    "single_frame": lambda: make_case(2, [1, 2], [0, 1], 6, [0, 1, 2], "f32", seed=42, reduction="none"),
+    "blank_first_label_is_blank": lambda: make_case(2, [9, 6], [4, 2], 13, [0, 1, 2, 3], "f32", seed=43,
+                                                    reduction="none", blank=0, label_high=13),
+    "durations_unsorted_no_zero": lambda: make_case(2, [11, 8], [3, 3], 9, [3, 1, 2], "bf16", seed=44,
+                                                    reduction="mean", sigma=-0.2),
+    "single_duration_1": lambda: make_case(2, [10, 7], [4, 6], 9, [1], "f16", seed=45, reduction="mean_batch"),
+    "more_labels_than_frames": lambda: make_case(2, [6, 4], [12, 9], 17, [0, 1, 2], "f32", seed=46,
+                                                 reduction="mean_volume"),
+    "max_duration_16": lambda: make_case(2, [40, 33], [7, 5], 10, [0, 1, 5, 16, 9], "f32", seed=47,
+                                         reduction="sum", sigma=0.05),
+    "duration_8_multiwave": lambda: make_case(1, [30], [300], 21, list(range(9)), "bf16", seed=48,
+                                              reduction="sum"),
+    "lattice_r2_multiwave": lambda: make_case(1, [12], [1100], 7, [0, 1, 2], "f32", seed=49, reduction="sum"),
+    "wide_vocab_multipass": lambda: make_case(1, [5], [2], 40000, [0, 1, 2, 3, 4], "bf16", seed=50,
+                                              reduction="none"),
+    "tiny_vocab": lambda: make_case(2, [8, 6], [3, 2], 2, [0, 1, 2], "f32", seed=51, reduction="none",
+                                    label_high=1),
+    "ragged_padded_f16": lambda: make_case(5, None, None, 129, [0, 1, 2, 3, 4], "f16", seed=52, Tmax=70, U1max=30,
+                                           T_range=(1, 70), U_range=(0, 29), reduction="mean", extra_cols=3),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_case_parity(name):
+    _full_parity(EDGE[name]().to("cuda"))
+
+
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean", "mean_batch", "mean_volume"])
+def test_every_reduction(reduction):
+    case = make_case(4, None, None, 65, [0, 1, 2, 3, 4], "f32", seed=60, Tmax=30, U1max=12, T_range=(5, 30),
+                     U_range=(1, 11), sigma=0.05, device="cuda")
+    _full_parity(case, reduction=reduction)
+
+
+def test_infeasible_and_data_errors():
+    case = make_case(5, [8, 5, 8, 8, 7], [2, 1, 3, 2, 2], 10, [2, 4], "f32", seed=61, reduction="none",
+                     device="cuda", Tmax=10, U1max=5)
+    # utt 1: durations {2,4} and T=5 (odd): no alignment; utt 2: a label out of range;
+    # utt 3: logit length beyond T_max; utt 4: zero frames
+    case.labels[2, 1] = 10
+    case.logit_lengths[3] = 11
+    case.logit_lengths[4] = 0
+    loss, gt, gd, st = gpu_run(case)
+    orc = oracle_run(case.to("cpu"))
+    check_loss(loss, orc, "none", torch.float32)
+    check_grads(gt, gd, orc, torch.float32)
+    s = st.cpu().numpy()
+    assert s[0] == 0 and s[1] == tdt.UTT_INFEASIBLE and s[2] == tdt.UTT_BAD_LABEL
+    assert s[3] == tdt.UTT_BAD_LOGIT_LENGTH and s[4] == tdt.UTT_INFEASIBLE
+    l = loss.cpu().numpy()
+    assert math.isinf(l[1]) and math.isnan(l[2]) and math.isnan(l[3]) and math.isinf(l[4])
+    for b in (1, 2, 3, 4):
+        assert gt[b].abs().max().item() == 0 and gd[b].abs().max().item() == 0
+
+
+def test_forward_only_matches():
+    case = config_case(0, device="cuda")
+    loss_f, g, gd, _ = gpu_run(case, compute_grad=False)
+    assert g is None and gd is None
+    loss_b, _, _, _ = gpu_run(case)
+    assert torch.equal(loss_f, loss_b)
+
+
+def test_separate_gradient_buffers_unaligned_path():
+    """Gradients in separate contiguous buffers while the logits are slices of a joint
+    tensor of odd width: logits and gradient rows are not co-aligned (per-element path)."""
+    case = make_case(2, [9, 7], [3, 4], 37, [0, 1, 2, 3], "bf16", seed=62, reduction="mean", extra_cols=1,
+                     device="cuda")
+    g = torch.full(case.tok.shape, float("nan"), dtype=case.joint.dtype, device="cuda")
+    gd = torch.full(case.dur.shape, float("nan"), dtype=case.joint.dtype, device="cuda")
+    loss, gt, gdd, _ = gpu_run(case, grads=(g, gd))
+    orc = oracle_run(case.to("cpu"))
+    check_loss(loss, orc, "mean", case.joint.dtype)
+    check_grads(gt, gdd, orc, case.joint.dtype)
+
+
+def test_padding_canary_and_determinism():
+    """Every element of the gradient views is written (NaN canaries disappear) and two runs
+    are bitwise identical."""
+    case = config_case(3, device="cuda")
+    g, gd = tdt.alloc_grads_like(case.tok, case.dur)
+    g.fill_(float("nan"))
+    gd.fill_(float("nan"))
+    loss1, g1, gd1, _ = gpu_run(case, grads=(g, gd))
+    assert not torch.isnan(g1).any().item() and not torch.isnan(gd1).any().item()
+    snap = (loss1.clone(), g1.clone(), gd1.clone())
+    loss2, g2, gd2, _ = gpu_run(case)
+    assert torch.equal(snap[0], loss2) and torch.equal(snap[1], g2) and torch.equal(snap[2], gd2)
