@@ -70,7 +70,7 @@ def main() -> int:
         g, gd = tdt.alloc_grads_like(tok, dur)
         sets.append((joint, tok, dur, g, gd))
     loss = torch.empty(B if red == 0 else 1, dtype=torch.float32, device=dev)
-    ws_bytes = tdt.workspace_size(B, Tm, U1, case.durations)
+    ws_bytes = tdt.workspace_size(dtype_code, B, Tm, U1, V, case.durations)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     labels, tl, ul = case.labels.contiguous(), case.logit_lengths.contiguous(), case.label_lengths.contiguous()
     stream = torch.cuda.current_stream(dev)

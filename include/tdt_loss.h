@@ -77,12 +77,13 @@ typedef enum {
 
 /*
  * Workspace bytes needed by tdt_loss_fwd_bwd for these sizes.
- *   B, T_max, U1_max: padded batch shape of the logits [B, T_max, U1_max, *].
- *   durations[num_durations]: host array of the duration values.
+ *   dtype: tdt_dtype_t of the logits.  B, T_max, U1_max: padded batch shape of the
+ *   logits [B, T_max, U1_max, *].  V: token classes.  durations[num_durations]: host
+ *   array of the duration values.
  * Writes the size to *bytes and returns TDT_OK, or a negative code for invalid sizes.
  */
-int tdt_loss_workspace_size(int64_t B, int64_t T_max, int64_t U1_max, const int32_t* durations,
-                            int32_t num_durations, size_t* bytes);
+int tdt_loss_workspace_size(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,
+                            const int32_t* durations, int32_t num_durations, size_t* bytes);
 
 /*
  * TDT loss forward and backward, stream-ordered on `stream` (a hipStream_t; NULL =

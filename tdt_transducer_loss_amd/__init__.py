@@ -84,7 +84,7 @@ def tdt_loss_fwd_bwd(logits: torch.Tensor, dur_logits: torch.Tensor, labels: tor
         grad_logits, grad_dur_logits = alloc_grads_like(logits, dur_logits)
     if not compute_grad:
         grad_logits = grad_dur_logits = None
-    nbytes = workspace_size(B, T_max, U1_max, durations)
+    nbytes = workspace_size(_DTYPES[logits.dtype], B, T_max, U1_max, V, durations)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream

@@ -25,7 +25,8 @@ _i32, _i64, _vp, _f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.
 _i64p = ctypes.POINTER(ctypes.c_int64)
 _i32p = ctypes.POINTER(ctypes.c_int32)
 SIGNATURES = {
-    "tdt_loss_workspace_size": (ctypes.c_int, [_i64, _i64, _i64, _i32p, _i32, ctypes.POINTER(ctypes.c_size_t)]),
+    "tdt_loss_workspace_size": (ctypes.c_int, [_i32, _i64, _i64, _i64, _i64, _i32p, _i32,
+                                                ctypes.POINTER(ctypes.c_size_t)]),
     "tdt_loss_fwd_bwd": (ctypes.c_int, [
         _i32, _i64, _i64, _i64, _i64,       # dtype, B, T_max, U1_max, V
         _vp, _i64p, _vp, _i64p, _i32,       # logits, strides, dur_logits, strides, num_durations
@@ -80,10 +81,11 @@ def i32_array(vals):
     return (ctypes.c_int32 * len(vals))(*[int(v) for v in vals])
 
 
-def workspace_size(B: int, T_max: int, U1_max: int, durations) -> int:
+def workspace_size(dtype: int, B: int, T_max: int, U1_max: int, V: int, durations) -> int:
     d = i32_array(list(durations))
     out = ctypes.c_size_t(0)
-    rc = lib().tdt_loss_workspace_size(int(B), int(T_max), int(U1_max), d, len(d), ctypes.byref(out))
+    rc = lib().tdt_loss_workspace_size(int(dtype), int(B), int(T_max), int(U1_max), int(V), d, len(d),
+                                       ctypes.byref(out))
     if rc != TDT_OK:
         raise ValueError(f"tdt_loss_workspace_size: {status_string(rc)} ({rc})")
     return int(out.value)

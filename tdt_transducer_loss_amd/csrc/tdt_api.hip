@@ -6,14 +6,16 @@
 
 #include "tdt_kernels.h"
 #include "tdt_loss.h"
+#include "tdt_rows.h"
 
 namespace {
 
 using tdt::Params;
 
 struct Layout {
-  int KD, WP, DM, NW, NPR, RS;
-  size_t off_rstat, off_lse, off_pr, off_wm, off_we, off_am, off_ae, off_bm, off_be, off_rec;
+  int KD, WP, DM, NW, NPR, RS, nseg, nch;
+  int RW;
+  size_t off_rstat, off_part, off_pr, off_wout, off_win, off_ar, off_br, off_rec;
   size_t off_logp, off_logpa, off_wts, off_pm, off_pe, off_uok;
   size_t total;
 };
@@ -40,8 +42,10 @@ int check_durations(const int32_t* durations, int32_t D) {
   return any_pos ? maxd : TDT_ERR_INVALID_ARGUMENT;
 }
 
-int make_layout(int64_t B, int64_t Tmax, int64_t U1max, int32_t D, int maxd, Layout* L) {
-  if (B < 1 || Tmax < 1 || U1max < 1) return TDT_ERR_INVALID_ARGUMENT;
+int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V, int32_t D, int maxd, Layout* L) {
+  if (dtype < 0 || dtype > 2) return TDT_ERR_UNSUPPORTED_DTYPE;
+  if (B < 1 || Tmax < 1 || U1max < 1 || V < 1) return TDT_ERR_INVALID_ARGUMENT;
+  if (V > ((int64_t)1 << 30) || B > ((int64_t)1 << 24)) return TDT_ERR_UNSUPPORTED;
   if (U1max > TDT_MAX_U1) return TDT_ERR_UNSUPPORTED;
   if (Tmax > (1 << 24)) return TDT_ERR_UNSUPPORTED;
   L->KD = (int)(Tmax + U1max - 1);
@@ -50,7 +54,11 @@ int make_layout(int64_t B, int64_t Tmax, int64_t U1max, int32_t D, int maxd, Lay
   L->NW = 2 * L->DM + 1;
   L->NPR = L->DM + 3;
   L->RS = 5 + D;
+  tdt::pick_segments(V, dtype == 0 ? 4 : 8, &L->nch, &L->nseg);
   const size_t NP = (size_t)B * (size_t)L->KD * (size_t)L->WP;
+  L->RW = tdt::rec_bytes(L->DM);
+  // the lattice addresses one utterance's weight records with 32-bit byte offsets
+  if ((size_t)L->KD * (size_t)L->WP * (size_t)L->RW > (size_t)0x7fffffff) return TDT_ERR_UNSUPPORTED;
   if (NP > ((size_t)1 << 40)) return TDT_ERR_UNSUPPORTED;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -59,14 +67,12 @@ int make_layout(int64_t B, int64_t Tmax, int64_t U1max, int32_t D, int maxd, Lay
     return at;
   };
   L->off_rstat = take(NP * 16);
-  L->off_lse = take(NP * 8);
+  L->off_part = take(NP * (size_t)L->nseg * 8);
   L->off_pr = take(NP * (size_t)L->NPR * 8);
-  L->off_wm = take(NP * (size_t)L->NW * 8);
-  L->off_we = take(NP * (size_t)L->NW * 4);
-  L->off_am = take(NP * 8);
-  L->off_ae = take(NP * 4);
-  L->off_bm = take(NP * 8);
-  L->off_be = take(NP * 4);
+  L->off_wout = take(NP * (size_t)L->RW);
+  L->off_win = take(NP * (size_t)L->RW);
+  L->off_ar = take(NP * 16);
+  L->off_br = take(NP * 16);
   L->off_rec = take(NP * (size_t)L->RS * 4);
   L->off_logp = take((size_t)B * 8);
   L->off_logpa = take((size_t)B * 8);
@@ -97,13 +103,13 @@ extern "C" const char* tdt_loss_status_string(int status) {
   }
 }
 
-extern "C" int tdt_loss_workspace_size(int64_t B, int64_t T_max, int64_t U1_max, const int32_t* durations,
-                                       int32_t num_durations, size_t* bytes) {
+extern "C" int tdt_loss_workspace_size(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,
+                                       const int32_t* durations, int32_t num_durations, size_t* bytes) {
   if (!bytes) return TDT_ERR_INVALID_ARGUMENT;
   const int maxd = check_durations(durations, num_durations);
   if (maxd < 0) return maxd;
   Layout L;
-  const int rc = make_layout(B, T_max, U1_max, num_durations, maxd, &L);
+  const int rc = make_layout(dtype, B, T_max, U1_max, V, num_durations, maxd, &L);
   if (rc != TDT_OK) return rc;
   *bytes = L.total;
   return TDT_OK;
@@ -123,7 +129,7 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
   if (!logits || !logits_strides || !dur_logits || !dur_strides || !labels || !logit_lengths || !label_lengths ||
       !loss_out || !workspace)
     return TDT_ERR_INVALID_ARGUMENT;
-  if (V < 1 || V > (int64_t)1 << 30 || B > (int64_t)1 << 24) return V < 1 ? TDT_ERR_INVALID_ARGUMENT : TDT_ERR_UNSUPPORTED;
+  if (V < 1) return TDT_ERR_INVALID_ARGUMENT;
   if (blank < 0 || blank >= V) return TDT_ERR_INVALID_ARGUMENT;
   if (!isfinite(sigma)) return TDT_ERR_INVALID_ARGUMENT;
   if (labels_stride < U1_max - 1) return TDT_ERR_BAD_STRIDE;
@@ -133,7 +139,7 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
   const int maxd = check_durations(durations, num_durations);
   if (maxd < 0) return maxd;
   Layout L;
-  int rc = make_layout(B, T_max, U1_max, num_durations, maxd, &L);
+  int rc = make_layout(dtype, B, T_max, U1_max, V, num_durations, maxd, &L);
   if (rc != TDT_OK) return rc;
   if (workspace_bytes < L.total) return TDT_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned_to(workspace, 256)) return TDT_ERR_BAD_STRIDE;
@@ -157,6 +163,8 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
   p.NW = L.NW;
   p.NPR = L.NPR;
   p.RS = L.RS;
+  p.nseg = L.nseg;
+  p.nch = L.nch;
   p.sigma = sigma;
   for (int d = 0; d <= tdt::kMaxDval; ++d) p.didx[d] = -1;
   for (int i = 0; i < num_durations; ++i) {
@@ -189,14 +197,13 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
   }
   char* ws = (char*)workspace;
   p.rstat = (float4*)(ws + L.off_rstat);
-  p.lse = (double*)(ws + L.off_lse);
+  p.part = (float*)(ws + L.off_part);
   p.pr = (double*)(ws + L.off_pr);
-  p.wm = (double*)(ws + L.off_wm);
-  p.we = (int*)(ws + L.off_we);
-  p.am = (double*)(ws + L.off_am);
-  p.ae = (int*)(ws + L.off_ae);
-  p.bm = (double*)(ws + L.off_bm);
-  p.be = (int*)(ws + L.off_be);
+  p.wout = ws + L.off_wout;
+  p.win = ws + L.off_win;
+  p.ar = ws + L.off_ar;
+  p.br = ws + L.off_br;
+  p.RW = L.RW;
   p.rec = (float*)(ws + L.off_rec);
   p.logp = (double*)(ws + L.off_logp);
   p.logpa = (double*)(ws + L.off_logpa);

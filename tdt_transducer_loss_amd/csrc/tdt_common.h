@@ -11,6 +11,9 @@ constexpr int kWave = 64;
 constexpr int kMaxD = 16;      // durations per call
 constexpr int kMaxDval = 16;   // largest duration value
 constexpr int kEZ = -(1 << 28);  // exponent of the extended-range zero
+// Stored weight exponents carry this bias, so a weight read as all-zero bits (out of
+// range of a buffer load) decodes as mantissa 0 with exponent -kWBias: a zero.
+constexpr int kWBias = 1 << 29;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kLn2 = 0.6931471805599453094;
@@ -22,12 +25,12 @@ constexpr double kLog2eD = 1.4426950408889634074;
 //
 // Workspace layout.  Per utterance b the lattice nodes are stored by anti-diagonal:
 // position (b, k, i) with k = t + u in [0, KD) and i = u - ulo(k) in [0, WP), where
-// ulo(k) = max(0, k - T + 1).  pos = (b*KD + k)*WP + i.  Transition weights use
-// [b][k][slot][i]: slot d-1 (d = 1..DM) is the blank move of duration d, slot DM + d
-// (d = 0..DM) the label move of duration d; absent durations hold the zero value.
+// ulo(k) = max(0, k - T + 1).  pos = (b*KD + k)*WP + i.  Each position holds records
+// of row statistics, transition weights, alpha, beta and the gradient-pass coefficients.
 struct Params {
   int B, Tmax, U1max, V, D, blank, red, dtype;
   int KD, WP, DM, NW, NPR, RS;
+  int nseg, nch;  // row segments per row, 16-byte chunks per lane per segment
   double sigma;
   int dval[kMaxD];          // duration value of index i
   int didx[kMaxDval + 1];   // index of duration value d, -1 when absent
@@ -49,14 +52,13 @@ struct Params {
   int64_t gds0, gds1, gds2;
   // workspace, per position
   float4* rstat;  // {mL, K, h_blank, h_label}: mL = f32(rowmax * log2e), K = log2 sum 2^(x log2e - mL)
-  double* lse;    // natural-log normaliser of the token logits
+  float* part;    // [2 * nseg] per row segment: its mL and its sum 2^(x log2e - mL)
   double* pr;     // [NPR]: softmax(h)_blank, softmax(h)_label, softmax(g) by duration value 0..DM
-  double* wm;     // transition weight mantissas [B][KD][NW][WP]
-  int* we;        // transition weight exponents
-  double* am;     // alpha (extended range)
-  int* ae;
-  double* bm;     // beta
-  int* be;
+  char* wout;     // [positions] weight records of the moves out of each node (RW bytes)
+  char* win;      // [positions] weight records of the moves into each node
+  char* ar;       // [positions] alpha, 16-byte records (float64 mantissa, int32 exponent)
+  char* br;       // [positions] beta, same records
+  int RW;         // bytes per weight record
   float* rec;     // [RS] per-node record of the gradient pass
   // workspace, per utterance
   double* logp;   // log P from beta(0,0)
@@ -130,9 +132,9 @@ __device__ __forceinline__ int64_t node_pos(const Params& p, int b, int k, int i
   return ((int64_t)b * p.KD + k) * p.WP + i;
 }
 
-__device__ __forceinline__ int64_t w_index(const Params& p, int b, int k, int slot, int i) {
-  return (((int64_t)b * p.KD + k) * p.NW + slot) * p.WP + i;
-}
+// Bytes of one node's weight record: 2*DM+1 float64 mantissas and as many int32
+// exponents, rounded up to 16 bytes.
+__host__ __device__ constexpr int rec_bytes(int DM) { return ((12 * (2 * DM + 1) + 15) / 16) * 16; }
 
 __device__ __forceinline__ bool utt_dims_ok(const Params& p, int64_t T, int64_t U) {
   return T >= 0 && T <= p.Tmax && U >= 0 && U <= p.U1max - 1;

@@ -1,6 +1,7 @@
 // Lattice side of the TDT loss on gfx950:
 //   node weights  — duration log-softmax and the extended-range weight of every move out
-//                   of a node (thread per node);
+//                   of a node (thread per node), stored per node as an outgoing record
+//                   and scattered into the incoming record of each destination;
 //   lattice       — float64 alpha and beta sweeps over the T x (U+1) lattice, one
 //                   work-group per (utterance, direction), anti-diagonal wavefront with
 //                   the label index across lanes (the alpha/beta passes of the page
@@ -16,22 +17,53 @@
 
 namespace tdt {
 
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
 // Reduction weight w_b of utterance b (d reduced loss / d loss_b).
 __device__ double reduction_weight(const Params& p, int b, int64_t sumU) {
   switch (p.red) {
-    case 3: return 1.0 / (double)p.B;                                        // mean_batch
-    case 2: { int64_t U = p.Ulen[b]; return 1.0 / ((double)p.B * (double)(U > 1 ? U : 1)); }  // mean
-    case 4: return 1.0 / (double)(sumU > 1 ? sumU : 1);                      // mean_volume
-    default: return 1.0;                                                     // none, sum
+    case 3: return 1.0 / (double)p.B;  // mean_batch
+    case 2: {                          // mean
+      const int64_t U = p.Ulen[b];
+      return 1.0 / ((double)p.B * (double)(U > 1 ? U : 1));
+    }
+    case 4: return 1.0 / (double)(sumU > 1 ? sumU : 1);  // mean_volume
+    default: return 1.0;                                 // none, sum
   }
+}
+
+// ---- records ----
+// Weight record of a node (RW bytes, 16-byte aligned): NW float64 mantissas, then NW
+// int32 exponents carrying +kWBias (all-zero bits = the zero weight).  Slot d-1
+// (d = 1..DM) is the blank move of duration d, slot DM+d (d = 0..DM) the label move of
+// duration d.  Alpha / beta records are 16 bytes: float64 mantissa, int32 exponent.
+__device__ __forceinline__ char* wrec(char* base, const Params& p, int64_t pos) { return base + pos * p.RW; }
+
+__device__ __forceinline__ void wrec_put(char* rec, int NW, int s, Ext w) {
+  ((double*)rec)[s] = w.m;
+  ((int*)(rec + 8 * NW))[s] = w.m == 0.0 ? 0 : w.e + kWBias;
+}
+
+__device__ __forceinline__ Ext wrec_get(const char* rec, int NW, int s) {
+  return Ext{((const double*)rec)[s], ((const int*)(rec + 8 * NW))[s] - kWBias};
+}
+
+__device__ __forceinline__ Ext xrec_get(const char* base, int64_t pos) {
+  const char* r = base + pos * 16;
+  return Ext{*(const double*)r, *(const int*)(r + 8)};
 }
 
 // ------------------------------------------------------------------------------------
 // Node weights: for node n = (t,u)
 //   l_blank = h_blank - lse, l_label = h_{y_{u+1}} - lse, lambda = log_softmax(g(n)),
-//   W_blank(d) = exp(l_blank - sigma + lambda_d)  (d > 0),
-//   W_label(d) = exp(l_label - sigma + lambda_d)  (u < U),
-// plus softmax(h)_blank, softmax(h)_label and softmax(g) for the gradient.
+//   W_blank(d) = exp(l_blank - sigma + lambda_d)  (d > 0; t+d < T, or t+d = T at u = U),
+//   W_label(d) = exp(l_label - sigma + lambda_d)  (u < U, t+d < T),
+// plus softmax(h)_blank, softmax(h)_label and softmax(g) for the gradient.  Every
+// record of the padded [B][KD][WP] layout is written: moves that leave the lattice,
+// absent durations, moves with no source and positions outside the utterance hold the
+// zero weight, so the sweeps read any in-range record without predicates.  Slot s of
+// the incoming record of n is written by the source of that move, or zeroed by n's own
+// thread when the source does not exist (exactly one writer per slot).
 template <int DM>
 __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
   constexpr int NW = 2 * DM + 1;
@@ -42,17 +74,37 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
   const int64_t rem = g - (int64_t)b * per;
   const int k = (int)(rem / p.WP);
   const int i = (int)(rem - (int64_t)k * p.WP);
+  const int64_t pos = (int64_t)b * per + rem;
+  char* orec = wrec(p.wout, p, pos);
+  char* irec = wrec(p.win, p, pos);
   const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
-  if (!utt_dims_ok(p, T64, U64)) return;
   const int T = (int)T64, U = (int)U64;
-  if (k >= T + U) return;
-  const int u = diag_ulo(k, T) + i;
-  if (u > min(k, U)) return;
+  const bool dims = utt_dims_ok(p, T64, U64);
+  const int u = dims ? diag_ulo(k, T) + i : 0;
+  const bool valid = dims && k < T + U && u <= min(k, U);
+  if (!valid) {
+#pragma unroll
+    for (int s = 0; s < NW; ++s) {
+      wrec_put(orec, NW, s, ext_zero());
+      wrec_put(irec, NW, s, ext_zero());
+    }
+    return;
+  }
   const int t = k - u;
-  const int64_t pos = node_pos(p, b, k, i);
 
+  // log-sum-exp of the token logits from the row-segment partials
+  const float* part = p.part + pos * 2 * p.nseg;
+  float mL = part[0];
+  for (int s = 1; s < p.nseg; ++s) mL = fmaxf(mL, part[2 * s]);
+  double S = 0.0;
+  for (int s = 0; s < p.nseg; ++s) {
+    const float ps = part[2 * s + 1];
+    if (ps > 0.f) S += (double)ps * exp2((double)(part[2 * s] - mL));
+  }
+  const double K = log2(S);
+  const double L = ((double)mL + K) * kLn2;  // natural-log normaliser
   const float4 rs = p.rstat[pos];
-  const double L = p.lse[pos];
+  ((float2*)(p.rstat + pos))[0] = make_float2(mL, (float)K);
   const double lb = (double)rs.z - L;
   const double ly = (u < U && rs.w > -__builtin_inff()) ? (double)rs.w - L : -__builtin_inf();
 
@@ -79,8 +131,7 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
   pr[1] = exp(ly);
   const Ext eb = ext_exp(lb - p.sigma);
   const Ext ey = ext_exp(ly - p.sigma);
-  double* wm = p.wm;
-  int* we = p.we;
+  const int64_t ub = (int64_t)b * per;
 #pragma unroll
   for (int d = 0; d <= DM; ++d) {
     const bool has = p.didx[d] >= 0;
@@ -88,27 +139,39 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
     pr[2 + d] = has ? exp(lam) : 0.0;
     const Ext ed = has ? ext_exp(lam) : ext_zero();
     if (d >= 1) {
-      const Ext wb = has ? ext_mul(eb, ed) : ext_zero();
-      const int64_t o = w_index(p, b, k, d - 1, i);
-      wm[o] = wb.m;
-      we[o] = wb.e;
+      const bool inside = t + d < T;
+      const bool ok = has && (inside || (t + d == T && u == U));
+      const Ext wb = ok ? ext_mul(eb, ed) : ext_zero();
+      wrec_put(orec, NW, d - 1, wb);
+      if (inside) {  // incoming slot of (t+d, u)
+        const int k2 = k + d;
+        wrec_put(wrec(p.win, p, ub + (int64_t)k2 * p.WP + (u - diag_ulo(k2, T))), NW, d - 1, wb);
+      }
+      if (t - d < 0) wrec_put(irec, NW, d - 1, ext_zero());  // no source for this slot
     }
-    const Ext wl = (has && u < U) ? ext_mul(ey, ed) : ext_zero();
-    const int64_t o = w_index(p, b, k, DM + d, i);
-    wm[o] = wl.m;
-    we[o] = wl.e;
+    const bool inside = u < U && t + d < T;
+    const Ext wl = (has && inside) ? ext_mul(ey, ed) : ext_zero();
+    wrec_put(orec, NW, DM + d, wl);
+    if (inside) {  // incoming slot of (t+d, u+1)
+      const int k2 = k + d + 1;
+      wrec_put(wrec(p.win, p, ub + (int64_t)k2 * p.WP + (u + 1 - diag_ulo(k2, T))), NW, DM + d, wl);
+    }
+    if (u == 0 || t - d < 0) wrec_put(irec, NW, DM + d, ext_zero());
   }
-  (void)NW;
 }
 
 // ------------------------------------------------------------------------------------
 // Lattice sweeps.  Thread j owns labels u = j*R .. j*R + R - 1.  Step k of the alpha
 // sweep computes anti-diagonal k (t = k - u); every dependency lies on diagonals
-// k-1 .. k-1-DM, kept in a register ring of S >= DM+1 slots (S even, so the double
-// buffer of prefetched weights has a fixed slot per unrolled phase).  The value of the
-// neighbouring label index owned by the next thread is exchanged once per step (DPP
+// k-1 .. k-1-DM, kept in a register ring of S >= DM+1 slots.  S is a multiple of 6 so
+// that, after unrolling S steps, the exchange parity (2) and the triple buffer of
+// weight records prefetched two steps ahead (3) sit in fixed registers.  The value of
+// the neighbouring label index owned by the next thread is exchanged once per step (DPP
 // wave shift for one wave, LDS + barrier otherwise).  The beta sweep runs the same
 // wavefront from the last diagonal back to (0,0).
+template <int DM>
+__host__ __device__ constexpr int ring_size() { return ((DM + 1 + 5) / 6) * 6; }
+
 template <bool SW>
 __device__ __forceinline__ Ext exchange(Ext v, bool from_left, int parity, double* xm, int* xe) {
   if (SW) {
@@ -137,103 +200,59 @@ __device__ __forceinline__ Ext exchange(Ext v, bool from_left, int parity, doubl
   }
 }
 
-__device__ __forceinline__ Ext load_ext(const Params& p, int64_t o) { return Ext{p.wm[o], p.we[o]}; }
-
-template <int DM, int R, bool SW>
-__device__ void alpha_sweep(const Params& p, int b, int T, int U, double* xm, int* xe) {
-  constexpr int NW = 2 * DM + 1;
-  constexpr int S = ((DM + 2) / 2) * 2;
-  const int tid = threadIdx.x;
-  const int nsteps = T + U;
-  Ext h[R][S];
-  Ext nb[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    nb[s] = ext_zero();
-#pragma unroll
-    for (int r = 0; r < R; ++r) h[r][s] = ext_zero();
-  }
-  Ext wb[2][R][NW];
-
-  auto load_w = [&](int k, Ext (&w)[R][NW]) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int u = tid * R + r, t = k - u;
-      const bool act = t >= 0 && t < T && u <= U;
-#pragma unroll
-      for (int d = 1; d <= DM; ++d) {
-        w[r][d - 1] = ext_zero();
-        if (act && t - d >= 0) w[r][d - 1] = load_ext(p, w_index(p, b, k - d, d - 1, u - diag_ulo(k - d, T)));
-      }
-#pragma unroll
-      for (int d = 0; d <= DM; ++d) {
-        w[r][DM + d] = ext_zero();
-        if (act && u >= 1 && t - d >= 0)
-          w[r][DM + d] = load_ext(p, w_index(p, b, k - 1 - d, DM + d, u - 1 - diag_ulo(k - 1 - d, T)));
-      }
-    }
-  };
-
-  load_w(0, wb[0]);
-  for (int k0 = 0; k0 < nsteps; k0 += S) {
-#pragma unroll
-    for (int ph = 0; ph < S; ++ph) {
-      const int k = k0 + ph;
-      if (k >= nsteps) break;
-      if (k + 1 < nsteps) load_w(k + 1, wb[(ph + 1) & 1]);
-      Ext nv[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int u = tid * R + r, t = k - u;
-        const bool act = t >= 0 && t < T && u <= U;
-        Ext terms[NW];
-#pragma unroll
-        for (int d = 1; d <= DM; ++d) terms[d - 1] = ext_mul(h[r][(ph - d + 4 * S) % S], wb[ph & 1][r][d - 1]);
-#pragma unroll
-        for (int d = 0; d <= DM; ++d) {
-          const Ext src = r > 0 ? h[r > 0 ? r - 1 : 0][(ph - 1 - d + 4 * S) % S] : nb[(ph - 1 - d + 4 * S) % S];
-          terms[DM + d] = ext_mul(src, wb[ph & 1][r][DM + d]);
-        }
-        Ext a = ext_sum(terms);
-        if (k == 0 && u == 0) a = ext_one();
-        if (!act) a = ext_zero();
-        nv[r] = a;
-        if (act) {
-          const int64_t pos = node_pos(p, b, k, u - diag_ulo(k, T));
-          p.am[pos] = a.m;
-          p.ae[pos] = a.e;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) h[r][ph] = nv[r];
-      nb[ph] = exchange<SW>(nv[R - 1], true, ph & 1, xm, xe);
-    }
-  }
-  // log P from the alpha side: blanks that land on t = T from u = U
-  if (tid * R <= U && U < tid * R + R) {
-    __threadfence();
-    Ext terms[DM];
-#pragma unroll
-    for (int d = 1; d <= DM; ++d) {
-      terms[d - 1] = ext_zero();
-      const int t = T - d;
-      if (t >= 0) {
-        const int k = t + U;
-        const int i = U - diag_ulo(k, T);
-        const int64_t pos = node_pos(p, b, k, i);
-        terms[d - 1] = ext_mul(Ext{p.am[pos], p.ae[pos]}, load_ext(p, w_index(p, b, k, d - 1, i)));
-      }
-    }
-    p.logpa[b] = ext_log(ext_sum(terms));
-  }
+// Pairwise (tree) reductions for the sum of extended values: shorter dependency chains
+// than a running sum, which is what bounds one lattice step.
+template <int N>
+__device__ __forceinline__ int tree_max_e(const Ext* t) {
+  if constexpr (N == 1) return t[0].e;
+  else return max(tree_max_e<N / 2>(t), tree_max_e<N - N / 2>(t + N / 2));
+}
+template <int N>
+__device__ __forceinline__ double tree_sum_m(const Ext* t, int E) {
+  if constexpr (N == 1) return ldexp(t[0].m, t[0].e - E);
+  else return tree_sum_m<N / 2>(t, E) + tree_sum_m<N - N / 2>(t + N / 2, E);
+}
+// Sum of terms whose exponents all carry +kWBias; returns the un-biased sum.
+template <int N>
+__device__ __forceinline__ Ext ext_sum_biased(const Ext (&t)[N]) {
+  const int E = tree_max_e<N>(t);
+  const double sm = tree_sum_m<N>(t, E);
+  return ext_norm(sm, E - kWBias);
 }
 
-template <int DM, int R, bool SW>
-__device__ void beta_sweep(const Params& p, int b, int T, int U, double* xm, int* xe) {
+// A weight record loaded as RW/16 16-byte words; decoded slot by slot.
+template <int DM>
+struct WRec {
+  static constexpr int NW = 2 * DM + 1;
+  static constexpr int NQ = rec_bytes(DM) / 16;
+  u32x4v q[NQ];
+  __device__ __forceinline__ uint32_t dw(int j) const { return q[j >> 2][j & 3]; }
+  __device__ __forceinline__ Ext get(int s) const {  // biased exponent kept
+    const uint64_t bits = ((uint64_t)dw(2 * s + 1) << 32) | dw(2 * s);
+    return Ext{__builtin_bit_cast(double, bits), (int)dw(2 * NW + s)};
+  }
+};
+
+// One direction of the lattice.  ALPHA: forward sweep with the incoming records;
+// otherwise backward sweep with the node's outgoing records, beta of the terminal
+// (t = T, u = U) seeded as 1 in the ring.  Moves that leave the lattice and moves with
+// no source have zero weight, and sources outside the lattice have zero alpha, so no
+// term needs a predicate; a node outside the lattice is forced to zero.  Out-of-range
+// record reads return zero (buffer range check).  `prog` (LDS) receives the step index
+// for the L2 warm-up waves.
+template <int DM, int R, bool SW, bool ALPHA>
+__device__ void sweep(const Params& p, int b, int T, int U, double* xm, int* xe, volatile int* prog) {
   constexpr int NW = 2 * DM + 1;
-  constexpr int S = ((DM + 2) / 2) * 2;
+  constexpr int S = ring_size<DM>();
+  constexpr int RWB = rec_bytes(DM);
   const int tid = threadIdx.x;
   const int nsteps = T + U;
+  const int WP = p.WP;
+  const int64_t nrec = (int64_t)p.KD * WP;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((ALPHA ? p.win : p.wout) + b * nrec * RWB), (short)0, (int)(nrec * RWB), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((ALPHA ? p.ar : p.br) + b * nrec * 16), (short)0, (int)(nrec * 16), 0x00020000);
   Ext h[R][S];
   Ext nb[S];
 #pragma unroll
@@ -242,56 +261,65 @@ __device__ void beta_sweep(const Params& p, int b, int T, int U, double* xm, int
 #pragma unroll
     for (int r = 0; r < R; ++r) h[r][s] = ext_zero();
   }
-  Ext wb[2][R][NW];
+  if (!ALPHA) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (tid * R + r == U) h[r][S - 1] = ext_one();  // beta(T, U): the terminal
+  }
+  WRec<DM> wb[3][R];
 
-  auto load_w = [&](int ks, Ext (&w)[R][NW]) {
-    const int k = nsteps - 1 - ks;
+  auto load_w = [&](int ks, WRec<DM> (&w)[R]) {
+    const int k = ALPHA ? ks : nsteps - 1 - ks;
+    const int base = k * WP - diag_ulo(k, T);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int u = tid * R + r, t = k - u;
-      const bool act = t >= 0 && t < T && u <= U;
-      const int i = u - diag_ulo(k, T);
+      const int off = (base + tid * R + r) * RWB;
 #pragma unroll
-      for (int s = 0; s < NW; ++s) {
-        w[r][s] = ext_zero();
-        if (act) w[r][s] = load_ext(p, w_index(p, b, k, s, i));
-      }
+      for (int j = 0; j < WRec<DM>::NQ; ++j) w[r].q[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16 * j, 0, 0);
     }
   };
 
   load_w(0, wb[0]);
+  if (nsteps > 1) load_w(1, wb[1]);
   for (int k0 = 0; k0 < nsteps; k0 += S) {
 #pragma unroll
     for (int ph = 0; ph < S; ++ph) {
       const int ks = k0 + ph;
       if (ks >= nsteps) break;
-      if (ks + 1 < nsteps) load_w(ks + 1, wb[(ph + 1) & 1]);
-      const int k = nsteps - 1 - ks;
+      if (ks + 2 < nsteps) load_w(ks + 2, wb[(ph + 2) % 3]);
+      const int k = ALPHA ? ks : nsteps - 1 - ks;
+      const int base = k * WP - diag_ulo(k, T);
       Ext nv[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int u = tid * R + r, t = k - u;
-        const bool act = t >= 0 && t < T && u <= U;
+        const bool act = (unsigned)t < (unsigned)T && u <= U;
+        const WRec<DM>& w = wb[ph % 3][r];
         Ext terms[NW];
 #pragma unroll
-        for (int d = 1; d <= DM; ++d) {
-          const Ext dst = (t + d == T && u == U) ? ext_one() : h[r][(ph - d + 4 * S) % S];
-          terms[d - 1] = ext_mul(dst, wb[ph & 1][r][d - 1]);
-        }
+        for (int d = 1; d <= DM; ++d) terms[d - 1] = ext_mul(h[r][(ph - d + 4 * S) % S], w.get(d - 1));
+        if (ALPHA) {
 #pragma unroll
-        for (int d = 0; d <= DM; ++d) {
-          const Ext dst = r < R - 1 ? h[r < R - 1 ? r + 1 : 0][(ph - 1 - d + 4 * S) % S] : nb[(ph - 1 - d + 4 * S) % S];
-          terms[DM + d] = ext_mul(dst, wb[ph & 1][r][DM + d]);
+          for (int d = 0; d <= DM; ++d) {
+            const Ext src = r > 0 ? h[r > 0 ? r - 1 : 0][(ph - 1 - d + 4 * S) % S] : nb[(ph - 1 - d + 4 * S) % S];
+            terms[DM + d] = ext_mul(src, w.get(DM + d));
+          }
+        } else {
+#pragma unroll
+          for (int d = 0; d <= DM; ++d) {
+            const Ext dst = r < R - 1 ? h[r < R - 1 ? r + 1 : 0][(ph - 1 - d + 4 * S) % S] : nb[(ph - 1 - d + 4 * S) % S];
+            terms[DM + d] = ext_mul(dst, w.get(DM + d));
+          }
         }
-        Ext a = ext_sum(terms);
+        Ext a = ext_sum_biased(terms);
+        if (ALPHA && ks == 0 && u == 0) a = ext_one();
         if (!act) a = ext_zero();
         nv[r] = a;
-        if (act) {
-          const int64_t pos = node_pos(p, b, k, u - diag_ulo(k, T));
-          p.bm[pos] = a.m;
-          p.be[pos] = a.e;
-        }
-        if (k == 0 && u == 0) {  // beta(0,0) = P
+        const int o = act ? (base + u) * 16 : -16;
+        const uint64_t mb = __builtin_bit_cast(uint64_t, a.m);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4v{(uint32_t)mb, (uint32_t)(mb >> 32), (uint32_t)a.e, 0u}, xr, o, 0,
+                                               0);
+        if (!ALPHA && ks == nsteps - 1 && u == 0) {  // beta(0,0) = P
           const double lp = ext_log(a);
           p.logp[b] = lp;
           p.pm[b] = a.m;
@@ -303,16 +331,54 @@ __device__ void beta_sweep(const Params& p, int b, int T, int U, double* xm, int
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) h[r][ph] = nv[r];
-      nb[ph] = exchange<SW>(nv[0], false, ph & 1, xm, xe);
+      nb[ph] = exchange<SW>(ALPHA ? nv[R - 1] : nv[0], ALPHA, ph & 1, xm, xe);
+      if (SW) *prog = ks;
     }
+  }
+  if (ALPHA && tid * R <= U && U < tid * R + R) {
+    // log P from the alpha side: blanks that land on t = T from u = U
+    __threadfence();
+    Ext terms[DM];
+#pragma unroll
+    for (int d = 1; d <= DM; ++d) {
+      terms[d - 1] = ext_zero();
+      const int t = T - d;
+      if (t >= 0) {
+        const int k = t + U;
+        const int64_t pos = node_pos(p, b, k, U - diag_ulo(k, T));
+        terms[d - 1] = ext_mul(xrec_get(p.ar, pos), wrec_get(wrec(p.wout, p, pos), NW, d - 1));
+      }
+    }
+    p.logpa[b] = ext_log(ext_sum(terms));
   }
 }
 
+// L2 warm-up for a single-wave sweep: the other waves of the work-group touch every
+// 128-byte line of the weight records of the diagonals the chain will reach next, at
+// most kLead diagonals ahead of it (the chain never waits for them).
+constexpr int kLead = 48;
+
+__device__ void l2_warm(const Params& p, int b, int nsteps, bool alpha, volatile int* prog) {
+  const int hl = threadIdx.x - 64, nh = blockDim.x - 64;
+  const int64_t dbytes = (int64_t)p.WP * p.RW;  // one diagonal of records
+  const int lines = (int)((dbytes + 127) / 128);
+  const char* base = (alpha ? p.win : p.wout) + (int64_t)b * p.KD * dbytes;
+  uint32_t acc = 0;
+  for (int ks = 0; ks < nsteps; ++ks) {
+    while (ks > *prog + kLead) __builtin_amdgcn_s_sleep(2);
+    const int k = alpha ? ks : nsteps - 1 - ks;
+    const char* blk = base + (int64_t)k * dbytes;
+    for (int l = hl; l < lines; l += nh) acc += *(const uint32_t*)(blk + (int64_t)l * 128);
+  }
+  if (acc == 0x9e3779b9u && p.B < 0) p.uok[0] = (int)acc;  // keeps the touching loads alive
+}
+
 template <int DM, int R, bool SW>
-__global__ __launch_bounds__(SW ? 64 : 1024) void k_lattice(const Params p) {
+__global__ __launch_bounds__(SW ? 256 : 1024) void k_lattice(const Params p) {
   __shared__ double xm[SW ? 1 : 2 * 1024];
   __shared__ int xe[SW ? 1 : 2 * 1024];
   __shared__ unsigned long long s_sumU;
+  __shared__ int s_prog;
   const int b = blockIdx.x >> 1, dir = blockIdx.x & 1;
   const int tid = threadIdx.x, nt = blockDim.x;
   const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
@@ -326,7 +392,10 @@ __global__ __launch_bounds__(SW ? 64 : 1024) void k_lattice(const Params p) {
       bad |= (y < 0 || y >= p.V);
     }
   }
-  if (tid == 0) s_sumU = 0;
+  if (tid == 0) {
+    s_sumU = 0;
+    s_prog = -1;
+  }
   if (__syncthreads_or(bad)) status |= 4;
   if (dir == 1 && p.red == 4) {
     unsigned long long part = 0;
@@ -350,10 +419,14 @@ __global__ __launch_bounds__(SW ? 64 : 1024) void k_lattice(const Params p) {
     }
     return;
   }
+  if (SW && tid >= 64) {
+    l2_warm(p, b, T + U, dir == 0, &s_prog);
+    return;
+  }
   if (dir == 0)
-    alpha_sweep<DM, R, SW>(p, b, T, U, xm, xe);
+    sweep<DM, R, SW, true>(p, b, T, U, xm, xe, &s_prog);
   else
-    beta_sweep<DM, R, SW>(p, b, T, U, xm, xe);
+    sweep<DM, R, SW, false>(p, b, T, U, xm, xe, &s_prog);
 }
 
 // ------------------------------------------------------------------------------------
@@ -376,6 +449,7 @@ __device__ void reduce_loss(const Params& p) {
 
 template <int DM>
 __global__ __launch_bounds__(256) void k_coef(const Params p) {
+  constexpr int NW = 2 * DM + 1;
   if (blockIdx.x == 0 && threadIdx.x == 0) reduce_loss(p);
   const int64_t g = (int64_t)xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
   const int64_t per = (int64_t)p.KD * p.WP;
@@ -392,7 +466,8 @@ __global__ __launch_bounds__(256) void k_coef(const Params p) {
   const int t = k - u;
   const int64_t pos = node_pos(p, b, k, i);
 
-  const Ext a = Ext{p.am[pos], p.ae[pos]};
+  const Ext a = xrec_get(p.ar, pos);
+  const char* wr = wrec(p.wout, p, pos);
   const double Pm = p.pm[b];
   const int Pe = p.pe[b];
   double gbl[DM + 1], glb[DM + 1];
@@ -405,22 +480,18 @@ __global__ __launch_bounds__(256) void k_coef(const Params p) {
       Ext bt = ext_zero();
       if (t + d < T) {
         const int k2 = k + d;
-        const int64_t o = node_pos(p, b, k2, u - diag_ulo(k2, T));
-        bt = Ext{p.bm[o], p.be[o]};
+        bt = xrec_get(p.br, node_pos(p, b, k2, u - diag_ulo(k2, T)));
       } else if (t + d == T && u == U) {
         bt = ext_one();
       }
-      const Ext w = load_ext(p, w_index(p, b, k, d - 1, i));
-      const Ext gm = ext_mul(ext_mul(a, w), bt);
+      const Ext gm = ext_mul(ext_mul(a, wrec_get(wr, NW, d - 1)), bt);
       gbl[d] = ext_to_double(Ext{gm.m / Pm, gm.e - Pe});
       cb += gbl[d];
     }
     if (u < U && t + d < T) {
       const int k2 = k + d + 1;
-      const int64_t o = node_pos(p, b, k2, u + 1 - diag_ulo(k2, T));
-      const Ext bt = Ext{p.bm[o], p.be[o]};
-      const Ext w = load_ext(p, w_index(p, b, k, DM + d, i));
-      const Ext gm = ext_mul(ext_mul(a, w), bt);
+      const Ext bt = xrec_get(p.br, node_pos(p, b, k2, u + 1 - diag_ulo(k2, T)));
+      const Ext gm = ext_mul(ext_mul(a, wrec_get(wr, NW, DM + d)), bt);
       glb[d] = ext_to_double(Ext{gm.m / Pm, gm.e - Pe});
       cl += glb[d];
     }
@@ -432,7 +503,7 @@ __global__ __launch_bounds__(256) void k_coef(const Params p) {
   int y = -1;
   if (u < U) y = (int)p.labels[(int64_t)b * p.lab_stride + u];
   double Gb = wgt * (O * pr[0] - cb);
-  double Gy = wgt * (O * pr[1] - cl);
+  const double Gy = wgt * (O * pr[1] - cl);
   if (y == p.blank) {  // both corrections land on the blank column
     Gb -= wgt * cl;
     y = -1;
@@ -461,11 +532,11 @@ static hipError_t launch_lattice_dm(const Params& p, hipStream_t st) {
   const int u1 = p.U1max;
   const dim3 grid(2 * p.B);
   if (u1 <= 64) {
-    hipLaunchKernelGGL((k_lattice<DM, 1, true>), grid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((k_lattice<DM, 1, true>), grid, dim3(256), 0, st, p);
   } else if (u1 <= 128) {
-    hipLaunchKernelGGL((k_lattice<DM, 2, true>), grid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((k_lattice<DM, 2, true>), grid, dim3(256), 0, st, p);
   } else if (u1 <= 256) {
-    hipLaunchKernelGGL((k_lattice<DM, 4, true>), grid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((k_lattice<DM, 4, true>), grid, dim3(256), 0, st, p);
   } else {
     int R = u1 <= 1024 ? 1 : u1 <= 2048 ? 2 : u1 <= 4096 ? 4 : 8;
     const int nt = ((u1 + R - 1) / R + 63) / 64 * 64;

@@ -1,23 +1,23 @@
-// Streaming passes over the token-logit rows of the joint output (one 64-lane wave per
-// lattice node):
-//   row statistics — log-softmax normaliser of the V token logits, plus the blank and
-//                    label logits (the per-node log-softmax of the page "tdt-loss: add
-//                    TDT loss kernel", comment "What's in it");
-//   gradient       — d loss / d token logit for every column of every node, zeros at
-//                    padded nodes, written in the logits' dtype (the fused gradient
-//                    kernel of the same comment).
+// Streaming passes over the token-logit rows of the joint output:
+//   row partials — per row segment, the log-sum-exp partial of the V token logits
+//                  (the per-node log-softmax of the page "tdt-loss: add TDT loss
+//                  kernel", comment "What's in it"), plus the blank and label logits;
+//   gradient     — d loss / d token logit for every column of every node, zeros at
+//                  padded nodes, written in the logits' dtype (the fused gradient
+//                  kernel of the same comment).
 //
-// Rows are read in place, whatever their alignment: a wave covers the row with the
-// 16-byte aligned chunks that overlap it (an aligned chunk holding a byte of the row
-// never leaves that row's page), masks the head and tail slots, and writes partial
-// chunks slot by slot.
+// A row of V elements is covered by the 16-byte aligned chunks that overlap it (an
+// aligned chunk holding a byte of the row never leaves that row's page); head and tail
+// slots are masked on reads and written slot by slot.  A row is split into `nseg`
+// segments of 64 x NCH chunks, one 64-lane wave per segment, so that a wave keeps at
+// most 8 chunks (32 VGPRs) of raw data in flight and many waves fit on each SIMD.
 #pragma once
 
 #include "tdt_common.h"
 
 namespace tdt {
 
-constexpr int kRowsPerBlock = 4;  // waves (rows) per 256-thread work-group
+constexpr int kWavesPerBlock = 4;  // 256-thread work-groups
 
 template <typename TI>
 __device__ __forceinline__ uint4 neg_inf_chunk() {
@@ -25,19 +25,83 @@ __device__ __forceinline__ uint4 neg_inf_chunk() {
   return make_uint4(w, w, w, w);
 }
 
-// Statistics of one token row: mL = f32(max * log2e), K = log2 sum_v 2^(h_v log2e - mL),
-// lse = (mL + K) ln 2, and the blank / label logits.
+// Running maximum of the raw chunk words, in a form that shares no arithmetic with the
+// float decode of the exp pass (so the compiler keeps only the raw words alive).
+//   fp32: float max;  fp16: packed half max;  bf16: packed int16 max of order-preserving
+//   keys (negative values get their magnitude bits flipped).
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+
+template <typename TI>
+struct MaxAcc;
+
+template <>
+struct MaxAcc<F32> {
+  float m = -__builtin_inff();
+  __device__ __forceinline__ void add(uint32_t w) { m = fmaxf(m, __uint_as_float(w)); }
+  __device__ __forceinline__ float value() const { return m; }
+};
+
+template <>
+struct MaxAcc<F16> {
+  h16x2 m = {(_Float16)-__builtin_inff(), (_Float16)-__builtin_inff()};
+  __device__ __forceinline__ void add(uint32_t w) {
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(h16x2, w));
+  }
+  __device__ __forceinline__ float value() const { return fmaxf((float)m.x, (float)m.y); }
+};
+
+template <>
+struct MaxAcc<BF16> {
+  s16x2 m = {(short)-32768, (short)-32768};
+  __device__ __forceinline__ void add(uint32_t w) {
+    const s16x2 x = __builtin_bit_cast(s16x2, w);
+    const s16x2 key = x ^ ((x >> (short)15) & (short)0x7fff);
+    m = __builtin_elementwise_max(m, key);
+  }
+  __device__ __forceinline__ float value() const {
+    const short k = m.x > m.y ? m.x : m.y;
+    const short x = k ^ ((k >> 15) & 0x7fff);
+    return __uint_as_float(((uint32_t)(uint16_t)x) << 16);
+  }
+};
+
+// Row geometry shared by the two passes.
+struct RowCover {
+  const uint4* base;  // first 16-byte chunk overlapping the row
+  int head;           // elements of chunk 0 before the row starts
+  int nch;            // chunks overlapping the row
+};
+
+template <typename TI>
+__device__ __forceinline__ RowCover row_cover(const void* row, int V) {
+  constexpr int EPC = TI::kEpc;
+  const uintptr_t a = (uintptr_t)row;
+  RowCover rc;
+  rc.base = (const uint4*)(a & ~(uintptr_t)15);
+  rc.head = (int)((a & 15) / sizeof(typename TI::T));
+  rc.nch = (rc.head + V + EPC - 1) / EPC;
+  return rc;
+}
+
+// Partial log-sum-exp of one row segment.  Writes, per (node, segment):
+//   part[2*seg] = mL = f32(max * log2e), part[2*seg + 1] = sum 2^(h log2e - mL)
+// (floats, in a [positions][2*nseg] array), and the blank / label logits into rstat.
 template <typename TI, int NCH>
-__global__ __launch_bounds__(256) void k_row_stats(const Params p) {
+__global__ __launch_bounds__(256) void k_row_partial(const Params p) {
   constexpr int EPC = TI::kEpc;
   using ET = typename TI::T;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t g = (int64_t)xcd_block(blockIdx.x, gridDim.x) * kRowsPerBlock + wv;
+  const int64_t g = (int64_t)xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
+  const int nseg = p.nseg;
+  const int64_t node = g / nseg;
+  const int seg = (int)(g - node * nseg);
   const int64_t per = (int64_t)p.KD * p.WP;
-  const int b = (int)(g / per);
+  const int b = (int)(node / per);
   if (b >= p.B) return;
-  const int64_t rem = g - (int64_t)b * per;
+  const int64_t rem = node - (int64_t)b * per;
   const int k = (int)(rem / p.WP);
   const int i = (int)(rem - (int64_t)k * p.WP);
   const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
@@ -47,7 +111,6 @@ __global__ __launch_bounds__(256) void k_row_stats(const Params p) {
   const int u = diag_ulo(k, T) + i;
   if (u > min(k, U)) return;
   const int t = k - u;
-  const int64_t pos = node_pos(p, b, k, i);
 
   int y = -1;
   if (u < U) {
@@ -55,102 +118,85 @@ __global__ __launch_bounds__(256) void k_row_stats(const Params p) {
     if (yy >= 0 && yy < p.V) y = (int)yy;
   }
   const int V = p.V;
-  const char* row = (const char*)p.tok + (int64_t)sizeof(ET) * ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
-  const uintptr_t a = (uintptr_t)row;
-  const uint4* base = (const uint4*)(a & ~(uintptr_t)15);
-  const int head = (int)((a & 15) / sizeof(ET));
-  const int nch = (head + V + EPC - 1) / EPC;
-  const int cb = (head + p.blank) / EPC, sb = (head + p.blank) % EPC;
-  const int cy = y >= 0 ? (head + y) / EPC : -1, sy = y >= 0 ? (head + y) % EPC : 0;
+  const ET* row = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
+  const RowCover rc = row_cover<TI>(row, V);
+  const int c0 = seg * 64 * NCH;
 
-  float m = -__builtin_inff();
-  float mL = -__builtin_inff();
-  float acc = 0.f;
-  float hb = 0.f, hy = 0.f;
-  bool own_b = false, own_y = false;
-  for (int c0 = 0; c0 < nch; c0 += 64 * NCH) {
-    uint4 v[NCH];
+  uint4 v[NCH];
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = c0 + lane + 64 * j;
-      v[j] = c < nch ? base[c] : neg_inf_chunk<TI>();
-    }
+  for (int j = 0; j < NCH; ++j) {
+    const int c = c0 + lane + 64 * j;
+    v[j] = c < rc.nch ? rc.base[c] : neg_inf_chunk<TI>();
+  }
+  float* rs = (float*)(p.rstat + rem + (int64_t)b * per);
+  const int cb = (rc.head + p.blank) / EPC, sb = (rc.head + p.blank) % EPC;
+  const int cy = y >= 0 ? (rc.head + y) / EPC : -1, sy = y >= 0 ? (rc.head + y) % EPC : 0;
+  MaxAcc<TI> mx;
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = c0 + lane + 64 * j;
-      if (c == 0 || c == nch - 1) {
-#pragma unroll
-        for (int s = 0; s < EPC; ++s) {
-          const int e = c * EPC + s - head;
-          if (e < 0 || e >= V) chunk_set<TI>(v[j], s, TI::kNegInf);
-        }
-      }
-      if (c == cb) {
-        hb = TI::get(v[j], sb);
-        own_b = true;
-      }
-      if (c == cy) {
-        hy = TI::get(v[j], sy);
-        own_y = true;
-      }
-    }
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-#pragma unroll
-      for (int s = 0; s < EPC; ++s) mx = fmaxf(mx, TI::get(v[j], s));
-    }
-    mx = wave_max_f32(mx);
-    if (mx > m) {  // wave-uniform
-      const float mLn = mx * kLog2e;
-      acc = acc * __builtin_amdgcn_exp2f(mL - mLn);
-      m = mx;
-      mL = mLn;
-    }
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
+  for (int j = 0; j < NCH; ++j) {
+    const int c = c0 + lane + 64 * j;
+    if (c == 0 || c == rc.nch - 1) {
 #pragma unroll
       for (int s = 0; s < EPC; ++s) {
-        const float e2 = __builtin_amdgcn_exp2f(fmaf(TI::get(v[j], s), kLog2e, -mL));
-        if ((s & 3) == 0) a0 += e2;
-        else if ((s & 3) == 1) a1 += e2;
-        else if ((s & 3) == 2) a2 += e2;
-        else a3 += e2;
+        const int e = c * EPC + s - rc.head;
+        if (e < 0 || e >= V) chunk_set<TI>(v[j], s, TI::kNegInf);
       }
     }
-    acc += (a0 + a1) + (a2 + a3);
+    if (c == cb) rs[2] = TI::get(v[j], sb);
+    if (c == cy) rs[3] = TI::get(v[j], sy);
+    mx.add(v[j].x);
+    mx.add(v[j].y);
+    mx.add(v[j].z);
+    mx.add(v[j].w);
   }
-  const double S = wave_sum_f64((double)acc);
-  float* rs = (float*)(p.rstat + pos);
+  // lane-local exp sum relative to the lane's own maximum
+  const float mLl = mx.value() * kLog2e;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+#pragma unroll
+    for (int s = 0; s < EPC; ++s) {
+      const float e2 = __builtin_amdgcn_exp2f(fmaf(TI::get(v[j], s), kLog2e, -mLl));
+      if ((s & 3) == 0) a0 += e2;
+      else if ((s & 3) == 1) a1 += e2;
+      else if ((s & 3) == 2) a2 += e2;
+      else a3 += e2;
+    }
+  }
+  float acc = (a0 + a1) + (a2 + a3);
+  if (!(mLl > -__builtin_inff())) acc = 0.f;  // a lane holding only masked slots
+  const float mL = wave_max_f32(mLl);
+  const float scaled = acc > 0.f ? acc * __builtin_amdgcn_exp2f(mLl - mL) : 0.f;
+  const double S = wave_sum_f64((double)scaled);
   if (lane == 0) {
-    const double K = log2(S);
-    rs[0] = mL;
-    rs[1] = (float)K;
-    p.lse[pos] = ((double)mL + K) * kLn2;
-    if (y < 0) rs[3] = -__builtin_inff();
+    float* part = p.part + (rem + (int64_t)b * per) * 2 * nseg + 2 * seg;
+    part[0] = mL;
+    part[1] = (float)S;
+    if (seg == 0 && y < 0) rs[3] = -__builtin_inff();
   }
-  if (own_b) rs[2] = hb;
-  if (own_y) rs[3] = hy;
 }
 
-// Gradient of one token row (natural node order over the padded [B, Tmax, U1max]):
+// Gradient of one row segment (natural node order over the padded [B, Tmax, U1max]):
 //   grad_v = w O softmax(h)_v  computed as  A' * 2^(h_v log2e - mL),  A' = w O 2^-K,
 // with the blank and label columns and the D duration gradients taken from the per-node
 // record (computed in float64 from the lattice).  Padded nodes and utterances without
 // gradient get zeros.  ALIGNED: the logits row and the gradient row have the same
-// address modulo 16 bytes (then both use the same chunks).
+// address modulo 16 bytes (then both use the same chunks); otherwise each lane walks
+// single elements.
 template <typename TI, int NCH, bool ALIGNED>
 __global__ __launch_bounds__(256) void k_grad(const Params p) {
   constexpr int EPC = TI::kEpc;
   using ET = typename TI::T;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t g = (int64_t)xcd_block(blockIdx.x, gridDim.x) * kRowsPerBlock + wv;
+  const int64_t g = (int64_t)xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
+  const int nseg = p.nseg;
+  const int64_t node = g / nseg;
+  const int seg = (int)(g - node * nseg);
   const int64_t per = (int64_t)p.Tmax * p.U1max;
-  const int b = (int)(g / per);
+  const int b = (int)(node / per);
   if (b >= p.B) return;
-  const int64_t rem = g - (int64_t)b * per;
+  const int64_t rem = node - (int64_t)b * per;
   const int t = (int)(rem / p.U1max);
   const int u = (int)(rem - (int64_t)t * p.U1max);
   const int V = p.V;
@@ -172,59 +218,63 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
       ycol = __float_as_int(rec[4]);
     }
   }
-  char* orow = (char*)p.gtok + (int64_t)sizeof(ET) * ((int64_t)b * p.gs0 + (int64_t)t * p.gs1 + (int64_t)u * p.gs2);
-  const char* irow = (const char*)p.tok + (int64_t)sizeof(ET) * ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
+  ET* orow = (ET*)p.gtok + ((int64_t)b * p.gs0 + (int64_t)t * p.gs1 + (int64_t)u * p.gs2);
+  const ET* irow = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
 
   if (ALIGNED) {
-    const uintptr_t a = (uintptr_t)orow;
-    uint4* obase = (uint4*)(a & ~(uintptr_t)15);
+    const RowCover oc = row_cover<TI>(orow, V);
+    uint4* obase = (uint4*)oc.base;
     const uint4* ibase = (const uint4*)(((uintptr_t)irow) & ~(uintptr_t)15);
-    const int head = (int)((a & 15) / sizeof(ET));
-    const int nch = (head + V + EPC - 1) / EPC;
+    const int head = oc.head, nch = oc.nch;
     const int cb = (head + p.blank) / EPC, sb = (head + p.blank) % EPC;
     const int cy = ycol >= 0 ? (head + ycol) / EPC : -1, sy = ycol >= 0 ? (head + ycol) % EPC : 0;
-    for (int c0 = 0; c0 < nch; c0 += 64 * NCH) {
-      uint4 v[NCH];
-      if (valid) {
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-          const int c = c0 + lane + 64 * j;
-          if (c < nch) v[j] = ibase[c];
-        }
-      }
+    const int c0 = seg * 64 * NCH;
+    uint4 v[NCH];
+    if (valid) {
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int c = c0 + lane + 64 * j;
-        if (c >= nch) continue;
-        float o[EPC];
+        if (c < nch) {
+          const u32x4 x = __builtin_nontemporal_load((const u32x4*)(ibase + c));
+          v[j] = make_uint4(x.x, x.y, x.z, x.w);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = c0 + lane + 64 * j;
+      if (c >= nch) continue;
+      float o[EPC];
+#pragma unroll
+      for (int s = 0; s < EPC; ++s)
+        o[s] = valid ? A * __builtin_amdgcn_exp2f(fmaf(TI::get(v[j], s), kLog2e, -mL)) : 0.f;
+      if (valid && c == cb) {
 #pragma unroll
         for (int s = 0; s < EPC; ++s)
-          o[s] = valid ? A * __builtin_amdgcn_exp2f(fmaf(TI::get(v[j], s), kLog2e, -mL)) : 0.f;
-        if (valid && c == cb) {
+          if (s == sb) o[s] = Gb;
+      }
+      if (valid && c == cy) {
 #pragma unroll
-          for (int s = 0; s < EPC; ++s)
-            if (s == sb) o[s] = Gb;
-        }
-        if (valid && c == cy) {
+        for (int s = 0; s < EPC; ++s)
+          if (s == sy) o[s] = Gy;
+      }
+      const int e0 = c * EPC - head;
+      if (e0 >= 0 && e0 + EPC <= V) {
+        const uint4 q = TI::pack(o);
+        __builtin_nontemporal_store(u32x4{q.x, q.y, q.z, q.w}, (u32x4*)(obase + c));
+      } else {
+        ET* oe = (ET*)(obase + c);
 #pragma unroll
-          for (int s = 0; s < EPC; ++s)
-            if (s == sy) o[s] = Gy;
-        }
-        const int e0 = c * EPC - head;
-        if (e0 >= 0 && e0 + EPC <= V) {
-          obase[c] = TI::pack(o);
-        } else {
-          ET* oe = (ET*)(obase + c);
-#pragma unroll
-          for (int s = 0; s < EPC; ++s) {
-            const int e = e0 + s;
-            if (e >= 0 && e < V) TI::store(oe, s, o[s]);
-          }
+        for (int s = 0; s < EPC; ++s) {
+          const int e = e0 + s;
+          if (e >= 0 && e < V) TI::store(oe, s, o[s]);
         }
       }
     }
   } else {
-    for (int e = lane; e < V; e += 64) {
+    const int span = 64 * NCH * EPC;
+    const int e_end = min(V, (seg + 1) * span);
+    for (int e = seg * span + lane; e < e_end; e += 64) {
       float o = 0.f;
       if (valid) {
         o = A * __builtin_amdgcn_exp2f(fmaf(TI::load(irow, e), kLog2e, -mL));
@@ -234,42 +284,39 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
       TI::store(orow, e, o);
     }
   }
-  if (lane < p.D) {
+  if (seg == 0 && lane < p.D) {
     const float gd = valid ? rec[5 + lane] : 0.f;
     TI::store(p.gdur, (int64_t)b * p.gds0 + (int64_t)t * p.gds1 + (int64_t)u * p.gds2 + lane, gd);
   }
 }
 
-// Chunks per lane of the row kernels: the smallest variant that covers a row of V
-// elements (with its misaligned head) in one pass; wider rows loop over passes.
-constexpr int kNchVariants[] = {1, 2, 4, 9, 17, 33};
-
-inline int pick_nch(int64_t V, int epc) {
+// Segment split of a row of V elements: nseg segments of 64 x nch chunks, nch <= 8.
+inline void pick_segments(int64_t V, int epc, int* nch, int* nseg) {
   const int64_t chunks = (V + epc - 1) / epc + 1;
-  for (int n : kNchVariants)
-    if (chunks <= 64 * (int64_t)n) return n;
-  return 33;
+  int64_t s = (chunks + 64 * 8 - 1) / (64 * 8);
+  int64_t n = (chunks + 64 * s - 1) / (64 * s);
+  *nseg = (int)s;
+  *nch = (int)n;
 }
 
 template <typename TI>
 hipError_t launch_rows_t(const Params& p, bool aligned, hipStream_t st, int which) {
-  const int nch = pick_nch(p.V, TI::kEpc);
+  const int nch = p.nch;
+  const int64_t nodes = which == 0 ? (int64_t)p.B * p.KD * p.WP : (int64_t)p.B * p.Tmax * p.U1max;
+  const int64_t waves = nodes * p.nseg;
+  const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
   if (which == 0) {
-    const int64_t waves = (int64_t)p.B * p.KD * p.WP;
-    const dim3 grid((unsigned)((waves + kRowsPerBlock - 1) / kRowsPerBlock));
 #define TDT_RS(N) \
-  case N: hipLaunchKernelGGL((k_row_stats<TI, N>), grid, dim3(256), 0, st, p); break;
-    switch (nch) { TDT_RS(1) TDT_RS(2) TDT_RS(4) TDT_RS(9) TDT_RS(17) default: TDT_RS(33) }
+  case N: hipLaunchKernelGGL((k_row_partial<TI, N>), grid, dim3(256), 0, st, p); break;
+    switch (nch) { TDT_RS(1) TDT_RS(2) TDT_RS(3) TDT_RS(4) TDT_RS(5) TDT_RS(6) TDT_RS(7) default: TDT_RS(8) }
 #undef TDT_RS
   } else {
-    const int64_t waves = (int64_t)p.B * p.Tmax * p.U1max;
-    const dim3 grid((unsigned)((waves + kRowsPerBlock - 1) / kRowsPerBlock));
-#define TDT_GR(N)                                                              \
-  case N:                                                                      \
-    if (aligned) hipLaunchKernelGGL((k_grad<TI, N, true>), grid, dim3(256), 0, st, p); \
-    else hipLaunchKernelGGL((k_grad<TI, N, false>), grid, dim3(256), 0, st, p);        \
+#define TDT_GR(N)                                                                           \
+  case N:                                                                                   \
+    if (aligned) hipLaunchKernelGGL((k_grad<TI, N, true>), grid, dim3(256), 0, st, p);      \
+    else hipLaunchKernelGGL((k_grad<TI, N, false>), grid, dim3(256), 0, st, p);             \
     break;
-    switch (nch) { TDT_GR(1) TDT_GR(2) TDT_GR(4) TDT_GR(9) TDT_GR(17) default: TDT_GR(33) }
+    switch (nch) { TDT_GR(1) TDT_GR(2) TDT_GR(3) TDT_GR(4) TDT_GR(5) TDT_GR(6) TDT_GR(7) default: TDT_GR(8) }
 #undef TDT_GR
   }
   return hipGetLastError();

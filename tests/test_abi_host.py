@@ -41,17 +41,19 @@ def test_status_strings():
 
 
 def test_workspace_size():
-    small = _native.workspace_size(1, 10, 5, [0, 1, 2])
-    big = _native.workspace_size(4, 200, 41, [0, 1, 2, 3, 4])
+    small = _native.workspace_size(0, 1, 10, 5, 17, [0, 1, 2])
+    big = _native.workspace_size(2, 4, 200, 41, 8193, [0, 1, 2, 3, 4])
     assert 0 < small < big
     assert big % 256 == 0
     for bad in ([], [0], [1, 1], [-1, 1], [0, 17]):
         with pytest.raises(ValueError):
-            _native.workspace_size(1, 10, 5, bad)
+            _native.workspace_size(0, 1, 10, 5, 17, bad)
     with pytest.raises(ValueError):
-        _native.workspace_size(1, 10, 8193, [0, 1])
+        _native.workspace_size(0, 1, 10, 8193, 17, [0, 1])
     with pytest.raises(ValueError):
-        _native.workspace_size(0, 10, 5, [0, 1])
+        _native.workspace_size(0, 0, 10, 5, 17, [0, 1])
+    with pytest.raises(ValueError):
+        _native.workspace_size(3, 1, 10, 5, 17, [0, 1])
 
 
 FAKE = 1 << 20  # a 256-aligned non-null address that is never dereferenced
