@@ -1,7 +1,8 @@
 """Benchmark of the TDT loss forward+backward on one MI355X.
 
-One step = one call of the C ABI (row statistics, node weights, lattice, coefficients,
-gradient pass) over one batch of the Parakeet-size workload: B=4, T=200, U=40,
+One step = one call of the C ABI (row partials, node weights, lattice, coefficients,
+gradient pass, loss reduction, in order on one stream) over one batch of the
+Parakeet-size workload: B=4, T=200, U=40,
 V=8193 (blank 8192), durations {0..4}, bf16 logits read in place as the slice
 [..., :8193] of a [4, 200, 41, 8198] joint output, sigma 0.05, reduction mean_batch.
 Inputs are seeded synthetic data resident in HBM; several input/gradient buffer sets are
@@ -10,9 +11,10 @@ cache.
 
 Prints one JSON line: value = algorithmic GB/s of the whole step (two reads of every
 valid lattice row and one write of every gradient row, V + D elements each), the
-roofline of the dominant kernel (the gradient pass, timed with HIP events recorded by
-the library between its kernels over the timed region), and the float64 CPU oracle
-timed on the host on the same workload.
+roofline of the dominant kernel (the gradient pass, timed with HIP events the library
+records on the stream right before and after its launch in every timed step), a
+per-kernel breakdown from a second loop with events between all kernels, and the
+float64 CPU oracle timed on the host on the same workload.
 """
 from __future__ import annotations
 
@@ -86,18 +88,23 @@ def main() -> int:
         if rc != 0:
             raise RuntimeError(f"tdt_loss_fwd_bwd: {_native.status_string(rc)}")
 
+    def make_events(n_steps, n_ev):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(n_steps)]
+        for row in evs:  # materialise the HIP events before a timed region
+            for e in row:
+                e.record(stream)
+        torch.cuda.synchronize()
+        return evs, [[e.cuda_event for e in row] for row in evs]
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
+    # Timed region: K steps.  The library records events[0]/[1] around the whole step
+    # and events[2]/[3] right around the gradient kernel; the step time is the host
+    # clock over the region.
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
-    for row in evs:  # materialise the HIP events on this stream before the timed region
-        for e in row:
-            e.record(stream)
-    torch.cuda.synchronize()
-    handles = [[e.cuda_event for e in row] for row in evs]
-
+    evs, handles = make_events(K, 4)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -105,21 +112,29 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
+    grad_ms = sum(row[2].elapsed_time(row[3]) for row in evs) / K  # average gradient-kernel launch
+    event_ms = sum(row[0].elapsed_time(row[1]) for row in evs) / K
 
-    names = ["row_stats", "node_weights", "lattice", "coef", "grad"]
+    # Per-kernel breakdown (diagnostic, outside the timed region): events between all
+    # kernels of the step.
+    names = ["row_partials", "node_weights", "lattice", "coef", "grad", "reduce"]
+    pevs, phandles = make_events(K, 7)
+    for i in range(K):
+        step(i, phandles[i])
+    torch.cuda.synchronize()
     phase_ms = {n: 0.0 for n in names}
-    for row in evs:
+    for row in pevs:
         for j, n in enumerate(names):
             phase_ms[n] += row[j].elapsed_time(row[j + 1]) / K
-    kernel_sum_ms = sum(phase_ms.values())
+    serial_ms = sum(phase_ms.values())
 
     alg = algorithmic_bytes(case)
     value = alg / (ms_per_step * 1e-3) / 1e9
-    # dominant kernel: the gradient pass reads every valid row once and writes every row once
+    # dominant kernel: the gradient pass reads every valid row once and writes every row
+    # once, in one launch per step
     row_bytes = (V + D) * elt
     valid = int((case.logit_lengths.cpu() * (case.label_lengths.cpu() + 1)).sum())
     grad_bytes = valid * row_bytes + B * Tm * U1 * row_bytes
-    grad_ms = phase_ms["grad"]
     achieved = grad_bytes / (grad_ms * 1e-3) / 1e9
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
@@ -159,10 +174,11 @@ def main() -> int:
                    "algorithmic_bytes": alg, "buffer_sets": len(sets)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "k_grad (gradient pass)", "kernel_ms": round(grad_ms, 4),
-                     "bytes_per_launch": grad_bytes},
+                     "kernel": "k_grad (gradient pass)",
+                     "kernel_ms": round(grad_ms, 4), "launches_per_step": 1, "bytes_per_launch": int(grad_bytes)},
+        "event_ms_per_step": round(event_ms, 4),
         "kernel_ms": {k: round(v, 4) for k, v in phase_ms.items()},
-        "kernel_sum_ms": round(kernel_sum_ms, 4),
+        "kernel_sum_ms": round(serial_ms, 4),
         "frac_of_peak_whole_step": round(value / PEAK_HBM_GBS, 4),
         "cpu_baseline": cpu,
     }

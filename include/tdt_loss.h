@@ -87,9 +87,10 @@ int tdt_loss_workspace_size(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_
 
 /*
  * TDT loss forward and backward, stream-ordered on `stream` (a hipStream_t; NULL =
- * the default stream).  The call only validates arguments on the host and enqueues
- * kernels: it never synchronises, never allocates and keeps no pointer after it
- * returns.  All pointers except `durations` and the three stride arrays are device
+ * the default stream): results are ready when work enqueued after the call on `stream`
+ * runs.  The call only validates arguments on the host and enqueues kernels (see the
+ * launch sequence below): it never synchronises, never allocates device memory and
+ * keeps no pointer after it returns.  All pointers except `durations` and the three stride arrays are device
  * pointers owned by the caller.
  *
  *   dtype            element type of logits, dur_logits, grad_logits, grad_dur_logits.
@@ -133,14 +134,20 @@ int tdt_loss_fwd_bwd(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, in
                      size_t workspace_bytes, void* stream);
 
 /*
+ * Launch sequence, all on `stream`, in order: row partials (log-sum-exp partials of the
+ * token-logit rows), node weights, lattice (alpha and beta sweeps), coefficients,
+ * gradient pass, loss reduction.  A forward-only call skips the coefficients and the
+ * gradient pass.
+ *
  * Same as tdt_loss_fwd_bwd, and additionally records caller-created events (hipEvent_t
- * handles) on `stream` at the kernel boundaries, for profiling:
- *   events[0] before the row-statistics kernel, events[1] after it, events[2] after the
- *   node-weight kernel, events[3] after the lattice kernel, events[4] after the
- *   coefficient kernel (or the loss reduction of a forward-only call), events[5] after
- *   the gradient kernel.
- * num_events must be 6; a NULL entry is skipped.  Intended for benchmarks and tools
- * that attribute time per kernel (the events themselves cost a few microseconds).
+ * handles on the device of `stream`; NULL entries are skipped) on `stream`, for tools
+ * that attribute time per kernel:
+ *   num_events == 4: events[0] before the first kernel, [1] after the last one, [2]
+ *     right before the gradient pass and [3] right after it;
+ *   num_events == 7: events[0] before the row partials, [1] after them, [2] after the
+ *     node weights, [3] after the lattice, [4] after the coefficients, [5] after the
+ *     gradient pass, [6] after the loss reduction.
+ * Any other count (or events == NULL) returns TDT_ERR_INVALID_ARGUMENT.
  */
 int tdt_loss_fwd_bwd_timed(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,
                            const void* logits, const int64_t* logits_strides, const void* dur_logits,

@@ -95,12 +95,13 @@ def fwd_bwd_raw(dtype, B, T_max, U1_max, V, logits, lstr, dur, dstr, D, labels, 
                 durations, blank, sigma, reduction, loss, glog, gstr, gdur, gdstr, status, ws, ws_bytes,
                 stream, events=None) -> int:
     """Direct call with raw integers / pointers (device addresses as ints, None for NULL).
-    With ``events`` (6 hipEvent_t handles as ints) the timed entry point is used."""
+    With ``events`` (4 or 7 hipEvent_t handles as ints, see tdt_loss_fwd_bwd_timed) the
+    timed entry point is used."""
     extra = ()
     fn = lib().tdt_loss_fwd_bwd
     if events is not None:
         fn = lib().tdt_loss_fwd_bwd_timed
-        extra = ((ctypes.c_void_p * 6)(*events), 6)
+        extra = ((ctypes.c_void_p * len(events))(*events), len(events))
     return fn(
         int(dtype), int(B), int(T_max), int(U1_max), int(V),
         logits, i64_array(lstr), dur, i64_array(dstr), int(D),

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/tdt_loss.h: argument validation, workspace
-// layout and the stream-ordered launch sequence
-//   row statistics -> node weights -> lattice (alpha || beta) -> coefficients -> gradient.
+// layout and the launch sequence.  On the caller's stream the kernels run
+//   row partials -> node weights -> lattice (alpha || beta) -> coefficients -> gradient
+//   -> loss reduction.
 #include <math.h>
 #include <string.h>
 
@@ -88,7 +89,7 @@ bool aligned_to(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 }  // namespace
 
-extern "C" int tdt_loss_abi_version(void) { return 1; }
+extern "C" int tdt_loss_abi_version(void) { return 2; }
 
 extern "C" const char* tdt_loss_status_string(int status) {
   switch (status) {
@@ -123,7 +124,7 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
                  const int64_t* label_lengths, const int32_t* durations, int32_t blank, double sigma,
                  int32_t reduction, float* loss_out, void* grad_logits, const int64_t* grad_strides,
                  void* grad_dur_logits, const int64_t* grad_dur_strides, int32_t* utt_status, void* workspace,
-                 size_t workspace_bytes, void* stream, void* const* events) {
+                 size_t workspace_bytes, void* stream, void* const* events, int32_t num_events) {
   if (dtype < 0 || dtype > 2) return TDT_ERR_UNSUPPORTED_DTYPE;
   if (reduction < 0 || reduction > 4) return TDT_ERR_INVALID_ARGUMENT;
   if (!logits || !logits_strides || !dur_logits || !dur_strides || !labels || !logit_lengths || !label_lengths ||
@@ -183,6 +184,8 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
   p.lab_stride = labels_stride;
   p.Tlen = logit_lengths;
   p.Ulen = label_lengths;
+  p.Btot = p.B;
+  p.Ulen_tot = label_lengths;
   p.loss = loss_out;
   p.ustatus = utt_status;
   if (grads) {
@@ -222,29 +225,29 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
   }
 
   hipStream_t st = (hipStream_t)stream;
-  auto mark = [&](int i) {
-    if (events && events[i]) (void)hipEventRecord((hipEvent_t)events[i], st);
+  auto rows = [&](const Params& q, int which, hipStream_t s) {
+    return dtype == 0 ? tdt::launch_rows_f32(q, aligned, s, which)
+                      : (dtype == 1 ? tdt::launch_rows_f16(q, aligned, s, which)
+                                    : tdt::launch_rows_bf16(q, aligned, s, which));
   };
-  auto rows = [&](int which) {
-    return dtype == 0 ? tdt::launch_rows_f32(p, aligned, st, which)
-                      : (dtype == 1 ? tdt::launch_rows_f16(p, aligned, st, which) : tdt::launch_rows_bf16(p, aligned, st, which));
+  // events: 4 = {start, end, before the gradient pass, after it}; 7 = phase boundaries
+  const bool phases = num_events == 7;
+  auto rec = [&](int i) {
+    if (events && i < num_events && events[i]) (void)hipEventRecord((hipEvent_t)events[i], st);
   };
-  mark(0);
-  if (rows(0) != hipSuccess) return TDT_ERR_HIP;
-  mark(1);
+  rec(0);
+  if (rows(p, 0, st) != hipSuccess) return TDT_ERR_HIP;
+  if (phases) rec(1);
   if (tdt::launch_lattice_side(p, 0, st) != hipSuccess) return TDT_ERR_HIP;
-  mark(2);
+  if (phases) rec(2);
   if (tdt::launch_lattice_side(p, 1, st) != hipSuccess) return TDT_ERR_HIP;
-  mark(3);
-  if (grads) {
-    if (tdt::launch_lattice_side(p, 2, st) != hipSuccess) return TDT_ERR_HIP;
-    mark(4);
-    if (rows(1) != hipSuccess) return TDT_ERR_HIP;
-  } else {
-    if (tdt::launch_lattice_side(p, 3, st) != hipSuccess) return TDT_ERR_HIP;
-    mark(4);
-  }
-  mark(5);
+  if (phases) rec(3);
+  if (grads && tdt::launch_lattice_side(p, 2, st) != hipSuccess) return TDT_ERR_HIP;
+  rec(phases ? 4 : 2);
+  if (grads && rows(p, 1, st) != hipSuccess) return TDT_ERR_HIP;
+  rec(phases ? 5 : 3);
+  if (tdt::launch_lattice_side(p, 3, st) != hipSuccess) return TDT_ERR_HIP;
+  rec(phases ? 6 : 1);
   return TDT_OK;
 }
 
@@ -261,7 +264,7 @@ extern "C" int tdt_loss_fwd_bwd(int32_t dtype, int64_t B, int64_t T_max, int64_t
   return fwd_bwd_impl(dtype, B, T_max, U1_max, V, logits, logits_strides, dur_logits, dur_strides, num_durations,
                       labels, labels_stride, logit_lengths, label_lengths, durations, blank, sigma, reduction,
                       loss_out, grad_logits, grad_strides, grad_dur_logits, grad_dur_strides, utt_status, workspace,
-                      workspace_bytes, stream, nullptr);
+                      workspace_bytes, stream, nullptr, 0);
 }
 
 extern "C" int tdt_loss_fwd_bwd_timed(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,
@@ -274,9 +277,9 @@ extern "C" int tdt_loss_fwd_bwd_timed(int32_t dtype, int64_t B, int64_t T_max, i
                                       const int64_t* grad_dur_strides, int32_t* utt_status, void* workspace,
                                       size_t workspace_bytes, void* stream, void* const* events,
                                       int32_t num_events) {
-  if (!events || num_events != 6) return TDT_ERR_INVALID_ARGUMENT;
+  if (!events || (num_events != 4 && num_events != 7)) return TDT_ERR_INVALID_ARGUMENT;
   return fwd_bwd_impl(dtype, B, T_max, U1_max, V, logits, logits_strides, dur_logits, dur_strides, num_durations,
                       labels, labels_stride, logit_lengths, label_lengths, durations, blank, sigma, reduction,
                       loss_out, grad_logits, grad_strides, grad_dur_logits, grad_dur_strides, utt_status, workspace,
-                      workspace_bytes, stream, events);
+                      workspace_bytes, stream, events, num_events);
 }

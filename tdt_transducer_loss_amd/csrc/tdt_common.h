@@ -43,6 +43,11 @@ struct Params {
   int64_t lab_stride;
   const int64_t* Tlen;
   const int64_t* Ulen;
+  // The kernels of one call may see a group of utterances (all pointers above and
+  // below offset to the group's first utterance, B = group size); the reduction
+  // weights use the whole batch: Btot utterances with label lengths Ulen_tot.
+  int Btot;
+  const int64_t* Ulen_tot;
   // outputs
   float* loss;
   int32_t* ustatus;

@@ -18,14 +18,18 @@
 namespace tdt {
 
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x3v __attribute__((ext_vector_type(3)));
+// Pointer into LDS (address space 3): stores and loads through it are ds_* operations
+// and never wait on outstanding global loads.
+typedef __attribute__((address_space(3))) int lds_int;
 
 // Reduction weight w_b of utterance b (d reduced loss / d loss_b).
 __device__ double reduction_weight(const Params& p, int b, int64_t sumU) {
   switch (p.red) {
-    case 3: return 1.0 / (double)p.B;  // mean_batch
-    case 2: {                          // mean
+    case 3: return 1.0 / (double)p.Btot;  // mean_batch
+    case 2: {                             // mean
       const int64_t U = p.Ulen[b];
-      return 1.0 / ((double)p.B * (double)(U > 1 ? U : 1));
+      return 1.0 / ((double)p.Btot * (double)(U > 1 ? U : 1));
     }
     case 4: return 1.0 / (double)(sumU > 1 ? sumU : 1);  // mean_volume
     default: return 1.0;                                 // none, sum
@@ -241,7 +245,7 @@ struct WRec {
 // record reads return zero (buffer range check).  `prog` (LDS) receives the step index
 // for the L2 warm-up waves.
 template <int DM, int R, bool SW, bool ALPHA>
-__device__ void sweep(const Params& p, int b, int T, int U, double* xm, int* xe, volatile int* prog) {
+__device__ void sweep(const Params& p, int b, int T, int U, double* xm, int* xe, lds_int* prog) {
   constexpr int NW = 2 * DM + 1;
   constexpr int S = ring_size<DM>();
   constexpr int RWB = rec_bytes(DM);
@@ -266,27 +270,36 @@ __device__ void sweep(const Params& p, int b, int T, int U, double* xm, int* xe,
     for (int r = 0; r < R; ++r)
       if (tid * R + r == U) h[r][S - 1] = ext_one();  // beta(T, U): the terminal
   }
-  WRec<DM> wb[3][R];
+  // NB record buffers, prefetched NB-1 steps ahead (NB divides the unroll length S)
+  constexpr int NB = (DM <= 4 && R == 1) ? S : 3;
+  WRec<DM> wb[NB][R];
 
   auto load_w = [&](int ks, WRec<DM> (&w)[R]) {
     const int k = ALPHA ? ks : nsteps - 1 - ks;
     const int base = k * WP - diag_ulo(k, T);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int off = (base + tid * R + r) * RWB;
+      int off = (base + tid * R + r) * RWB;
+      asm volatile("" : "+v"(off));  // keep the per-chunk constants in the instruction offset
+      constexpr int NQ = WRec<DM>::NQ;
 #pragma unroll
-      for (int j = 0; j < WRec<DM>::NQ; ++j) w[r].q[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16 * j, 0, 0);
+      for (int j = 0; j < NQ - 1; ++j) w[r].q[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16 * j, 0, 0);
+      // the record holds 12*NW bytes (NW odd): its last 16-byte word ends with 4 bytes of
+      // padding, which are not loaded
+      const u32x3v last = __builtin_amdgcn_raw_buffer_load_b96(wr, off + 16 * (NQ - 1), 0, 0);
+      w[r].q[NQ - 1] = u32x4v{last.x, last.y, last.z, 0u};
     }
   };
 
-  load_w(0, wb[0]);
-  if (nsteps > 1) load_w(1, wb[1]);
+#pragma unroll
+  for (int j = 0; j < NB - 1; ++j)
+    if (j < nsteps) load_w(j, wb[j]);
   for (int k0 = 0; k0 < nsteps; k0 += S) {
 #pragma unroll
     for (int ph = 0; ph < S; ++ph) {
       const int ks = k0 + ph;
       if (ks >= nsteps) break;
-      if (ks + 2 < nsteps) load_w(ks + 2, wb[(ph + 2) % 3]);
+      if (ks + NB - 1 < nsteps) load_w(ks + NB - 1, wb[(ph + NB - 1) % NB]);
       const int k = ALPHA ? ks : nsteps - 1 - ks;
       const int base = k * WP - diag_ulo(k, T);
       Ext nv[R];
@@ -294,7 +307,7 @@ __device__ void sweep(const Params& p, int b, int T, int U, double* xm, int* xe,
       for (int r = 0; r < R; ++r) {
         const int u = tid * R + r, t = k - u;
         const bool act = (unsigned)t < (unsigned)T && u <= U;
-        const WRec<DM>& w = wb[ph % 3][r];
+        const WRec<DM>& w = wb[ph % NB][r];
         Ext terms[NW];
 #pragma unroll
         for (int d = 1; d <= DM; ++d) terms[d - 1] = ext_mul(h[r][(ph - d + 4 * S) % S], w.get(d - 1));
@@ -332,7 +345,7 @@ __device__ void sweep(const Params& p, int b, int T, int U, double* xm, int* xe,
 #pragma unroll
       for (int r = 0; r < R; ++r) h[r][ph] = nv[r];
       nb[ph] = exchange<SW>(ALPHA ? nv[R - 1] : nv[0], ALPHA, ph & 1, xm, xe);
-      if (SW) *prog = ks;
+      if (SW) __hip_atomic_store(prog, ks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   }
   if (ALPHA && tid * R <= U && U < tid * R + R) {
@@ -358,14 +371,15 @@ __device__ void sweep(const Params& p, int b, int T, int U, double* xm, int* xe,
 // most kLead diagonals ahead of it (the chain never waits for them).
 constexpr int kLead = 48;
 
-__device__ void l2_warm(const Params& p, int b, int nsteps, bool alpha, volatile int* prog) {
+__device__ void l2_warm(const Params& p, int b, int nsteps, bool alpha, lds_int* prog) {
   const int hl = threadIdx.x - 64, nh = blockDim.x - 64;
   const int64_t dbytes = (int64_t)p.WP * p.RW;  // one diagonal of records
   const int lines = (int)((dbytes + 127) / 128);
   const char* base = (alpha ? p.win : p.wout) + (int64_t)b * p.KD * dbytes;
   uint32_t acc = 0;
   for (int ks = 0; ks < nsteps; ++ks) {
-    while (ks > *prog + kLead) __builtin_amdgcn_s_sleep(2);
+    while (ks > __hip_atomic_load(prog, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + kLead)
+      __builtin_amdgcn_s_sleep(2);
     const int k = alpha ? ks : nsteps - 1 - ks;
     const char* blk = base + (int64_t)k * dbytes;
     for (int l = hl; l < lines; l += nh) acc += *(const uint32_t*)(blk + (int64_t)l * 128);
@@ -399,7 +413,7 @@ __global__ __launch_bounds__(SW ? 256 : 1024) void k_lattice(const Params p) {
   if (__syncthreads_or(bad)) status |= 4;
   if (dir == 1 && p.red == 4) {
     unsigned long long part = 0;
-    for (int bb = tid; bb < p.B; bb += nt) part += (unsigned long long)p.Ulen[bb];
+    for (int bb = tid; bb < p.Btot; bb += nt) part += (unsigned long long)p.Ulen_tot[bb];
     if (part) atomicAdd(&s_sumU, part);
   }
   __syncthreads();
@@ -420,13 +434,13 @@ __global__ __launch_bounds__(SW ? 256 : 1024) void k_lattice(const Params p) {
     return;
   }
   if (SW && tid >= 64) {
-    l2_warm(p, b, T + U, dir == 0, &s_prog);
+    l2_warm(p, b, T + U, dir == 0, (lds_int*)&s_prog);
     return;
   }
   if (dir == 0)
-    sweep<DM, R, SW, true>(p, b, T, U, xm, xe, &s_prog);
+    sweep<DM, R, SW, true>(p, b, T, U, xm, xe, (lds_int*)&s_prog);
   else
-    sweep<DM, R, SW, false>(p, b, T, U, xm, xe, &s_prog);
+    sweep<DM, R, SW, false>(p, b, T, U, xm, xe, (lds_int*)&s_prog);
 }
 
 // ------------------------------------------------------------------------------------
@@ -450,7 +464,6 @@ __device__ void reduce_loss(const Params& p) {
 template <int DM>
 __global__ __launch_bounds__(256) void k_coef(const Params p) {
   constexpr int NW = 2 * DM + 1;
-  if (blockIdx.x == 0 && threadIdx.x == 0) reduce_loss(p);
   const int64_t g = (int64_t)xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
   const int64_t per = (int64_t)p.KD * p.WP;
   const int b = (int)(g / per);
@@ -563,12 +576,12 @@ hipError_t launch_lattice_side(const Params& p, int which, hipStream_t st) {
       if (p.DM == 4) return launch_lattice_dm<4>(p, st);
       if (p.DM == 8) return launch_lattice_dm<8>(p, st);
       return launch_lattice_dm<16>(p, st);
-    case 2:  // coefficients + loss
+    case 2:  // coefficients
       if (p.DM == 4) hipLaunchKernelGGL((k_coef<4>), grid, dim3(256), 0, st, p);
       else if (p.DM == 8) hipLaunchKernelGGL((k_coef<8>), grid, dim3(256), 0, st, p);
       else hipLaunchKernelGGL((k_coef<16>), grid, dim3(256), 0, st, p);
       return hipGetLastError();
-    default:  // loss only
+    default:  // loss reduction over the whole batch
       hipLaunchKernelGGL(k_reduce, dim3(1), dim3(64), 0, st, p);
       return hipGetLastError();
   }

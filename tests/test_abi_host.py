@@ -37,7 +37,7 @@ def test_status_strings():
     for code in range(0, -7, -1):
         assert _native.status_string(code) != "unknown status"
     assert _native.status_string(-99) == "unknown status"
-    assert _native.lib().tdt_loss_abi_version() == 1
+    assert _native.lib().tdt_loss_abi_version() == 2
 
 
 def test_workspace_size():
@@ -94,10 +94,12 @@ def test_invalid_arguments_are_rejected(over, code):
     assert _call(**over) == code
 
 
-def test_timed_entry_needs_six_events():
+@pytest.mark.parametrize("n_events", [0, 1, 2, 3, 5, 6, 8, 11])
+def test_timed_entry_rejects_bad_event_lists(n_events):
     lib = _native.lib()
     i64 = _native.i64_array
+    evs = (ctypes.c_void_p * max(n_events, 1))()
     rc = lib.tdt_loss_fwd_bwd_timed(2, 2, 10, 5, 9, FAKE, i64([1, 1, 1]), FAKE, i64([1, 1, 1]), 3, FAKE, 4, FAKE,
                                     FAKE, _native.i32_array([0, 1, 2]), 8, 0.0, 3, FAKE, None, None, None, None,
-                                    None, FAKE, ctypes.c_size_t(1 << 40), None, None, 6)
+                                    None, FAKE, ctypes.c_size_t(1 << 40), None, evs, n_events)
     assert rc == _native.TDT_ERR_INVALID_ARGUMENT

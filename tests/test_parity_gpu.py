@@ -152,3 +152,37 @@ def test_padding_canary_and_determinism():
     snap = (loss1.clone(), g1.clone(), gd1.clone())
     loss2, g2, gd2, _ = gpu_run(case)
     assert torch.equal(snap[0], loss2) and torch.equal(snap[1], g2) and torch.equal(snap[2], gd2)
+
+
+@pytest.mark.parametrize("n_events", [4, 7])
+def test_timed_entry_point_matches_plain_bitwise(n_events):
+    """The timed entry point (events between the kernels) produces the bits of the plain
+    entry point."""
+    from tdt_transducer_loss_amd import _native
+
+    case = config_case(3, device="cuda")
+    loss_a, ga, gda, _ = gpu_run(case)
+    snap = (loss_a.clone(), ga.clone(), gda.clone())
+    g, gd = tdt.alloc_grads_like(case.tok, case.dur)
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    B, Tm, U1, V = case.tok.shape
+    ws_bytes = tdt.workspace_size(1, B, Tm, U1, V, case.durations)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    say(f"[gpu] ragged_f16 through the timed entry point, {n_events} events")
+    rc = _native.fwd_bwd_raw(1, B, Tm, U1, V, case.tok.data_ptr(), list(case.tok.stride()[:3]),
+                             case.dur.data_ptr(), list(case.dur.stride()[:3]), case.D, case.labels.data_ptr(),
+                             case.labels.stride(0), case.logit_lengths.data_ptr(), case.label_lengths.data_ptr(),
+                             case.durations, case.blank, case.sigma, tdt.REDUCTIONS[case.reduction],
+                             loss.data_ptr(), g.data_ptr(), list(g.stride()[:3]), gd.data_ptr(),
+                             list(gd.stride()[:3]), None, ws.data_ptr(), ws_bytes,
+                             torch.cuda.current_stream().cuda_stream, events=[e.cuda_event for e in evs])
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert torch.equal(snap[0].reshape(1), loss) and torch.equal(snap[1], g) and torch.equal(snap[2], gd)
+    order = [0, 2, 3, 1] if n_events == 4 else list(range(7))  # recording order on the stream
+    times = [evs[a].elapsed_time(evs[b]) for a, b in zip(order, order[1:])]
+    assert all(x >= 0.0 for x in times)
