@@ -31,6 +31,31 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "TDT loss fwd+bwd ms and achieved HBM GB/s, B4 T200 U40 V8193 bf16"
 
 
+def measured_traffic(path: str):
+    """HBM bytes per gradient-kernel launch from a committed counter summary, or None when
+    the summary is missing or was taken on other kernel sources than the current ones."""
+    import hashlib
+
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if not line.startswith("#") and "=" in line:
+                k, v = line.split("=", 1)
+                fields[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for name in fields["hashed_files"].split():
+            with open(os.path.join(ROOT, name), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != fields["kernel_source_sha256"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -39,8 +64,12 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, help="workload id in tdt_inputs.CONFIGS")
     ap.add_argument("--rotate", type=int, default=3, help="input/gradient buffer sets cycled over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", type=str, default=None,
-                    help="JSON with measured HBM bytes per launch of the gradient kernel (from rocprofv3 --pmc)")
+    ap.add_argument("--traffic", type=str,
+                    default=os.path.join(ROOT, "profiles", "k_grad_parakeet_bf16_hbm_bytes.txt"),
+                    help="rocprofv3 counter summary holding the measured HBM bytes per gradient-kernel launch")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (calibrates the HBM byte "
+                         "counters of rocprofv3 --pmc) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -50,6 +79,16 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+        return 0
 
     import tdt_transducer_loss_amd as tdt
     from tdt_transducer_loss_amd import _native
@@ -136,10 +175,7 @@ def main() -> int:
     valid = int((case.logit_lengths.cpu() * (case.label_lengths.cpu() + 1)).sum())
     grad_bytes = valid * row_bytes + B * Tm * U1 * row_bytes
     achieved = grad_bytes / (grad_ms * 1e-3) / 1e9
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("grad_bytes_per_launch")
+    traffic = measured_traffic(args.traffic) if cfg["name"] == "parakeet_bf16" else None
 
     cpu = None
     if not args.no_cpu_baseline:
