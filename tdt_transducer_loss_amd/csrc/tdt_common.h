@@ -56,8 +56,8 @@ struct Params {
   void* gdur;
   int64_t gds0, gds1, gds2;
   // workspace, per position
-  float4* rstat;  // {mL, K, h_blank, h_label}: mL = f32(rowmax * log2e), K = log2 sum 2^(x log2e - mL)
-  float* part;    // [2 * nseg] per row segment: its mL and its sum 2^(x log2e - mL)
+  float4* rstat;  // {m, K, h_blank, h_label}: m = row maximum, K = log2 sum 2^((x - m) log2e)
+  float* part;    // [2 * nseg] per row segment: its maximum m and its sum 2^((x - m) log2e)
   double* pr;     // [NPR]: softmax(h)_blank, softmax(h)_label, softmax(g) by duration value 0..DM
   char* wout;     // [positions] weight records of the moves out of each node (RW bytes)
   char* win;      // [positions] weight records of the moves into each node
@@ -72,6 +72,7 @@ struct Params {
   double* pm;     // P as mantissa / exponent
   int* pe;
   int* uok;       // 1: gradients are written from the lattice, 0: zeros
+  int* xflag;     // 1: some move weight lies outside [2^-300, 2^300] (extended-range sweep only)
 };
 
 // ---- extended-range non-negative numbers: value = m * 2^e ----

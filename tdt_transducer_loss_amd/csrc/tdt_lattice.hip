@@ -18,6 +18,7 @@
 namespace tdt {
 
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x3v __attribute__((ext_vector_type(3)));
 // Pointer into LDS (address space 3): stores and loads through it are ds_* operations
 // and never wait on outstanding global loads.
@@ -46,6 +47,24 @@ __device__ __forceinline__ char* wrec(char* base, const Params& p, int64_t pos) 
 __device__ __forceinline__ void wrec_put(char* rec, int NW, int s, Ext w) {
   ((double*)rec)[s] = w.m;
   ((int*)(rec + 8 * NW))[s] = w.m == 0.0 ? 0 : w.e + kWBias;
+}
+
+// A move weight: values in [2^-1000, 2^1000] are stored as plain float64 numbers with a
+// zero exponent (exactly), others in extended form.  Returns true when the weight is
+// non-zero and outside [2^-300, 2^300], the range the plain-float64 sweep accepts.
+__device__ __forceinline__ bool wrec_put_weight(char* rec, int NW, int s, Ext w) {
+  if (w.m == 0.0) {
+    wrec_put(rec, NW, s, ext_zero());
+    return false;
+  }
+  const Ext n = ext_norm(w.m, w.e);  // value in [2^(e-1), 2^e)
+  if (n.e >= -999 && n.e <= 1000) {
+    ((double*)rec)[s] = ldexp(n.m, n.e);
+    ((int*)(rec + 8 * NW))[s] = kWBias;
+  } else {
+    wrec_put(rec, NW, s, n);
+  }
+  return n.e < -299 || n.e > 300;
 }
 
 __device__ __forceinline__ Ext wrec_get(const char* rec, int NW, int s) {
@@ -98,17 +117,17 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
 
   // log-sum-exp of the token logits from the row-segment partials
   const float* part = p.part + pos * 2 * p.nseg;
-  float mL = part[0];
-  for (int s = 1; s < p.nseg; ++s) mL = fmaxf(mL, part[2 * s]);
+  float mx = part[0];
+  for (int s = 1; s < p.nseg; ++s) mx = fmaxf(mx, part[2 * s]);
   double S = 0.0;
   for (int s = 0; s < p.nseg; ++s) {
     const float ps = part[2 * s + 1];
-    if (ps > 0.f) S += (double)ps * exp2((double)(part[2 * s] - mL));
+    if (ps > 0.f) S += (double)ps * exp2(((double)part[2 * s] - (double)mx) * kLog2eD);
   }
   const double K = log2(S);
-  const double L = ((double)mL + K) * kLn2;  // natural-log normaliser
+  const double L = (double)mx + K * kLn2;  // natural-log normaliser
   const float4 rs = p.rstat[pos];
-  ((float2*)(p.rstat + pos))[0] = make_float2(mL, (float)K);
+  ((float2*)(p.rstat + pos))[0] = make_float2(mx, (float)K);
   const double lb = (double)rs.z - L;
   const double ly = (u < U && rs.w > -__builtin_inff()) ? (double)rs.w - L : -__builtin_inf();
 
@@ -136,6 +155,7 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
   const Ext eb = ext_exp(lb - p.sigma);
   const Ext ey = ext_exp(ly - p.sigma);
   const int64_t ub = (int64_t)b * per;
+  bool wide = false;
 #pragma unroll
   for (int d = 0; d <= DM; ++d) {
     const bool has = p.didx[d] >= 0;
@@ -146,22 +166,23 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
       const bool inside = t + d < T;
       const bool ok = has && (inside || (t + d == T && u == U));
       const Ext wb = ok ? ext_mul(eb, ed) : ext_zero();
-      wrec_put(orec, NW, d - 1, wb);
+      wide |= wrec_put_weight(orec, NW, d - 1, wb);
       if (inside) {  // incoming slot of (t+d, u)
         const int k2 = k + d;
-        wrec_put(wrec(p.win, p, ub + (int64_t)k2 * p.WP + (u - diag_ulo(k2, T))), NW, d - 1, wb);
+        wrec_put_weight(wrec(p.win, p, ub + (int64_t)k2 * p.WP + (u - diag_ulo(k2, T))), NW, d - 1, wb);
       }
       if (t - d < 0) wrec_put(irec, NW, d - 1, ext_zero());  // no source for this slot
     }
     const bool inside = u < U && t + d < T;
     const Ext wl = (has && inside) ? ext_mul(ey, ed) : ext_zero();
-    wrec_put(orec, NW, DM + d, wl);
+    wide |= wrec_put_weight(orec, NW, DM + d, wl);
     if (inside) {  // incoming slot of (t+d, u+1)
       const int k2 = k + d + 1;
-      wrec_put(wrec(p.win, p, ub + (int64_t)k2 * p.WP + (u + 1 - diag_ulo(k2, T))), NW, DM + d, wl);
+      wrec_put_weight(wrec(p.win, p, ub + (int64_t)k2 * p.WP + (u + 1 - diag_ulo(k2, T))), NW, DM + d, wl);
     }
     if (u == 0 || t - d < 0) wrec_put(irec, NW, DM + d, ext_zero());
   }
+  if (wide) atomicOr(p.xflag + b, 1);
 }
 
 // ------------------------------------------------------------------------------------
@@ -237,6 +258,40 @@ struct WRec {
   }
 };
 
+// P = beta(0,0) of utterance b: log P, P as mantissa / exponent, the gradient flag and
+// the infeasible status bit.
+__device__ void beta_final(const Params& p, int b, Ext P) {
+  const double lp = ext_log(P);
+  p.logp[b] = lp;
+  p.pm[b] = P.m;
+  p.pe[b] = P.e;
+  const bool feasible = P.m > 0.0 && lp == lp;
+  p.uok[b] = feasible ? 1 : 0;
+  if (p.ustatus) p.ustatus[b] = (P.m > 0.0 || lp != lp) ? 0 : 8;
+}
+
+// log P from the alpha side (the thread that owns u = U, after its last alpha store):
+// the blanks that land on t = T from u = U.
+template <int DM>
+__device__ double alpha_terminal(const Params& p, int b, int T, int U) {
+  constexpr int NW = 2 * DM + 1;
+  __threadfence();
+  Ext terms[DM];
+#pragma unroll
+  for (int d = 1; d <= DM; ++d) {
+    terms[d - 1] = ext_zero();
+    const int t = T - d;
+    if (t >= 0) {
+      const int k = t + U;
+      const int64_t pos = node_pos(p, b, k, U - diag_ulo(k, T));
+      terms[d - 1] = ext_mul(xrec_get(p.ar, pos), wrec_get(wrec(p.wout, p, pos), NW, d - 1));
+    }
+  }
+  const double lp = ext_log(ext_sum(terms));
+  p.logpa[b] = lp;
+  return lp;
+}
+
 // One direction of the lattice.  ALPHA: forward sweep with the incoming records;
 // otherwise backward sweep with the node's outgoing records, beta of the terminal
 // (t = T, u = U) seeded as 1 in the ring.  Moves that leave the lattice and moves with
@@ -245,11 +300,10 @@ struct WRec {
 // record reads return zero (buffer range check).  `prog` (LDS) receives the step index
 // for the L2 warm-up waves.
 template <int DM, int R, bool SW, bool ALPHA>
-__device__ void sweep(const Params& p, int b, int T, int U, double* xm, int* xe, lds_int* prog) {
+__device__ void sweep(const Params& p, int b, int T, int U, int tid, double* xm, int* xe, lds_int* prog) {
   constexpr int NW = 2 * DM + 1;
   constexpr int S = ring_size<DM>();
   constexpr int RWB = rec_bytes(DM);
-  const int tid = threadIdx.x;
   const int nsteps = T + U;
   const int WP = p.WP;
   const int64_t nrec = (int64_t)p.KD * WP;
@@ -292,14 +346,16 @@ __device__ void sweep(const Params& p, int b, int T, int U, double* xm, int* xe,
   };
 
 #pragma unroll
-  for (int j = 0; j < NB - 1; ++j)
-    if (j < nsteps) load_w(j, wb[j]);
+  for (int j = 0; j < NB - 1; ++j) load_w(j, wb[j]);
   for (int k0 = 0; k0 < nsteps; k0 += S) {
 #pragma unroll
     for (int ph = 0; ph < S; ++ph) {
       const int ks = k0 + ph;
       if (ks >= nsteps) break;
-      if (ks + NB - 1 < nsteps) load_w(ks + NB - 1, wb[(ph + NB - 1) % NB]);
+      // unconditional: past the last step the offsets fall outside the records of this
+      // utterance and the buffer range check returns zeros (never consumed), and a
+      // conditional load would make the wait before the next use cover this load too
+      load_w(ks + NB - 1, wb[(ph + NB - 1) % NB]);
       const int k = ALPHA ? ks : nsteps - 1 - ks;
       const int base = k * WP - diag_ulo(k, T);
       Ext nv[R];
@@ -332,15 +388,7 @@ __device__ void sweep(const Params& p, int b, int T, int U, double* xm, int* xe,
         const uint64_t mb = __builtin_bit_cast(uint64_t, a.m);
         __builtin_amdgcn_raw_buffer_store_b128(u32x4v{(uint32_t)mb, (uint32_t)(mb >> 32), (uint32_t)a.e, 0u}, xr, o, 0,
                                                0);
-        if (!ALPHA && ks == nsteps - 1 && u == 0) {  // beta(0,0) = P
-          const double lp = ext_log(a);
-          p.logp[b] = lp;
-          p.pm[b] = a.m;
-          p.pe[b] = a.e;
-          const bool feasible = a.m > 0.0 && lp == lp;
-          p.uok[b] = feasible ? 1 : 0;
-          if (p.ustatus) p.ustatus[b] = (a.m > 0.0 || lp != lp) ? 0 : 8;
-        }
+        if (!ALPHA && ks == nsteps - 1 && u == 0) beta_final(p, b, a);  // beta(0,0) = P
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) h[r][ph] = nv[r];
@@ -348,52 +396,196 @@ __device__ void sweep(const Params& p, int b, int T, int U, double* xm, int* xe,
       if (SW) __hip_atomic_store(prog, ks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   }
-  if (ALPHA && tid * R <= U && U < tid * R + R) {
-    // log P from the alpha side: blanks that land on t = T from u = U
-    __threadfence();
-    Ext terms[DM];
+  if (ALPHA && tid * R <= U && U < tid * R + R) (void)alpha_terminal<DM>(p, b, T, U);
+}
+
+// ------------------------------------------------------------------------------------
+// Plain-float64 sweep (one wave, one label index per lane).  Lane u keeps its values as
+// plain float64 numbers x relative to a lane scale: value = x * 2^sc.  Every S steps
+// each lane shifts its rings and sc so that its newest value is near 1; a neighbour's
+// value arrives with the neighbour's scale and is converted once.  A step is then
+// DM + (DM + 1) fused multiply-adds on plain numbers.  Every move weight of the
+// utterance lies in [2^-300, 2^300] (checked by the node-weight kernel).  Mass lost to
+// underflow (or an overflow) cannot be seen step by step without cost; it is caught
+// afterwards by comparing log P from the two directions, each of which would lose a
+// different share of it, and the caller then redoes both with the extended-range sweep.
+// Alpha/beta records are written in extended form.
+template <int DM>
+struct WMant {  // the NW plain-float64 weights of a record (its first 8*NW bytes)
+  static constexpr int NW = 2 * DM + 1;
+  static constexpr int NQ = NW / 2;  // full 16-byte words; NW is odd
+  u32x4v q[NQ];
+  u32x2v tail;
+  __device__ __forceinline__ double get(int s) const {
+    const uint32_t lo = s < 2 * NQ ? q[s >> 1][(s & 1) * 2] : tail.x;
+    const uint32_t hi = s < 2 * NQ ? q[s >> 1][(s & 1) * 2 + 1] : tail.y;
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+  }
+};
+
+template <int DM, bool ALPHA>
+__device__ void sweep_fast(const Params& p, int b, int T, int U, int u, lds_int* prog, double* lp_out) {
+  constexpr int S = ring_size<DM>();
+  constexpr int RWB = rec_bytes(DM);
+  constexpr int NB = S;  // record buffers, prefetched NB-1 steps ahead
+  const int nsteps = T + U;
+  const int WP = p.WP;
+  const int64_t nrec = (int64_t)p.KD * WP;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((ALPHA ? p.win : p.wout) + b * nrec * RWB), (short)0, (int)(nrec * RWB), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((ALPHA ? p.ar : p.br) + b * nrec * 16), (short)0, (int)(nrec * 16), 0x00020000);
+  const unsigned Tl = u <= U ? (unsigned)T : 0u;  // node (k - u, u) is in the lattice iff k - u < Tl
+  double h[S], nb[S];
 #pragma unroll
-    for (int d = 1; d <= DM; ++d) {
-      terms[d - 1] = ext_zero();
-      const int t = T - d;
-      if (t >= 0) {
-        const int k = t + U;
-        const int64_t pos = node_pos(p, b, k, U - diag_ulo(k, T));
-        terms[d - 1] = ext_mul(xrec_get(p.ar, pos), wrec_get(wrec(p.wout, p, pos), NW, d - 1));
+  for (int s = 0; s < S; ++s) h[s] = nb[s] = 0.0;
+  int sc = 0;
+  bool started = false;  // the lane holds a non-zero value, so its scale is fixed
+  if (!ALPHA && u == U) {  // beta(T, U): the terminal
+    h[S - 1] = 1.0;
+    started = true;
+  }
+  WMant<DM> wb[NB];
+  auto load_w = [&](int ks, WMant<DM>& w) {
+    const int k = ALPHA ? ks : nsteps - 1 - ks;
+    int off = (k * WP - diag_ulo(k, T) + u) * RWB;
+    asm volatile("" : "+v"(off));
+#pragma unroll
+    for (int j = 0; j < WMant<DM>::NQ; ++j) w.q[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16 * j, 0, 0);
+    w.tail = __builtin_amdgcn_raw_buffer_load_b64(wr, off + 16 * WMant<DM>::NQ, 0, 0);
+  };
+  // past the last step the loads fall outside this utterance's records (zeros) or hit
+  // records that are never consumed; loading unconditionally keeps the wait counts of
+  // the unrolled loop exact
+#pragma unroll
+  for (int j = 0; j < NB - 1; ++j) load_w(j, wb[j]);
+  // whole blocks of S steps: steps past the last diagonal are inactive for every lane
+  for (int k0 = 0; k0 < nsteps; k0 += S) {
+    {  // keep each lane's newest value near 1 (a zero lane shifts by 0)
+      int ex;
+      (void)frexp(h[S - 1], &ex);
+      sc += ex;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        h[s] = ldexp(h[s], -ex);
+        nb[s] = ldexp(nb[s], -ex);
       }
     }
-    p.logpa[b] = ext_log(ext_sum(terms));
+#pragma unroll
+    for (int ph = 0; ph < S; ++ph) {
+      const int ks = k0 + ph;
+      load_w(ks + NB - 1, wb[(ph + NB - 1) % NB]);
+      const int k = ALPHA ? ks : nsteps - 1 - ks;
+      const bool act = (unsigned)(k - u) < Tl;
+      const WMant<DM>& w = wb[ph % NB];
+      // own-lane moves (durations 1..DM) and the neighbour's moves (durations 0..DM), as
+      // two interleaved chains each
+      double c0 = 0.0, c1 = 0.0, c2 = 0.0, c3 = 0.0;
+#pragma unroll
+      for (int d = 1; d <= DM; ++d) {
+        const double x = h[(ph - d + 4 * S) % S] * w.get(d - 1);
+        if (d & 1) c0 += x; else c1 += x;
+      }
+#pragma unroll
+      for (int d = 0; d <= DM; ++d) {
+        const double x = nb[(ph - 1 - d + 4 * S) % S] * w.get(DM + d);
+        if (d & 1) c3 += x; else c2 += x;
+      }
+      double a = (c0 + c1) + (c2 + c3);
+      if (ALPHA && ks == 0 && u == 0) {
+        a = 1.0;
+        sc = 0;
+        started = true;
+      }
+      if (!act) a = 0.0;
+      h[ph] = a;
+      {
+        int ea;
+        const double ma = frexp(a, &ea);  // (0, 0) for a zero
+        const int eo = a != 0.0 ? ea + sc : kEZ;
+        const int o = act ? (k * WP - diag_ulo(k, T) + u) * 16 : -16;
+        const uint64_t mb = __builtin_bit_cast(uint64_t, ma);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4v{(uint32_t)mb, (uint32_t)(mb >> 32), (uint32_t)eo, 0u}, xr, o, 0,
+                                               0);
+      }
+      // neighbour exchange: alpha takes lane u-1's value, beta lane u+1's
+      const long long bits = __double_as_longlong(a);
+      int lo = (int)(bits & 0xffffffffll), hi = (int)(bits >> 32), e = sc;
+      constexpr int ctl = ALPHA ? 0x138 : 0x130;  // wave_shr:1 / wave_shl:1
+      lo = __builtin_amdgcn_update_dpp(0, lo, ctl, 0xf, 0xf, false);
+      hi = __builtin_amdgcn_update_dpp(0, hi, ctl, 0xf, 0xf, false);
+      e = __builtin_amdgcn_update_dpp(0, e, ctl, 0xf, 0xf, false);
+      const double m = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
+      started = started || a != 0.0;
+      if (!started) sc = e;  // an empty lane takes the scale of its first input
+      started = started || m != 0.0;
+      nb[ph] = ldexp(m, e - sc);
+      __hip_atomic_store(prog, ks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  if (ALPHA) {
+    if (u == U) *lp_out = alpha_terminal<DM>(p, b, T, U);
+  } else if (u == 0) {  // beta(0,0) = P: the value of the last step, still in the ring
+    const int last = (nsteps - 1) % S;
+    double a = h[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s)
+      if (s == last) a = h[s];
+    int ea;
+    const double ma = frexp(a, &ea);
+    const Ext P = a != 0.0 ? Ext{ma, ea + sc} : ext_zero();
+    beta_final(p, b, P);
+    *lp_out = ext_log(P);
   }
 }
 
-// L2 warm-up for a single-wave sweep: the other waves of the work-group touch every
-// 128-byte line of the weight records of the diagonals the chain will reach next, at
-// most kLead diagonals ahead of it (the chain never waits for them).
-constexpr int kLead = 48;
+// L2 warm-up for a single-wave sweep: a helper wave touches every 128-byte line of the
+// weight records of the diagonals its chain will reach next, at most kLead diagonals
+// ahead of it (the chain never waits for it).  Loads for kBatch diagonals are issued
+// before any is consumed, so the helper advances kBatch diagonals per memory round trip
+// rather than one.
+constexpr int kLead = 64;
+constexpr int kBatch = 16;
 
-__device__ void l2_warm(const Params& p, int b, int nsteps, bool alpha, lds_int* prog) {
-  const int hl = threadIdx.x - 64, nh = blockDim.x - 64;
+__device__ void l2_warm(const Params& p, int b, int nsteps, bool alpha, int lane, lds_int* prog) {
   const int64_t dbytes = (int64_t)p.WP * p.RW;  // one diagonal of records
   const int lines = (int)((dbytes + 127) / 128);
   const char* base = (alpha ? p.win : p.wout) + (int64_t)b * p.KD * dbytes;
   uint32_t acc = 0;
-  for (int ks = 0; ks < nsteps; ++ks) {
-    while (ks > __hip_atomic_load(prog, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + kLead)
+  for (int ks0 = 0; ks0 < nsteps; ks0 += kBatch) {
+    while (ks0 + kBatch - 1 > __hip_atomic_load(prog, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + kLead)
       __builtin_amdgcn_s_sleep(2);
-    const int k = alpha ? ks : nsteps - 1 - ks;
-    const char* blk = base + (int64_t)k * dbytes;
-    for (int l = hl; l < lines; l += nh) acc += *(const uint32_t*)(blk + (int64_t)l * 128);
+    for (int l = lane; l < lines; l += kWave) {
+      uint32_t x[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int ks = ks0 + j < nsteps ? ks0 + j : nsteps - 1;
+        const int k = alpha ? ks : nsteps - 1 - ks;
+        x[j] = *(const uint32_t*)(base + (int64_t)k * dbytes + (int64_t)l * 128);
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) acc += x[j];
+    }
   }
   if (acc == 0x9e3779b9u && p.B < 0) p.uok[0] = (int)acc;  // keeps the touching loads alive
 }
 
+// Lattice kernel.  SW (U1max <= 256): one 256-thread work-group per utterance, wave 0
+// the alpha chain, wave 1 the beta chain, waves 2 and 3 their L2 warm-up.  Otherwise one
+// work-group of up to 1024 threads per (utterance, direction).  With R = 1 the chains
+// first run the plain-float64 sweep; if log P from the alpha side and from the beta side
+// differ by more than 1e-9 (rounding alone stays below 1e-12: both sides sum the same
+// probability mass in float64), both directions are redone with the extended-range sweep.
 template <int DM, int R, bool SW>
 __global__ __launch_bounds__(SW ? 256 : 1024) void k_lattice(const Params p) {
   __shared__ double xm[SW ? 1 : 2 * 1024];
   __shared__ int xe[SW ? 1 : 2 * 1024];
   __shared__ unsigned long long s_sumU;
-  __shared__ int s_prog;
-  const int b = blockIdx.x >> 1, dir = blockIdx.x & 1;
+  __shared__ int s_prog[2];
+  __shared__ double s_lp[2];
+  const int b = SW ? blockIdx.x : blockIdx.x >> 1;
+  const int dir = SW ? -1 : (blockIdx.x & 1);
+  const bool alpha_side = dir != 1, beta_side = dir != 0;
   const int tid = threadIdx.x, nt = blockDim.x;
   const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
   int status = 0;
@@ -408,39 +600,55 @@ __global__ __launch_bounds__(SW ? 256 : 1024) void k_lattice(const Params p) {
   }
   if (tid == 0) {
     s_sumU = 0;
-    s_prog = -1;
+    s_prog[0] = s_prog[1] = -1;
   }
   if (__syncthreads_or(bad)) status |= 4;
-  if (dir == 1 && p.red == 4) {
+  if (beta_side && p.red == 4) {
     unsigned long long part = 0;
     for (int bb = tid; bb < p.Btot; bb += nt) part += (unsigned long long)p.Ulen_tot[bb];
     if (part) atomicAdd(&s_sumU, part);
   }
   __syncthreads();
-  if (dir == 1 && tid == 0) p.wts[b] = reduction_weight(p, b, (int64_t)s_sumU);
+  if (beta_side && tid == 0) p.wts[b] = reduction_weight(p, b, (int64_t)s_sumU);
   const int T = (int)T64, U = (int)U64;
   if (status != 0 || T == 0) {
     if (tid == 0) {
-      if (dir == 1) {
+      if (beta_side) {
         p.logp[b] = status ? __builtin_nan("") : -__builtin_inf();
         p.pm[b] = 0.0;
         p.pe[b] = kEZ;
         p.uok[b] = 0;
         if (p.ustatus) p.ustatus[b] = status ? status : 8;
-      } else {
-        p.logpa[b] = status ? __builtin_nan("") : -__builtin_inf();
       }
+      if (alpha_side) p.logpa[b] = status ? __builtin_nan("") : -__builtin_inf();
     }
     return;
   }
-  if (SW && tid >= 64) {
-    l2_warm(p, b, T + U, dir == 0, (lds_int*)&s_prog);
-    return;
+  if constexpr (SW) {
+    const int wv = tid >> 6, lane = tid & (kWave - 1);
+    const bool alpha = (wv & 1) == 0;
+    lds_int* prog = (lds_int*)&s_prog[wv & 1];
+    if constexpr (R == 1) {
+        if (!p.xflag[b]) {
+        if (wv == 0) sweep_fast<DM, true>(p, b, T, U, lane, prog, &s_lp[0]);
+        else if (wv == 1) sweep_fast<DM, false>(p, b, T, U, lane, prog, &s_lp[1]);
+        else l2_warm(p, b, T + U, alpha, lane, prog);
+        __syncthreads();
+        const double la = s_lp[0], lb = s_lp[1];
+        if (la == lb || fabs(la - lb) <= 1e-9) return;
+        if (tid == 0) s_prog[0] = s_prog[1] = -1;
+        __syncthreads();
+      }
+    }
+    if (wv == 0) sweep<DM, R, true, true>(p, b, T, U, lane, xm, xe, prog);
+    else if (wv == 1) sweep<DM, R, true, false>(p, b, T, U, lane, xm, xe, prog);
+    else l2_warm(p, b, T + U, alpha, lane, prog);
+  } else {
+    if (dir == 0)
+      sweep<DM, R, false, true>(p, b, T, U, tid, xm, xe, (lds_int*)&s_prog[0]);
+    else
+      sweep<DM, R, false, false>(p, b, T, U, tid, xm, xe, (lds_int*)&s_prog[0]);
   }
-  if (dir == 0)
-    sweep<DM, R, SW, true>(p, b, T, U, xm, xe, (lds_int*)&s_prog);
-  else
-    sweep<DM, R, SW, false>(p, b, T, U, xm, xe, (lds_int*)&s_prog);
 }
 
 // ------------------------------------------------------------------------------------
@@ -543,13 +751,13 @@ __global__ void k_reduce(const Params p) {
 template <int DM>
 static hipError_t launch_lattice_dm(const Params& p, hipStream_t st) {
   const int u1 = p.U1max;
-  const dim3 grid(2 * p.B);
+  const dim3 grid(2 * p.B), grid_sw(p.B);
   if (u1 <= 64) {
-    hipLaunchKernelGGL((k_lattice<DM, 1, true>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_lattice<DM, 1, true>), grid_sw, dim3(256), 0, st, p);
   } else if (u1 <= 128) {
-    hipLaunchKernelGGL((k_lattice<DM, 2, true>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_lattice<DM, 2, true>), grid_sw, dim3(256), 0, st, p);
   } else if (u1 <= 256) {
-    hipLaunchKernelGGL((k_lattice<DM, 4, true>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_lattice<DM, 4, true>), grid_sw, dim3(256), 0, st, p);
   } else {
     int R = u1 <= 1024 ? 1 : u1 <= 2048 ? 2 : u1 <= 4096 ? 4 : 8;
     const int nt = ((u1 + R - 1) / R + 63) / 64 * 64;

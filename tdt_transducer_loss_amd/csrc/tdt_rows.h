@@ -86,14 +86,19 @@ __device__ __forceinline__ RowCover row_cover(const void* row, int V) {
 }
 
 // Partial log-sum-exp of one row segment.  Writes, per (node, segment):
-//   part[2*seg] = mL = f32(max * log2e), part[2*seg + 1] = sum 2^(h log2e - mL)
+//   part[2*seg] = m = segment maximum, part[2*seg + 1] = sum 2^((h - m) log2e)
 // (floats, in a [positions][2*nseg] array), and the blank / label logits into rstat.
+// Exponents are formed as (h - m) * log2e: the difference is small for the elements
+// that carry the sum, so the rounding of log2e and of the product stays far below a
+// float32 ulp of the result whatever the magnitude of the logits.
 template <typename TI, int NCH>
 __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
   constexpr int EPC = TI::kEpc;
   using ET = typename TI::T;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (blockIdx.x == 0)  // the node-weight kernel that follows sets these flags
+    for (int i = threadIdx.x; i < p.B; i += blockDim.x) p.xflag[i] = 0;
   const int64_t g = (int64_t)xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
   const int nseg = p.nseg;
   const int64_t node = g / nseg;
@@ -150,13 +155,13 @@ __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
     mx.add(v[j].w);
   }
   // lane-local exp sum relative to the lane's own maximum
-  const float mLl = mx.value() * kLog2e;
+  const float ml = mx.value();
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
 #pragma unroll
     for (int s = 0; s < EPC; ++s) {
-      const float e2 = __builtin_amdgcn_exp2f(fmaf(TI::get(v[j], s), kLog2e, -mLl));
+      const float e2 = __builtin_amdgcn_exp2f((TI::get(v[j], s) - ml) * kLog2e);
       if ((s & 3) == 0) a0 += e2;
       else if ((s & 3) == 1) a1 += e2;
       else if ((s & 3) == 2) a2 += e2;
@@ -164,20 +169,20 @@ __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
     }
   }
   float acc = (a0 + a1) + (a2 + a3);
-  if (!(mLl > -__builtin_inff())) acc = 0.f;  // a lane holding only masked slots
-  const float mL = wave_max_f32(mLl);
-  const float scaled = acc > 0.f ? acc * __builtin_amdgcn_exp2f(mLl - mL) : 0.f;
+  if (!(ml > -__builtin_inff())) acc = 0.f;  // a lane holding only masked slots
+  const float mw = wave_max_f32(ml);
+  const float scaled = acc > 0.f ? acc * __builtin_amdgcn_exp2f((ml - mw) * kLog2e) : 0.f;
   const double S = wave_sum_f64((double)scaled);
   if (lane == 0) {
     float* part = p.part + (rem + (int64_t)b * per) * 2 * nseg + 2 * seg;
-    part[0] = mL;
+    part[0] = mw;
     part[1] = (float)S;
     if (seg == 0 && y < 0) rs[3] = -__builtin_inff();
   }
 }
 
 // Gradient of one row segment (natural node order over the padded [B, Tmax, U1max]):
-//   grad_v = w O softmax(h)_v  computed as  A' * 2^(h_v log2e - mL),  A' = w O 2^-K,
+//   grad_v = w O softmax(h)_v  computed as  A' * 2^((h_v - m) log2e),  A' = w O 2^-K,
 // with the blank and label columns and the D duration gradients taken from the per-node
 // record (computed in float64 from the lattice).  Padded nodes and utterances without
 // gradient get zeros.  ALIGNED: the logits row and the gradient row have the same
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
   const int V = p.V;
 
   bool valid = false;
-  float A = 0.f, mL = 0.f, Gb = 0.f, Gy = 0.f;
+  float A = 0.f, m = 0.f, Gb = 0.f, Gy = 0.f;
   int ycol = -1;
   const float* rec = nullptr;
   if (p.uok[b]) {
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
       const int k = t + u;
       rec = p.rec + node_pos(p, b, k, u - diag_ulo(k, T)) * p.RS;
       A = rec[0];
-      mL = rec[1];
+      m = rec[1];
       Gb = rec[2];
       Gy = rec[3];
       ycol = __float_as_int(rec[4]);
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
       float o[EPC];
 #pragma unroll
       for (int s = 0; s < EPC; ++s)
-        o[s] = valid ? A * __builtin_amdgcn_exp2f(fmaf(TI::get(v[j], s), kLog2e, -mL)) : 0.f;
+        o[s] = valid ? A * __builtin_amdgcn_exp2f((TI::get(v[j], s) - m) * kLog2e) : 0.f;
       if (valid && c == cb) {
 #pragma unroll
         for (int s = 0; s < EPC; ++s)
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
     for (int e = seg * span + lane; e < e_end; e += 64) {
       float o = 0.f;
       if (valid) {
-        o = A * __builtin_amdgcn_exp2f(fmaf(TI::load(irow, e), kLog2e, -mL));
+        o = A * __builtin_amdgcn_exp2f((TI::load(irow, e) - m) * kLog2e);
         if (e == p.blank) o = Gb;
         if (e == ycol) o = Gy;
       }

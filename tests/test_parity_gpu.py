@@ -81,6 +81,13 @@ EDGE = {
                                               reduction="none"),
     "tiny_vocab": lambda: make_case(2, [8, 6], [3, 2], 2, [0, 1, 2], "f32", seed=51, reduction="none",
                                     label_high=1),
+    # logits of standard deviation 12: move weights down to about e^-160, lattice values
+    # spread over hundreds of binary orders within one anti-diagonal
+    "large_logits_plain_range": lambda: make_case(2, [60, 45], [30, 20], 33, [0, 1, 2, 3, 4], "f32", seed=53,
+                                                  scale=12.0, reduction="sum"),
+    # standard deviation 400: weights far below 2^-300 (extended-range lattice path)
+    "huge_logits_extended_range": lambda: make_case(2, [40, 31], [12, 9], 17, [0, 1, 2], "f32", seed=54,
+                                                    scale=400.0, reduction="none"),
     "ragged_padded_f16": lambda: make_case(5, None, None, 129, [0, 1, 2, 3, 4], "f16", seed=52, Tmax=70, U1max=30,
                                            T_range=(1, 70), U_range=(0, 29), reduction="mean", extra_cols=3),
 }
@@ -154,10 +161,11 @@ def test_padding_canary_and_determinism():
     assert torch.equal(snap[0], loss2) and torch.equal(snap[1], g2) and torch.equal(snap[2], gd2)
 
 
-@pytest.mark.parametrize("n_events", [4, 7])
+@pytest.mark.parametrize("n_events", [6, 7])
 def test_timed_entry_point_matches_plain_bitwise(n_events):
-    """The timed entry point (events between the kernels) produces the bits of the plain
-    entry point."""
+    """The timed entry point (6 events: the two-group schedule of the plain entry point;
+    7 events: every kernel in order on one stream) produces the bits of the plain entry
+    point."""
     from tdt_transducer_loss_amd import _native
 
     case = config_case(3, device="cuda")
@@ -183,6 +191,6 @@ def test_timed_entry_point_matches_plain_bitwise(n_events):
     torch.cuda.synchronize()
     assert rc == 0
     assert torch.equal(snap[0].reshape(1), loss) and torch.equal(snap[1], g) and torch.equal(snap[2], gd)
-    order = [0, 2, 3, 1] if n_events == 4 else list(range(7))  # recording order on the stream
+    order = [0, 2, 3, 4, 5, 1] if n_events == 6 else list(range(7))  # recording order on the stream
     times = [evs[a].elapsed_time(evs[b]) for a, b in zip(order, order[1:])]
     assert all(x >= 0.0 for x in times)
