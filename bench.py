@@ -1,8 +1,7 @@
 """Benchmark of the TDT loss forward+backward on one MI355X.
 
 One step = one call of the C ABI (row partials, node weights, lattice, coefficients,
-gradient pass, loss reduction, over two utterance groups with the lattice of each
-overlapping the streaming passes, as the library schedules them) over one batch of the
+gradient pass, loss reduction, in order on one stream) over one batch of the
 Parakeet-size workload: B=4, T=200, U=40,
 V=8193 (blank 8192), durations {0..4}, bf16 logits read in place as the slice
 [..., :8193] of a [4, 200, 41, 8198] joint output, sigma 0.05, reduction mean_batch.
@@ -13,7 +12,7 @@ cache.
 Prints one JSON line: value = algorithmic GB/s of the whole step (two reads of every
 valid lattice row and one write of every gradient row, V + D elements each), the
 roofline of the dominant kernel (the gradient pass, timed with HIP events the library
-records on the stream right before and after each of its launches in every timed step), a
+records on the stream right before and after its launch in every timed step), a
 per-kernel breakdown from a second loop with events between all kernels, and the
 float64 CPU oracle timed on the host on the same workload.
 """
@@ -141,11 +140,10 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # Timed region: K steps.  The library records events[0]/[1] around the whole step
-    # and events[2+2g]/[3+2g] right around the gradient kernel of utterance group g; the
-    # step time is the host clock over the region.
+    # and events[2]/[3] right around the gradient kernel; the step time is the host
+    # clock over the region.
     K = args.steps
-    G = 2 if B >= 2 else 1
-    evs, handles = make_events(K, 2 + 2 * G)
+    evs, handles = make_events(K, 4)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -153,7 +151,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
-    grad_ms = sum(row[2 + 2 * g].elapsed_time(row[3 + 2 * g]) for row in evs for g in range(G)) / (K * G)
+    grad_ms = sum(row[2].elapsed_time(row[3]) for row in evs) / K  # average gradient-kernel launch
     event_ms = sum(row[0].elapsed_time(row[1]) for row in evs) / K
 
     # Per-kernel breakdown (diagnostic, outside the timed region): events between all
@@ -172,11 +170,10 @@ def main() -> int:
     alg = algorithmic_bytes(case)
     value = alg / (ms_per_step * 1e-3) / 1e9
     # dominant kernel: the gradient pass reads every valid row once and writes every row
-    # once, in one launch per utterance group (the groups of the benchmark workloads hold
-    # equal work)
+    # once, in one launch per step
     row_bytes = (V + D) * elt
     valid = int((case.logit_lengths.cpu() * (case.label_lengths.cpu() + 1)).sum())
-    grad_bytes = (valid * row_bytes + B * Tm * U1 * row_bytes) / G
+    grad_bytes = valid * row_bytes + B * Tm * U1 * row_bytes
     achieved = grad_bytes / (grad_ms * 1e-3) / 1e9
     traffic = measured_traffic(args.traffic) if cfg["name"] == "parakeet_bf16" else None
 
@@ -213,8 +210,8 @@ def main() -> int:
                    "algorithmic_bytes": alg, "buffer_sets": len(sets)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "k_grad (gradient pass, one launch per utterance group)",
-                     "kernel_ms": round(grad_ms, 4), "launches_per_step": G, "bytes_per_launch": int(grad_bytes)},
+                     "kernel": "k_grad (gradient pass)",
+                     "kernel_ms": round(grad_ms, 4), "launches_per_step": 1, "bytes_per_launch": int(grad_bytes)},
         "event_ms_per_step": round(event_ms, 4),
         "kernel_ms": {k: round(v, 4) for k, v in phase_ms.items()},
         "kernel_sum_ms": round(serial_ms, 4),

@@ -134,30 +134,19 @@ int tdt_loss_fwd_bwd(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, in
                      size_t workspace_bytes, void* stream);
 
 /*
- * Launch schedule.  A forward-only call, or B = 1, runs every kernel on `stream` in
- * order: row partials (log-sum-exp partials of the token-logit rows), node weights,
- * lattice (alpha and beta sweeps), coefficients, gradient pass, loss reduction (a
- * forward-only call skips the coefficients and the gradient pass).  With gradients and
- * B >= 2 the batch is split into G = 2 groups of consecutive utterances, A = [0, B1) and
- * B = [B1, B) with B1 = ceil(B / 2): `stream` runs the row partials and node weights of A
- * then of B, then the coefficients and gradient pass of A then of B, then the loss
- * reduction; one internal stream of the library runs the lattice of each group as soon as
- * that group's node weights are done, so that it overlaps the row pass of B (group A) and
- * the gradient pass of A (group B).  The internal stream (default priority) and four
- * events are created on the first such call on a device and kept for the life of the
- * process; the event/wait sequence of a call is enqueued under a per-device lock.  The
- * call stays stream-ordered on `stream`.
+ * Launch sequence, all on `stream`, in order: row partials (log-sum-exp partials of the
+ * token-logit rows), node weights, lattice (alpha and beta sweeps), coefficients,
+ * gradient pass, loss reduction.  A forward-only call skips the coefficients and the
+ * gradient pass.
  *
  * Same as tdt_loss_fwd_bwd, and additionally records caller-created events (hipEvent_t
  * handles on the device of `stream`; NULL entries are skipped) on `stream`, for tools
  * that attribute time per kernel:
- *   num_events == 2 + 2G (G as above): events[0] before the first kernel, [1] after the
- *     last one, [2 + 2g] right before the gradient pass of group g and [3 + 2g] right
- *     after it;
- *   num_events == 7: every kernel on `stream` in order (whatever B), with events[0]
- *     before the row partials, [1] after them, [2] after the node weights, [3] after the
- *     lattice, [4] after the coefficients, [5] after the gradient pass, [6] after the
- *     loss reduction.
+ *   num_events == 4: events[0] before the first kernel, [1] after the last one, [2]
+ *     right before the gradient pass and [3] right after it;
+ *   num_events == 7: events[0] before the row partials, [1] after them, [2] after the
+ *     node weights, [3] after the lattice, [4] after the coefficients, [5] after the
+ *     gradient pass, [6] after the loss reduction.
  * Any other count (or events == NULL) returns TDT_ERR_INVALID_ARGUMENT.
  */
 int tdt_loss_fwd_bwd_timed(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,

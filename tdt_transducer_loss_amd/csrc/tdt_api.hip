@@ -1,11 +1,10 @@
 // Host side of the C ABI declared in include/tdt_loss.h: argument validation, workspace
-// layout and the launch schedule.  Per group of utterances the kernels run
-//   row partials -> node weights -> lattice (alpha || beta) -> coefficients -> gradient,
-// and the loss reduction runs once at the end.
+// layout and the launch sequence.  On the caller's stream the kernels run
+//   row partials -> node weights -> lattice (alpha || beta) -> coefficients -> gradient
+//   -> loss reduction.
 #include <math.h>
 #include <string.h>
 
-#include <mutex>
 
 #include "tdt_kernels.h"
 #include "tdt_loss.h"
@@ -89,61 +88,6 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
 }
 
 bool aligned_to(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
-
-// ---- the two-group schedule ----
-constexpr int kMaxDevices = 64;
-
-// One internal stream (default priority) and four events per device, created on the
-// first call that needs them and kept for the life of the process.  `mu` serialises the
-// enqueue sequences of calls from different host threads, which share the events.
-struct DeviceSide {
-  std::mutex mu;
-  bool ready = false;
-  hipStream_t side = nullptr;
-  hipEvent_t ev[4] = {};
-};
-DeviceSide g_side[kMaxDevices];
-
-hipError_t init_side(DeviceSide& ds) {
-  hipError_t e = hipStreamCreateWithFlags(&ds.side, hipStreamNonBlocking);
-  for (int i = 0; i < 4 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&ds.ev[i], hipEventDisableTiming);
-  ds.ready = e == hipSuccess;
-  return e;
-}
-
-// Parameters of the group of utterances [b0, b0 + nb): every per-utterance pointer is
-// offset to utterance b0; the reduction weights keep the whole batch (Btot, Ulen_tot).
-Params group_params(const Params& p, int64_t b0, int64_t nb, size_t elt) {
-  Params q = p;
-  q.B = (int)nb;
-  q.tok = (const char*)p.tok + (int64_t)elt * b0 * p.ts0;
-  q.dur = (const char*)p.dur + (int64_t)elt * b0 * p.ds0;
-  if (p.gtok) {
-    q.gtok = (char*)p.gtok + (int64_t)elt * b0 * p.gs0;
-    q.gdur = (char*)p.gdur + (int64_t)elt * b0 * p.gds0;
-  }
-  q.labels = p.labels + b0 * p.lab_stride;
-  q.Tlen = p.Tlen + b0;
-  q.Ulen = p.Ulen + b0;
-  if (p.ustatus) q.ustatus = p.ustatus + b0;
-  const int64_t off = b0 * (int64_t)p.KD * p.WP;  // first lattice position of utterance b0
-  q.rstat = p.rstat + off;
-  q.part = p.part + off * 2 * p.nseg;
-  q.pr = p.pr + off * p.NPR;
-  q.wout = p.wout + off * p.RW;
-  q.win = p.win + off * p.RW;
-  q.ar = p.ar + off * 16;
-  q.br = p.br + off * 16;
-  q.rec = p.rec + off * p.RS;
-  q.logp = p.logp + b0;
-  q.logpa = p.logpa + b0;
-  q.wts = p.wts + b0;
-  q.pm = p.pm + b0;
-  q.pe = p.pe + b0;
-  q.uok = p.uok + b0;
-  q.xflag = p.xflag + b0;
-  return q;
-}
 
 }  // namespace
 
@@ -289,59 +233,24 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
                       : (dtype == 1 ? tdt::launch_rows_f16(q, aligned, s, which)
                                     : tdt::launch_rows_bf16(q, aligned, s, which));
   };
-  auto rec = [&](int i, hipStream_t s) {
-    if (events && i < num_events && events[i]) (void)hipEventRecord((hipEvent_t)events[i], s);
+  // events: 4 = {start, end, before the gradient pass, after it}; 7 = phase boundaries
+  const bool phases = num_events == 7;
+  auto rec = [&](int i) {
+    if (events && i < num_events && events[i]) (void)hipEventRecord((hipEvent_t)events[i], st);
   };
-  const int G = (grads && B >= 2) ? 2 : 1;
-  if (G == 1 || num_events == 7) {
-    // one stream, every kernel in order (7 events: the phase boundaries)
-    const bool phases = num_events == 7;
-    rec(0, st);
-    if (rows(p, 0, st) != hipSuccess) return TDT_ERR_HIP;
-    if (phases) rec(1, st);
-    if (tdt::launch_lattice_side(p, 0, st) != hipSuccess) return TDT_ERR_HIP;
-    if (phases) rec(2, st);
-    if (tdt::launch_lattice_side(p, 1, st) != hipSuccess) return TDT_ERR_HIP;
-    if (phases) rec(3, st);
-    if (grads && tdt::launch_lattice_side(p, 2, st) != hipSuccess) return TDT_ERR_HIP;
-    rec(phases ? 4 : 2, st);
-    if (grads && rows(p, 1, st) != hipSuccess) return TDT_ERR_HIP;
-    rec(phases ? 5 : 3, st);
-    if (tdt::launch_lattice_side(p, 3, st) != hipSuccess) return TDT_ERR_HIP;
-    rec(phases ? 6 : 1, st);
-    return TDT_OK;
-  }
-
-  // Two groups A = [0, nA), B = [nA, B).  The caller's stream runs the row partials and
-  // node weights of A then of B, and the coefficients and gradient pass of A then of B;
-  // the internal stream runs the lattice of each group as soon as its node weights are
-  // done, so the lattice of A overlaps the row pass of B and the lattice of B overlaps
-  // the gradient pass of A.
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TDT_ERR_HIP;
-  DeviceSide& ds = g_side[dev];
-  std::lock_guard<std::mutex> lock(ds.mu);
-  if (!ds.ready && init_side(ds) != hipSuccess) return TDT_ERR_HIP;
-  const int64_t nA = (B + 1) / 2;
-  const Params q[2] = {group_params(p, 0, nA, elt), group_params(p, nA, B - nA, elt)};
-  rec(0, st);
-  for (int g = 0; g < 2; ++g) {
-    if (rows(q[g], 0, st) != hipSuccess) return TDT_ERR_HIP;
-    if (tdt::launch_lattice_side(q[g], 0, st) != hipSuccess) return TDT_ERR_HIP;
-    if (hipEventRecord(ds.ev[2 * g], st) != hipSuccess || hipStreamWaitEvent(ds.side, ds.ev[2 * g], 0) != hipSuccess)
-      return TDT_ERR_HIP;
-    if (tdt::launch_lattice_side(q[g], 1, ds.side) != hipSuccess) return TDT_ERR_HIP;
-    if (hipEventRecord(ds.ev[2 * g + 1], ds.side) != hipSuccess) return TDT_ERR_HIP;
-  }
-  for (int g = 0; g < 2; ++g) {
-    if (hipStreamWaitEvent(st, ds.ev[2 * g + 1], 0) != hipSuccess) return TDT_ERR_HIP;
-    if (tdt::launch_lattice_side(q[g], 2, st) != hipSuccess) return TDT_ERR_HIP;
-    rec(2 + 2 * g, st);
-    if (rows(q[g], 1, st) != hipSuccess) return TDT_ERR_HIP;
-    rec(3 + 2 * g, st);
-  }
+  rec(0);
+  if (rows(p, 0, st) != hipSuccess) return TDT_ERR_HIP;
+  if (phases) rec(1);
+  if (tdt::launch_lattice_side(p, 0, st) != hipSuccess) return TDT_ERR_HIP;
+  if (phases) rec(2);
+  if (tdt::launch_lattice_side(p, 1, st) != hipSuccess) return TDT_ERR_HIP;
+  if (phases) rec(3);
+  if (grads && tdt::launch_lattice_side(p, 2, st) != hipSuccess) return TDT_ERR_HIP;
+  rec(phases ? 4 : 2);
+  if (grads && rows(p, 1, st) != hipSuccess) return TDT_ERR_HIP;
+  rec(phases ? 5 : 3);
   if (tdt::launch_lattice_side(p, 3, st) != hipSuccess) return TDT_ERR_HIP;
-  rec(1, st);
+  rec(phases ? 6 : 1);
   return TDT_OK;
 }
 
@@ -371,8 +280,7 @@ extern "C" int tdt_loss_fwd_bwd_timed(int32_t dtype, int64_t B, int64_t T_max, i
                                       const int64_t* grad_dur_strides, int32_t* utt_status, void* workspace,
                                       size_t workspace_bytes, void* stream, void* const* events,
                                       int32_t num_events) {
-  const bool two_groups = (grad_logits != nullptr || grad_dur_logits != nullptr) && B >= 2;
-  if (!events || (num_events != (two_groups ? 6 : 4) && num_events != 7)) return TDT_ERR_INVALID_ARGUMENT;
+  if (!events || (num_events != 4 && num_events != 7)) return TDT_ERR_INVALID_ARGUMENT;
   return fwd_bwd_impl(dtype, B, T_max, U1_max, V, logits, logits_strides, dur_logits, dur_strides, num_durations,
                       labels, labels_stride, logit_lengths, label_lengths, durations, blank, sigma, reduction,
                       loss_out, grad_logits, grad_strides, grad_dur_logits, grad_dur_strides, utt_status, workspace,

@@ -81,19 +81,25 @@ __device__ __forceinline__ Ext xrec_get(const char* base, int64_t pos) {
 //   l_blank = h_blank - lse, l_label = h_{y_{u+1}} - lse, lambda = log_softmax(g(n)),
 //   W_blank(d) = exp(l_blank - sigma + lambda_d)  (d > 0; t+d < T, or t+d = T at u = U),
 //   W_label(d) = exp(l_label - sigma + lambda_d)  (u < U, t+d < T),
-// plus softmax(h)_blank, softmax(h)_label and softmax(g) for the gradient.  Every
-// record of the padded [B][KD][WP] layout is written: moves that leave the lattice,
-// absent durations, moves with no source and positions outside the utterance hold the
-// zero weight, so the sweeps read any in-range record without predicates.  Slot s of
-// the incoming record of n is written by the source of that move, or zeroed by n's own
-// thread when the source does not exist (exactly one writer per slot).
+// plus softmax(h)_blank, softmax(h)_label and softmax(g) for the gradient.  A group of
+// NG = 8, 16 or 32 lanes (at least DM + 1) works on one lattice position: lane d of the
+// group handles duration value d, lanes 0..3 the per-node exponentials, so the float64
+// work of a node is spread over its group.  Every record of the padded [B][KD][WP]
+// layout is written: moves that leave the lattice, absent durations, moves with no
+// source and positions outside the utterance hold the zero weight, so the sweeps read
+// any in-range record without predicates.  Slot s of the incoming record of n is written
+// by the source of that move, or zeroed by n itself when the source does not exist
+// (exactly one writer per slot).
 template <int DM>
 __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
   constexpr int NW = 2 * DM + 1;
-  const int64_t g = (int64_t)xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+  constexpr int NG = DM < 8 ? 8 : (DM < 16 ? 16 : 32);
+  const int64_t gt = (int64_t)xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+  const int j = threadIdx.x & (NG - 1);  // lane in the group: duration value j
+  const int64_t g = gt / NG;              // lattice position of the group
   const int64_t per = (int64_t)p.KD * p.WP;
   const int b = (int)(g / per);
-  if (b >= p.B) return;
+  if (b >= p.B) return;  // whole groups leave together
   const int64_t rem = g - (int64_t)b * per;
   const int k = (int)(rem / p.WP);
   const int i = (int)(rem - (int64_t)k * p.WP);
@@ -105,63 +111,79 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
   const bool dims = utt_dims_ok(p, T64, U64);
   const int u = dims ? diag_ulo(k, T) + i : 0;
   const bool valid = dims && k < T + U && u <= min(k, U);
+  const int d = j;
   if (!valid) {
-#pragma unroll
-    for (int s = 0; s < NW; ++s) {
-      wrec_put(orec, NW, s, ext_zero());
-      wrec_put(irec, NW, s, ext_zero());
+    if (d <= DM) {
+      if (d >= 1) {
+        wrec_put(orec, NW, d - 1, ext_zero());
+        wrec_put(irec, NW, d - 1, ext_zero());
+      }
+      wrec_put(orec, NW, DM + d, ext_zero());
+      wrec_put(irec, NW, DM + d, ext_zero());
     }
     return;
   }
   const int t = k - u;
 
-  // log-sum-exp of the token logits from the row-segment partials
+  // the duration logit of this lane, loaded first
+  const int idx = d <= DM ? p.didx[d] : -1;
+  const bool has = idx >= 0;
+  const int64_t dbase = (int64_t)b * p.ds0 + (int64_t)t * p.ds1 + (int64_t)u * p.ds2;
+  const double gl = has ? (double)load_dur(p, dbase + idx) : -__builtin_inf();
+
+  // log-sum-exp of the token logits from the row-segment partials (lane s: segment s)
   const float* part = p.part + pos * 2 * p.nseg;
-  float mx = part[0];
-  for (int s = 1; s < p.nseg; ++s) mx = fmaxf(mx, part[2 * s]);
-  double S = 0.0;
-  for (int s = 0; s < p.nseg; ++s) {
-    const float ps = part[2 * s + 1];
-    if (ps > 0.f) S += (double)ps * exp2(((double)part[2 * s] - (double)mx) * kLog2eD);
+  float ms = -__builtin_inff();
+  float ps = 0.f;
+  for (int s2 = j; s2 < p.nseg; s2 += NG) {
+    const float m2 = part[2 * s2], p2 = part[2 * s2 + 1];
+    if (p2 > 0.f) {
+      const float mn = fmaxf(ms, m2);
+      ps = (ps > 0.f ? ps * __builtin_amdgcn_exp2f((ms - mn) * kLog2e) : 0.f) +
+           p2 * __builtin_amdgcn_exp2f((m2 - mn) * kLog2e);
+      ms = mn;
+    }
   }
+  float mx = ms;
+#pragma unroll
+  for (int o = NG / 2; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, NG));
+  double S = ps > 0.f ? (double)ps * exp2(((double)ms - (double)mx) * kLog2eD) : 0.0;
+#pragma unroll
+  for (int o = NG / 2; o >= 1; o >>= 1) S += __shfl_xor(S, o, NG);
   const double K = log2(S);
   const double L = (double)mx + K * kLn2;  // natural-log normaliser
   const float4 rs = p.rstat[pos];
-  ((float2*)(p.rstat + pos))[0] = make_float2(mx, (float)K);
   const double lb = (double)rs.z - L;
   const double ly = (u < U && rs.w > -__builtin_inff()) ? (double)rs.w - L : -__builtin_inf();
 
-  const int64_t dbase = (int64_t)b * p.ds0 + (int64_t)t * p.ds1 + (int64_t)u * p.ds2;
-  double gl[DM + 1];
-  double gmax = -__builtin_inf();
-#pragma unroll
-  for (int d = 0; d <= DM; ++d) {
-    const int idx = p.didx[d];
-    gl[d] = -__builtin_inf();
-    if (idx >= 0) {
-      gl[d] = (double)load_dur(p, dbase + idx);
-      gmax = fmax(gmax, gl[d]);
-    }
-  }
-  double s = 0.0;
-#pragma unroll
-  for (int d = 0; d <= DM; ++d)
-    if (p.didx[d] >= 0) s += exp(gl[d] - gmax);
-  const double lse_g = gmax + log(s);
-
+  // lanes 0..3: exp(l_blank - sigma), exp(l_label - sigma) in extended range, and
+  // softmax(h)_blank, softmax(h)_label
+  const double xl = (j & 1) ? ly : lb;
+  Ext ex = ext_zero();
+  if (j < 2) ex = ext_exp(xl - p.sigma);
   double* pr = p.pr + pos * p.NPR;
-  pr[0] = exp(lb);
-  pr[1] = exp(ly);
-  const Ext eb = ext_exp(lb - p.sigma);
-  const Ext ey = ext_exp(ly - p.sigma);
-  const int64_t ub = (int64_t)b * per;
-  bool wide = false;
+  if (j >= 2 && j < 4) pr[j - 2] = exp(xl);
+  if (j == 0) ((float2*)(p.rstat + pos))[0] = make_float2(mx, (float)K);
+  const int base = threadIdx.x & ~(NG - 1);
+  const Ext eb = Ext{__shfl(ex.m, base, 64), __shfl(ex.e, base, 64)};
+  const Ext ey = Ext{__shfl(ex.m, base + 1, 64), __shfl(ex.e, base + 1, 64)};
+
+  // duration softmax: lambda_d = gl - gmax - log(sg)
+  double gmax = gl;
 #pragma unroll
-  for (int d = 0; d <= DM; ++d) {
-    const bool has = p.didx[d] >= 0;
-    const double lam = gl[d] - lse_g;
-    pr[2 + d] = has ? exp(lam) : 0.0;
-    const Ext ed = has ? ext_exp(lam) : ext_zero();
+  for (int o = NG / 2; o >= 1; o >>= 1) gmax = fmax(gmax, __shfl_xor(gmax, o, NG));
+  const double eg = has ? exp(gl - gmax) : 0.0;
+  double sg = eg;
+#pragma unroll
+  for (int o = NG / 2; o >= 1; o >>= 1) sg += __shfl_xor(sg, o, NG);
+  const double pd = eg / sg;
+  // exp(lambda_d) in extended range: the quotient unless it left the normal range
+  const Ext ed = !has ? ext_zero() : (gl - gmax > -700.0 ? ext_norm(pd, 0) : ext_exp(gl - gmax - log(sg)));
+
+  bool wide = false;
+  if (d <= DM) {
+    pr[2 + d] = has ? pd : 0.0;
+    const int64_t ub = (int64_t)b * per;
     if (d >= 1) {
       const bool inside = t + d < T;
       const bool ok = has && (inside || (t + d == T && u == U));
@@ -775,11 +797,14 @@ hipError_t launch_lattice_side(const Params& p, int which, hipStream_t st) {
   const int64_t n = (int64_t)p.B * p.KD * p.WP;
   const dim3 grid((unsigned)((n + 255) / 256));
   switch (which) {
-    case 0:  // node weights
-      if (p.DM == 4) hipLaunchKernelGGL((k_node_weights<4>), grid, dim3(256), 0, st, p);
-      else if (p.DM == 8) hipLaunchKernelGGL((k_node_weights<8>), grid, dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((k_node_weights<16>), grid, dim3(256), 0, st, p);
+    case 0: {  // node weights: NG lanes per position
+      const int ng = p.DM < 8 ? 8 : (p.DM < 16 ? 16 : 32);
+      const dim3 gridw((unsigned)((n * ng + 255) / 256));
+      if (p.DM == 4) hipLaunchKernelGGL((k_node_weights<4>), gridw, dim3(256), 0, st, p);
+      else if (p.DM == 8) hipLaunchKernelGGL((k_node_weights<8>), gridw, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((k_node_weights<16>), gridw, dim3(256), 0, st, p);
       return hipGetLastError();
+    }
     case 1:  // lattice
       if (p.DM == 4) return launch_lattice_dm<4>(p, st);
       if (p.DM == 8) return launch_lattice_dm<8>(p, st);

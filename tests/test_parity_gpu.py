@@ -161,11 +161,10 @@ def test_padding_canary_and_determinism():
     assert torch.equal(snap[0], loss2) and torch.equal(snap[1], g2) and torch.equal(snap[2], gd2)
 
 
-@pytest.mark.parametrize("n_events", [6, 7])
+@pytest.mark.parametrize("n_events", [4, 7])
 def test_timed_entry_point_matches_plain_bitwise(n_events):
-    """The timed entry point (6 events: the two-group schedule of the plain entry point;
-    7 events: every kernel in order on one stream) produces the bits of the plain entry
-    point."""
+    """The timed entry point (events between the kernels) produces the bits of the plain
+    entry point."""
     from tdt_transducer_loss_amd import _native
 
     case = config_case(3, device="cuda")
@@ -191,6 +190,6 @@ def test_timed_entry_point_matches_plain_bitwise(n_events):
     torch.cuda.synchronize()
     assert rc == 0
     assert torch.equal(snap[0].reshape(1), loss) and torch.equal(snap[1], g) and torch.equal(snap[2], gd)
-    order = [0, 2, 3, 4, 5, 1] if n_events == 6 else list(range(7))  # recording order on the stream
+    order = [0, 2, 3, 1] if n_events == 4 else list(range(7))  # recording order on the stream
     times = [evs[a].elapsed_time(evs[b]) for a, b in zip(order, order[1:])]
     assert all(x >= 0.0 for x in times)
