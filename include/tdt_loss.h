@@ -135,9 +135,9 @@ int tdt_loss_fwd_bwd(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, in
 
 /*
  * Launch sequence, all on `stream`, in order: row partials (log-sum-exp partials of the
- * token-logit rows), node weights, lattice (alpha and beta sweeps), coefficients,
- * gradient pass, loss reduction.  A forward-only call skips the coefficients and the
- * gradient pass.
+ * token-logit rows), node weights, lattice (alpha and beta sweeps), coefficients (which
+ * also reduce the loss), gradient pass.  A forward-only call runs a loss-reduction
+ * kernel in place of the coefficients and the gradient pass.
  *
  * Same as tdt_loss_fwd_bwd, and additionally records caller-created events (hipEvent_t
  * handles on the device of `stream`; NULL entries are skipped) on `stream`, for tools
@@ -146,7 +146,8 @@ int tdt_loss_fwd_bwd(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, in
  *     right before the gradient pass and [3] right after it;
  *   num_events == 7: events[0] before the row partials, [1] after them, [2] after the
  *     node weights, [3] after the lattice, [4] after the coefficients, [5] after the
- *     gradient pass, [6] after the loss reduction.
+ *     gradient pass, [6] after the loss reduction kernel (forward only; with gradients
+ *     [6] directly follows [5]).
  * Any other count (or events == NULL) returns TDT_ERR_INVALID_ARGUMENT.
  */
 int tdt_loss_fwd_bwd_timed(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,

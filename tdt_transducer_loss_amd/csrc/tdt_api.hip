@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/tdt_loss.h: argument validation, workspace
 // layout and the launch sequence.  On the caller's stream the kernels run
-//   row partials -> node weights -> lattice (alpha || beta) -> coefficients -> gradient
-//   -> loss reduction.
+//   row partials -> node weights -> lattice (alpha || beta) -> coefficients and loss
+//   reduction -> gradient  (forward only: ... -> lattice -> loss reduction).
 #include <math.h>
 #include <string.h>
 
@@ -249,7 +249,8 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
   rec(phases ? 4 : 2);
   if (grads && rows(p, 1, st) != hipSuccess) return TDT_ERR_HIP;
   rec(phases ? 5 : 3);
-  if (tdt::launch_lattice_side(p, 3, st) != hipSuccess) return TDT_ERR_HIP;
+  // with gradients the coefficient kernel has reduced the loss already
+  if (!grads && tdt::launch_lattice_side(p, 3, st) != hipSuccess) return TDT_ERR_HIP;
   rec(phases ? 6 : 1);
   return TDT_OK;
 }

@@ -674,7 +674,7 @@ __global__ __launch_bounds__(SW ? 256 : 1024) void k_lattice(const Params p) {
 }
 
 // ------------------------------------------------------------------------------------
-// Posteriors and the per-node record of the gradient pass (thread per node):
+// Posteriors and the per-node record of the gradient pass:
 //   gamma(e) = alpha(n) W(e) beta(dest e) / P,   O(n) = sum over moves out of n,
 //   c_blank, c_label = sums over blank / label moves, c_dur(d) = moves of duration d,
 //   grad h_blank = w (O softmax(h)_blank - c_blank), grad h_y = w (O softmax(h)_y - c_label),
@@ -691,12 +691,20 @@ __device__ void reduce_loss(const Params& p) {
   if (p.red != 0) p.loss[0] = (float)s;
 }
 
+// A group of NG lanes works on one node (as in the node weights): lane d handles the
+// blank and the label move of duration value d; the group sums give O, c_blank, c_label.
+// The first work-group also reduces the loss (the lattice has finished every log P).
 template <int DM>
 __global__ __launch_bounds__(256) void k_coef(const Params p) {
   constexpr int NW = 2 * DM + 1;
-  const int64_t g = (int64_t)xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+  constexpr int NG = DM < 8 ? 8 : (DM < 16 ? 16 : 32);
+  if (blockIdx.x == 0 && threadIdx.x == 0) reduce_loss(p);
+  const int64_t gt = (int64_t)xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+  const int j = threadIdx.x & (NG - 1);
+  const int64_t g = gt / NG;
   const int64_t per = (int64_t)p.KD * p.WP;
   const int b = (int)(g / per);
+  // whole groups leave together below: every condition depends on the position only
   if (b >= p.B) return;
   if (!p.uok[b]) return;
   const int64_t rem = g - (int64_t)b * per;
@@ -713,12 +721,9 @@ __global__ __launch_bounds__(256) void k_coef(const Params p) {
   const char* wr = wrec(p.wout, p, pos);
   const double Pm = p.pm[b];
   const int Pe = p.pe[b];
-  double gbl[DM + 1], glb[DM + 1];
-  double cb = 0.0, cl = 0.0;
-#pragma unroll
-  for (int d = 0; d <= DM; ++d) {
-    gbl[d] = 0.0;
-    glb[d] = 0.0;
+  const int d = j;
+  double gb = 0.0, gy = 0.0;  // posteriors of the blank / label move of duration d
+  if (d <= DM) {
     if (d >= 1) {
       Ext bt = ext_zero();
       if (t + d < T) {
@@ -728,39 +733,44 @@ __global__ __launch_bounds__(256) void k_coef(const Params p) {
         bt = ext_one();
       }
       const Ext gm = ext_mul(ext_mul(a, wrec_get(wr, NW, d - 1)), bt);
-      gbl[d] = ext_to_double(Ext{gm.m / Pm, gm.e - Pe});
-      cb += gbl[d];
+      gb = ext_to_double(Ext{gm.m / Pm, gm.e - Pe});
     }
     if (u < U && t + d < T) {
       const int k2 = k + d + 1;
       const Ext bt = xrec_get(p.br, node_pos(p, b, k2, u + 1 - diag_ulo(k2, T)));
       const Ext gm = ext_mul(ext_mul(a, wrec_get(wr, NW, DM + d)), bt);
-      glb[d] = ext_to_double(Ext{gm.m / Pm, gm.e - Pe});
-      cl += glb[d];
+      gy = ext_to_double(Ext{gm.m / Pm, gm.e - Pe});
     }
+  }
+  double cb = gb, cl = gy;
+#pragma unroll
+  for (int o = NG / 2; o >= 1; o >>= 1) {
+    cb += __shfl_xor(cb, o, NG);
+    cl += __shfl_xor(cl, o, NG);
   }
   const double O = cb + cl;
   const double wgt = p.wts[b];
   const double* pr = p.pr + pos * p.NPR;
-  const float4 rs = p.rstat[pos];
-  int y = -1;
-  if (u < U) y = (int)p.labels[(int64_t)b * p.lab_stride + u];
-  double Gb = wgt * (O * pr[0] - cb);
-  const double Gy = wgt * (O * pr[1] - cl);
-  if (y == p.blank) {  // both corrections land on the blank column
-    Gb -= wgt * cl;
-    y = -1;
-  }
   float* rec = p.rec + pos * p.RS;
-  rec[0] = (float)(wgt * O * exp2(-(double)rs.y));
-  rec[1] = rs.x;
-  rec[2] = (float)Gb;
-  rec[3] = (float)Gy;
-  rec[4] = __int_as_float(y);
-#pragma unroll
-  for (int d = 0; d <= DM; ++d) {
+  if (j == 0) {
+    const float4 rs = p.rstat[pos];
+    int y = -1;
+    if (u < U) y = (int)p.labels[(int64_t)b * p.lab_stride + u];
+    double Gb = wgt * (O * pr[0] - cb);
+    const double Gy = wgt * (O * pr[1] - cl);
+    if (y == p.blank) {  // both corrections land on the blank column
+      Gb -= wgt * cl;
+      y = -1;
+    }
+    rec[0] = (float)(wgt * O * exp2(-(double)rs.y));
+    rec[1] = rs.x;
+    rec[2] = (float)Gb;
+    rec[3] = (float)Gy;
+    rec[4] = __int_as_float(y);
+  }
+  if (d <= DM) {
     const int idx = p.didx[d];
-    if (idx >= 0) rec[5 + idx] = (float)(wgt * (O * pr[2 + d] - (gbl[d] + glb[d])));
+    if (idx >= 0) rec[5 + idx] = (float)(wgt * (O * pr[2 + d] - (gb + gy)));
   }
 }
 
@@ -809,11 +819,14 @@ hipError_t launch_lattice_side(const Params& p, int which, hipStream_t st) {
       if (p.DM == 4) return launch_lattice_dm<4>(p, st);
       if (p.DM == 8) return launch_lattice_dm<8>(p, st);
       return launch_lattice_dm<16>(p, st);
-    case 2:  // coefficients
-      if (p.DM == 4) hipLaunchKernelGGL((k_coef<4>), grid, dim3(256), 0, st, p);
-      else if (p.DM == 8) hipLaunchKernelGGL((k_coef<8>), grid, dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((k_coef<16>), grid, dim3(256), 0, st, p);
+    case 2: {  // coefficients (and the loss reduction): NG lanes per position
+      const int ng = p.DM < 8 ? 8 : (p.DM < 16 ? 16 : 32);
+      const dim3 gridc((unsigned)((n * ng + 255) / 256));
+      if (p.DM == 4) hipLaunchKernelGGL((k_coef<4>), gridc, dim3(256), 0, st, p);
+      else if (p.DM == 8) hipLaunchKernelGGL((k_coef<8>), gridc, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((k_coef<16>), gridc, dim3(256), 0, st, p);
       return hipGetLastError();
+    }
     default:  // loss reduction over the whole batch
       hipLaunchKernelGGL(k_reduce, dim3(1), dim3(64), 0, st, p);
       return hipGetLastError();
