@@ -449,7 +449,11 @@ template <int DM, bool ALPHA>
 __device__ void sweep_fast(const Params& p, int b, int T, int U, int u, lds_int* prog, double* lp_out) {
   constexpr int S = ring_size<DM>();
   constexpr int RWB = rec_bytes(DM);
-  constexpr int NB = S;  // record buffers, prefetched NB-1 steps ahead
+  // record buffers, prefetched NB-1 steps ahead (a few microseconds: the records stay
+  // reachable at full HBM latency even when streaming kernels evict them from L2)
+  constexpr int NB = DM <= 4 ? 2 * S : 6;  // register budget: 2*DM+1 float64 per buffer
+  constexpr int UL = NB > S ? NB : S;     // steps unrolled per iteration
+  static_assert(UL % S == 0 && UL % NB == 0, "unroll must hold whole rings and buffer rounds");
   const int nsteps = T + U;
   const int WP = p.WP;
   const int64_t nrec = (int64_t)p.KD * WP;
@@ -481,25 +485,26 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int u, lds_int*
   // the unrolled loop exact
 #pragma unroll
   for (int j = 0; j < NB - 1; ++j) load_w(j, wb[j]);
-  // whole blocks of S steps: steps past the last diagonal are inactive for every lane
-  for (int k0 = 0; k0 < nsteps; k0 += S) {
-    {  // keep each lane's newest value near 1 (a zero lane shifts by 0)
-      int ex;
-      (void)frexp(h[S - 1], &ex);
-      sc += ex;
+  // whole blocks of UL steps: steps past the last diagonal are inactive for every lane
+  for (int k0 = 0; k0 < nsteps; k0 += UL) {
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        h[s] = ldexp(h[s], -ex);
-        nb[s] = ldexp(nb[s], -ex);
+    for (int q = 0; q < UL; ++q) {
+      const int ph = q % S;  // ring slot
+      if (ph == 0) {  // keep each lane's newest value near 1 (a zero lane shifts by 0)
+        int ex;
+        (void)frexp(h[S - 1], &ex);
+        sc += ex;
+#pragma unroll
+        for (int s2 = 0; s2 < S; ++s2) {
+          h[s2] = ldexp(h[s2], -ex);
+          nb[s2] = ldexp(nb[s2], -ex);
+        }
       }
-    }
-#pragma unroll
-    for (int ph = 0; ph < S; ++ph) {
-      const int ks = k0 + ph;
-      load_w(ks + NB - 1, wb[(ph + NB - 1) % NB]);
+      const int ks = k0 + q;
+      load_w(ks + NB - 1, wb[(q + NB - 1) % NB]);
       const int k = ALPHA ? ks : nsteps - 1 - ks;
       const bool act = (unsigned)(k - u) < Tl;
-      const WMant<DM>& w = wb[ph % NB];
+      const WMant<DM>& w = wb[q % NB];
       // own-lane moves (durations 1..DM) and the neighbour's moves (durations 0..DM), as
       // two interleaved chains each
       double c0 = 0.0, c1 = 0.0, c2 = 0.0, c3 = 0.0;
