@@ -445,15 +445,24 @@ struct WMant {  // the NW plain-float64 weights of a record (its first 8*NW byte
   }
 };
 
-template <int DM, bool ALPHA>
-__device__ void sweep_fast(const Params& p, int b, int T, int U, int u, lds_int* prog, double* lp_out) {
+// Record buffers of the plain sweep: as many as fit about 240 VGPRs (R records of
+// 2*DM+1 float64 per buffer), from {12, 6, 3, 2}; 0 when even 2 do not fit in 200 (the
+// extended-range sweep is used then).
+template <int DM, int R>
+__host__ __device__ constexpr int fast_buffers() {
+  constexpr int per = R * 2 * (2 * DM + 1);  // VGPRs of one buffer
+  return 12 * per <= 240 ? 12 : (6 * per <= 240 ? 6 : (3 * per <= 240 ? 3 : (2 * per <= 200 ? 2 : 0)));
+}
+
+template <int DM, int R, bool ALPHA>
+__device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, lds_int* prog, double* lp_out) {
   constexpr int S = ring_size<DM>();
   constexpr int RWB = rec_bytes(DM);
-  // record buffers, prefetched NB-1 steps ahead (a few microseconds: the records stay
-  // reachable at full HBM latency even when streaming kernels evict them from L2)
-  constexpr int NB = DM <= 4 ? 2 * S : 6;  // register budget: 2*DM+1 float64 per buffer
-  constexpr int UL = NB > S ? NB : S;     // steps unrolled per iteration
-  static_assert(UL % S == 0 && UL % NB == 0, "unroll must hold whole rings and buffer rounds");
+  // record buffers, prefetched NB-1 steps ahead (a few microseconds for R = 1: the
+  // records stay reachable at full HBM latency even when L2 lost them)
+  constexpr int NB = fast_buffers<DM, R>();
+  constexpr int UL = NB > S ? NB : S;  // steps unrolled per iteration
+  static_assert(NB >= 2 && UL % S == 0 && UL % NB == 0, "unroll must hold whole rings and buffer rounds");
   const int nsteps = T + U;
   const int WP = p.WP;
   const int64_t nrec = (int64_t)p.KD * WP;
@@ -461,24 +470,37 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int u, lds_int*
       (void*)((ALPHA ? p.win : p.wout) + b * nrec * RWB), (short)0, (int)(nrec * RWB), 0x00020000);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((ALPHA ? p.ar : p.br) + b * nrec * 16), (short)0, (int)(nrec * 16), 0x00020000);
-  const unsigned Tl = u <= U ? (unsigned)T : 0u;  // node (k - u, u) is in the lattice iff k - u < Tl
-  double h[S], nb[S];
+  const int u0 = lane * R;  // labels u0 .. u0 + R - 1 of this lane
+  unsigned Tl[R];          // node (k - u, u) is in the lattice iff k - u < Tl
 #pragma unroll
-  for (int s = 0; s < S; ++s) h[s] = nb[s] = 0.0;
+  for (int r = 0; r < R; ++r) Tl[r] = u0 + r <= U ? (unsigned)T : 0u;
+  double h[R][S], nb[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    nb[s] = 0.0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) h[r][s] = 0.0;
+  }
   int sc = 0;
   bool started = false;  // the lane holds a non-zero value, so its scale is fixed
-  if (!ALPHA && u == U) {  // beta(T, U): the terminal
-    h[S - 1] = 1.0;
+  if (!ALPHA && u0 <= U && U < u0 + R) {  // beta(T, U): the terminal
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (u0 + r == U) h[r][S - 1] = 1.0;
     started = true;
   }
-  WMant<DM> wb[NB];
-  auto load_w = [&](int ks, WMant<DM>& w) {
+  WMant<DM> wb[NB][R];
+  auto load_w = [&](int ks, WMant<DM> (&w)[R]) {
     const int k = ALPHA ? ks : nsteps - 1 - ks;
-    int off = (k * WP - diag_ulo(k, T) + u) * RWB;
-    asm volatile("" : "+v"(off));
+    const int base = k * WP - diag_ulo(k, T) + u0;
 #pragma unroll
-    for (int j = 0; j < WMant<DM>::NQ; ++j) w.q[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16 * j, 0, 0);
-    w.tail = __builtin_amdgcn_raw_buffer_load_b64(wr, off + 16 * WMant<DM>::NQ, 0, 0);
+    for (int r = 0; r < R; ++r) {
+      int off = (base + r) * RWB;
+      asm volatile("" : "+v"(off));
+#pragma unroll
+      for (int j = 0; j < WMant<DM>::NQ; ++j) w[r].q[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16 * j, 0, 0);
+      w[r].tail = __builtin_amdgcn_raw_buffer_load_b64(wr, off + 16 * WMant<DM>::NQ, 0, 0);
+    }
   };
   // past the last step the loads fall outside this utterance's records (zeros) or hit
   // records that are never consumed; loading unconditionally keeps the wait counts of
@@ -490,60 +512,74 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int u, lds_int*
 #pragma unroll
     for (int q = 0; q < UL; ++q) {
       const int ph = q % S;  // ring slot
-      if (ph == 0) {  // keep each lane's newest value near 1 (a zero lane shifts by 0)
+      if (ph == 0) {  // keep the lane's largest newest value near 1 (a zero lane shifts by 0)
+        double big = fabs(h[0][S - 1]);
+#pragma unroll
+        for (int r = 1; r < R; ++r) big = fmax(big, fabs(h[r][S - 1]));
         int ex;
-        (void)frexp(h[S - 1], &ex);
+        (void)frexp(big, &ex);
         sc += ex;
 #pragma unroll
         for (int s2 = 0; s2 < S; ++s2) {
-          h[s2] = ldexp(h[s2], -ex);
           nb[s2] = ldexp(nb[s2], -ex);
+#pragma unroll
+          for (int r = 0; r < R; ++r) h[r][s2] = ldexp(h[r][s2], -ex);
         }
       }
       const int ks = k0 + q;
       load_w(ks + NB - 1, wb[(q + NB - 1) % NB]);
       const int k = ALPHA ? ks : nsteps - 1 - ks;
-      const bool act = (unsigned)(k - u) < Tl;
-      const WMant<DM>& w = wb[q % NB];
-      // own-lane moves (durations 1..DM) and the neighbour's moves (durations 0..DM), as
-      // two interleaved chains each
-      double c0 = 0.0, c1 = 0.0, c2 = 0.0, c3 = 0.0;
+      const int base = k * WP - diag_ulo(k, T) + u0;
+      double a[R];
 #pragma unroll
-      for (int d = 1; d <= DM; ++d) {
-        const double x = h[(ph - d + 4 * S) % S] * w.get(d - 1);
-        if (d & 1) c0 += x; else c1 += x;
+      for (int r = 0; r < R; ++r) {
+        const WMant<DM>& w = wb[q % NB][r];
+        // own moves (durations 1..DM), and the neighbour label's moves (durations 0..DM):
+        // label u-1 (alpha) or u+1 (beta), in this lane or from the next lane over
+        double c0 = 0.0, c1 = 0.0, c2 = 0.0, c3 = 0.0;
+#pragma unroll
+        for (int d = 1; d <= DM; ++d) {
+          const double x = h[r][(ph - d + 4 * S) % S] * w.get(d - 1);
+          if (d & 1) c0 += x; else c1 += x;
+        }
+#pragma unroll
+        for (int d = 0; d <= DM; ++d) {
+          const int sl = (ph - 1 - d + 4 * S) % S;
+          const double src = ALPHA ? (r > 0 ? h[r > 0 ? r - 1 : 0][sl] : nb[sl])
+                                   : (r < R - 1 ? h[r < R - 1 ? r + 1 : 0][sl] : nb[sl]);
+          const double x = src * w.get(DM + d);
+          if (d & 1) c3 += x; else c2 += x;
+        }
+        a[r] = (c0 + c1) + (c2 + c3);
+        if (ALPHA && ks == 0 && u0 + r == 0) {
+          a[r] = 1.0;
+          sc = 0;
+          started = true;
+        }
+        if (!((unsigned)(k - u0 - r) < Tl[r])) a[r] = 0.0;
       }
 #pragma unroll
-      for (int d = 0; d <= DM; ++d) {
-        const double x = nb[(ph - 1 - d + 4 * S) % S] * w.get(DM + d);
-        if (d & 1) c3 += x; else c2 += x;
-      }
-      double a = (c0 + c1) + (c2 + c3);
-      if (ALPHA && ks == 0 && u == 0) {
-        a = 1.0;
-        sc = 0;
-        started = true;
-      }
-      if (!act) a = 0.0;
-      h[ph] = a;
-      {
+      for (int r = 0; r < R; ++r) {
+        h[r][ph] = a[r];
         int ea;
-        const double ma = frexp(a, &ea);  // (0, 0) for a zero
-        const int eo = a != 0.0 ? ea + sc : kEZ;
-        const int o = act ? (k * WP - diag_ulo(k, T) + u) * 16 : -16;
+        const double ma = frexp(a[r], &ea);  // (0, 0) for a zero
+        const int eo = a[r] != 0.0 ? ea + sc : kEZ;
+        const int o = (unsigned)(k - u0 - r) < Tl[r] ? (base + r) * 16 : -16;
         const uint64_t mb = __builtin_bit_cast(uint64_t, ma);
         __builtin_amdgcn_raw_buffer_store_b128(u32x4v{(uint32_t)mb, (uint32_t)(mb >> 32), (uint32_t)eo, 0u}, xr, o, 0,
                                                0);
+        started = started || a[r] != 0.0;
       }
-      // neighbour exchange: alpha takes lane u-1's value, beta lane u+1's
-      const long long bits = __double_as_longlong(a);
+      // lane exchange: alpha passes its last label's value to the next lane, beta its
+      // first label's value to the previous lane
+      const double out = ALPHA ? a[R - 1] : a[0];
+      const long long bits = __double_as_longlong(out);
       int lo = (int)(bits & 0xffffffffll), hi = (int)(bits >> 32), e = sc;
       constexpr int ctl = ALPHA ? 0x138 : 0x130;  // wave_shr:1 / wave_shl:1
       lo = __builtin_amdgcn_update_dpp(0, lo, ctl, 0xf, 0xf, false);
       hi = __builtin_amdgcn_update_dpp(0, hi, ctl, 0xf, 0xf, false);
       e = __builtin_amdgcn_update_dpp(0, e, ctl, 0xf, 0xf, false);
       const double m = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
-      started = started || a != 0.0;
       if (!started) sc = e;  // an empty lane takes the scale of its first input
       started = started || m != 0.0;
       nb[ph] = ldexp(m, e - sc);
@@ -551,13 +587,13 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int u, lds_int*
     }
   }
   if (ALPHA) {
-    if (u == U) *lp_out = alpha_terminal<DM>(p, b, T, U);
-  } else if (u == 0) {  // beta(0,0) = P: the value of the last step, still in the ring
+    if (u0 <= U && U < u0 + R) *lp_out = alpha_terminal<DM>(p, b, T, U);
+  } else if (lane == 0) {  // beta(0,0) = P: the value of the last step, still in the ring
     const int last = (nsteps - 1) % S;
-    double a = h[0];
+    double a = h[0][0];
 #pragma unroll
-    for (int s = 1; s < S; ++s)
-      if (s == last) a = h[s];
+    for (int s2 = 1; s2 < S; ++s2)
+      if (s2 == last) a = h[0][s2];
     int ea;
     const double ma = frexp(a, &ea);
     const Ext P = a != 0.0 ? Ext{ma, ea + sc} : ext_zero();
@@ -599,10 +635,11 @@ __device__ void l2_warm(const Params& p, int b, int nsteps, bool alpha, int lane
 
 // Lattice kernel.  SW (U1max <= 256): one 256-thread work-group per utterance, wave 0
 // the alpha chain, wave 1 the beta chain, waves 2 and 3 their L2 warm-up.  Otherwise one
-// work-group of up to 1024 threads per (utterance, direction).  With R = 1 the chains
-// first run the plain-float64 sweep; if log P from the alpha side and from the beta side
-// differ by more than 1e-9 (rounding alone stays below 1e-12: both sides sum the same
-// probability mass in float64), both directions are redone with the extended-range sweep.
+// work-group of up to 1024 threads per (utterance, direction).  Where its registers fit
+// (fast_buffers), the chains first run the plain-float64 sweep; if log P from the alpha
+// side and from the beta side differ by more than 1e-9 (rounding alone stays below 1e-12:
+// both sides sum the same probability mass in float64), both directions are redone with
+// the extended-range sweep.
 template <int DM, int R, bool SW>
 __global__ __launch_bounds__(SW ? 256 : 1024) void k_lattice(const Params p) {
   __shared__ double xm[SW ? 1 : 2 * 1024];
@@ -655,10 +692,10 @@ __global__ __launch_bounds__(SW ? 256 : 1024) void k_lattice(const Params p) {
     const int wv = tid >> 6, lane = tid & (kWave - 1);
     const bool alpha = (wv & 1) == 0;
     lds_int* prog = (lds_int*)&s_prog[wv & 1];
-    if constexpr (R == 1) {
-        if (!p.xflag[b]) {
-        if (wv == 0) sweep_fast<DM, true>(p, b, T, U, lane, prog, &s_lp[0]);
-        else if (wv == 1) sweep_fast<DM, false>(p, b, T, U, lane, prog, &s_lp[1]);
+    if constexpr (fast_buffers<DM, R>() > 0) {
+      if (!p.xflag[b]) {
+        if (wv == 0) sweep_fast<DM, R, true>(p, b, T, U, lane, prog, &s_lp[0]);
+        else if (wv == 1) sweep_fast<DM, R, false>(p, b, T, U, lane, prog, &s_lp[1]);
         else l2_warm(p, b, T + U, alpha, lane, prog);
         __syncthreads();
         const double la = s_lp[0], lb = s_lp[1];
