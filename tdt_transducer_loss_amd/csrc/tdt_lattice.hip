@@ -580,7 +580,12 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, lds_i
       hi = __builtin_amdgcn_update_dpp(0, hi, ctl, 0xf, 0xf, false);
       e = __builtin_amdgcn_update_dpp(0, e, ctl, 0xf, 0xf, false);
       const double m = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
-      if (!started) sc = e;  // an empty lane takes the scale of its first input
+      {  // an empty lane takes a scale that puts its first input near 1 (the sender's
+         // own scale may be stale at the wavefront, far from the value it sends)
+        int em;
+        (void)frexp(m, &em);  // 0 for a zero
+        if (!started) sc = e + em;
+      }
       started = started || m != 0.0;
       nb[ph] = ldexp(m, e - sc);
       __hip_atomic_store(prog, ks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -600,6 +605,169 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, lds_i
     beta_final(p, b, P);
     *lp_out = ext_log(P);
   }
+}
+
+// Plain-float64 sweep over several waves (U1max > 256): the lanes of all waves of the
+// work-group run across the labels, R per lane, with the lane scales, renormalisation and
+// per-step arithmetic of the single-wave sweep; the neighbour's value goes through LDS
+// with one barrier per step, and the records of the next step are loaded while that
+// exchange runs.  Alpha and beta run in different work-groups here, so the log P
+// comparison is not available: each lane checks instead that every value it creates,
+// converts or shifts stays within [2^-700, 2^700] (then, with every weight in
+// [2^-300, 2^300], no product or sum can underflow or overflow), and the work-group redoes
+// the direction with the extended-range sweep when any lane saw a value outside it.
+template <int DM, int R>
+__host__ __device__ constexpr bool fast_mw_ok() {
+  return R * 2 * (2 * DM + 1) + 2 * (R + 1) * ring_size<DM>() <= 150;  // VGPRs at 768 threads
+}
+
+__device__ __forceinline__ bool out_of_range(double x) {  // non-zero and outside [2^-700, 2^700]
+  const double a = fabs(x);
+  return a != 0.0 && (a < 0x1p-700 || a > 0x1p700);
+}
+
+template <int DM, int R, bool ALPHA>
+__device__ bool sweep_fast_mw(const Params& p, int b, int T, int U, int tid, double* xm, int* xe) {
+  constexpr int S = ring_size<DM>();
+  constexpr int RWB = rec_bytes(DM);
+  const int nt = blockDim.x;
+  const int nsteps = T + U;
+  const int WP = p.WP;
+  const int64_t nrec = (int64_t)p.KD * WP;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((ALPHA ? p.win : p.wout) + b * nrec * RWB), (short)0, (int)(nrec * RWB), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((ALPHA ? p.ar : p.br) + b * nrec * 16), (short)0, (int)(nrec * 16), 0x00020000);
+  const int u0 = tid * R;
+  unsigned Tl[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) Tl[r] = u0 + r <= U ? (unsigned)T : 0u;
+  double h[R][S], nb[S];
+#pragma unroll
+  for (int s2 = 0; s2 < S; ++s2) {
+    nb[s2] = 0.0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) h[r][s2] = 0.0;
+  }
+  int sc = 0;
+  bool started = false, trouble = false;
+  if (!ALPHA && u0 <= U && U < u0 + R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (u0 + r == U) h[r][S - 1] = 1.0;
+    started = true;
+  }
+  WMant<DM> w[R];
+  auto load_w = [&](int ks) {
+    const int k = ALPHA ? ks : nsteps - 1 - ks;
+    const int base = k * WP - diag_ulo(k, T) + u0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int off = (base + r) * RWB;
+#pragma unroll
+      for (int j = 0; j < WMant<DM>::NQ; ++j) w[r].q[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16 * j, 0, 0);
+      w[r].tail = __builtin_amdgcn_raw_buffer_load_b64(wr, off + 16 * WMant<DM>::NQ, 0, 0);
+    }
+  };
+  load_w(0);
+  for (int k0 = 0; k0 < nsteps; k0 += S) {
+#pragma unroll
+    for (int ph = 0; ph < S; ++ph) {
+      if (ph == 0) {  // keep the lane's largest newest value near 1
+        double big = fabs(h[0][S - 1]);
+#pragma unroll
+        for (int r = 1; r < R; ++r) big = fmax(big, fabs(h[r][S - 1]));
+        int ex;
+        (void)frexp(big, &ex);
+        sc += ex;
+#pragma unroll
+        for (int s2 = 0; s2 < S; ++s2) {
+          nb[s2] = ldexp(nb[s2], -ex);
+          trouble |= out_of_range(nb[s2]);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            h[r][s2] = ldexp(h[r][s2], -ex);
+            trouble |= out_of_range(h[r][s2]);
+          }
+        }
+      }
+      const int ks = k0 + ph;
+      const int k = ALPHA ? ks : nsteps - 1 - ks;
+      const int base = k * WP - diag_ulo(k, T) + u0;
+      double a[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        double c0 = 0.0, c1 = 0.0, c2 = 0.0, c3 = 0.0;
+#pragma unroll
+        for (int d = 1; d <= DM; ++d) {
+          const double x = h[r][(ph - d + 4 * S) % S] * w[r].get(d - 1);
+          if (d & 1) c0 += x; else c1 += x;
+        }
+#pragma unroll
+        for (int d = 0; d <= DM; ++d) {
+          const int sl = (ph - 1 - d + 4 * S) % S;
+          const double src = ALPHA ? (r > 0 ? h[r > 0 ? r - 1 : 0][sl] : nb[sl])
+                                   : (r < R - 1 ? h[r < R - 1 ? r + 1 : 0][sl] : nb[sl]);
+          const double x = src * w[r].get(DM + d);
+          if (d & 1) c3 += x; else c2 += x;
+        }
+        a[r] = (c0 + c1) + (c2 + c3);
+        if (ALPHA && ks == 0 && u0 + r == 0) {
+          a[r] = 1.0;
+          sc = 0;
+          started = true;
+        }
+        if (!((unsigned)(k - u0 - r) < Tl[r])) a[r] = 0.0;
+        trouble |= out_of_range(a[r]);
+      }
+      if (ks + 1 < nsteps) load_w(ks + 1);  // the records of the next step, during the exchange
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        h[r][ph] = a[r];
+        int ea;
+        const double ma = frexp(a[r], &ea);
+        const int eo = a[r] != 0.0 ? ea + sc : kEZ;
+        const int o = (unsigned)(k - u0 - r) < Tl[r] ? (base + r) * 16 : -16;
+        const uint64_t mb = __builtin_bit_cast(uint64_t, ma);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4v{(uint32_t)mb, (uint32_t)(mb >> 32), (uint32_t)eo, 0u}, xr, o, 0,
+                                               0);
+        started = started || a[r] != 0.0;
+      }
+      // neighbour exchange through LDS
+      const int par = (ks & 1) * 1024;
+      xm[par + tid] = ALPHA ? a[R - 1] : a[0];
+      xe[par + tid] = sc;
+      __syncthreads();
+      const int src = ALPHA ? tid - 1 : tid + 1;
+      const bool has = src >= 0 && src < nt;
+      const double m = has ? xm[par + src] : 0.0;
+      const int e = has ? xe[par + src] : 0;
+      {  // an empty lane takes a scale that puts its first input near 1 (the sender's
+         // own scale may be stale at the wavefront, far from the value it sends)
+        int em;
+        (void)frexp(m, &em);  // 0 for a zero
+        if (!started) sc = e + em;
+      }
+      started = started || m != 0.0;
+      nb[ph] = ldexp(m, e - sc);
+      trouble |= m != 0.0 && out_of_range(nb[ph]);
+    }
+  }
+  trouble = __syncthreads_or(trouble);
+  if (trouble) return true;
+  if (ALPHA) {
+    if (u0 <= U && U < u0 + R) (void)alpha_terminal<DM>(p, b, T, U);
+  } else if (tid == 0) {
+    const int last = (nsteps - 1) % S;
+    double a = h[0][0];
+#pragma unroll
+    for (int s2 = 1; s2 < S; ++s2)
+      if (s2 == last) a = h[0][s2];
+    int ea;
+    const double ma = frexp(a, &ea);
+    beta_final(p, b, a != 0.0 ? Ext{ma, ea + sc} : ext_zero());
+  }
+  return false;
 }
 
 // L2 warm-up for a single-wave sweep: a helper wave touches every 128-byte line of the
@@ -634,14 +802,16 @@ __device__ void l2_warm(const Params& p, int b, int nsteps, bool alpha, int lane
 }
 
 // Lattice kernel.  SW (U1max <= 256): one 256-thread work-group per utterance, wave 0
-// the alpha chain, wave 1 the beta chain, waves 2 and 3 their L2 warm-up.  Otherwise one
-// work-group of up to 1024 threads per (utterance, direction).  Where its registers fit
-// (fast_buffers), the chains first run the plain-float64 sweep; if log P from the alpha
-// side and from the beta side differ by more than 1e-9 (rounding alone stays below 1e-12:
-// both sides sum the same probability mass in float64), both directions are redone with
-// the extended-range sweep.
+// the alpha chain, wave 1 the beta chain, waves 2 and 3 their L2 warm-up.  Where its
+// registers fit (fast_buffers), the chains first run the plain-float64 sweep; if log P
+// from the alpha side and from the beta side differ by more than 1e-9 (rounding alone
+// stays below 1e-12: both sides sum the same probability mass in float64), both
+// directions are redone with the extended-range sweep.  Otherwise one work-group of up to
+// 768 threads (1024 for R = 8) per (utterance, direction), with the range-checked
+// multi-wave plain sweep where its registers fit (fast_mw_ok) and the extended-range
+// sweep after it or instead of it.
 template <int DM, int R, bool SW>
-__global__ __launch_bounds__(SW ? 256 : 1024) void k_lattice(const Params p) {
+__global__ __launch_bounds__(SW ? 256 : (R <= 4 ? 768 : 1024)) void k_lattice(const Params p) {
   __shared__ double xm[SW ? 1 : 2 * 1024];
   __shared__ int xe[SW ? 1 : 2 * 1024];
   __shared__ unsigned long long s_sumU;
@@ -708,6 +878,14 @@ __global__ __launch_bounds__(SW ? 256 : 1024) void k_lattice(const Params p) {
     else if (wv == 1) sweep<DM, R, true, false>(p, b, T, U, lane, xm, xe, prog);
     else l2_warm(p, b, T + U, alpha, lane, prog);
   } else {
+    if constexpr (fast_mw_ok<DM, R>()) {
+      if (!p.xflag[b]) {
+        const bool trouble = dir == 0 ? sweep_fast_mw<DM, R, true>(p, b, T, U, tid, xm, xe)
+                                      : sweep_fast_mw<DM, R, false>(p, b, T, U, tid, xm, xe);
+        if (!trouble) return;
+        __syncthreads();  // the exchange arrays are reused below
+      }
+    }
     if (dir == 0)
       sweep<DM, R, false, true>(p, b, T, U, tid, xm, xe, (lds_int*)&s_prog[0]);
     else
@@ -833,7 +1011,8 @@ static hipError_t launch_lattice_dm(const Params& p, hipStream_t st) {
   } else if (u1 <= 256) {
     hipLaunchKernelGGL((k_lattice<DM, 4, true>), grid_sw, dim3(256), 0, st, p);
   } else {
-    int R = u1 <= 1024 ? 1 : u1 <= 2048 ? 2 : u1 <= 4096 ? 4 : 8;
+    // at most 768 threads for R <= 4 (about 170 VGPRs per lane), 1024 for R = 8
+    int R = u1 <= 768 ? 1 : u1 <= 1536 ? 2 : u1 <= 3072 ? 4 : 8;
     const int nt = ((u1 + R - 1) / R + 63) / 64 * 64;
     switch (R) {
       case 1: hipLaunchKernelGGL((k_lattice<DM, 1, false>), grid, dim3(nt), 0, st, p); break;
