@@ -17,7 +17,8 @@
 
 namespace tdt {
 
-constexpr int kWavesPerBlock = 4;  // 256-thread work-groups
+constexpr int kWavesPerBlock = 4;   // 256-thread work-groups
+constexpr int kRowStatBlocks = 4096;  // grid of the persistent row-statistics pass (16K waves)
 
 template <typename TI>
 __device__ __forceinline__ uint4 neg_inf_chunk() {
@@ -99,85 +100,90 @@ __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (blockIdx.x == 0)  // the node-weight kernel that follows sets these flags
     for (int i = threadIdx.x; i < p.B; i += blockDim.x) p.xflag[i] = 0;
-  const int64_t g = (int64_t)xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
+  // persistent: a fixed grid of waves walks the (position, segment) space, skipping
+  // positions outside their utterance in a few instructions (ragged batches leave most
+  // of the padded space empty)
   const int nseg = p.nseg;
-  const int64_t node = g / nseg;
-  const int seg = (int)(g - node * nseg);
   const int64_t per = (int64_t)p.KD * p.WP;
-  const int b = (int)(node / per);
-  if (b >= p.B) return;
-  const int64_t rem = node - (int64_t)b * per;
-  const int k = (int)(rem / p.WP);
-  const int i = (int)(rem - (int64_t)k * p.WP);
-  const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
-  if (!utt_dims_ok(p, T64, U64)) return;
-  const int T = (int)T64, U = (int)U64;
-  if (k >= T + U) return;
-  const int u = diag_ulo(k, T) + i;
-  if (u > min(k, U)) return;
-  const int t = k - u;
+  const int64_t total = (int64_t)p.B * per * nseg;
+  const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+  for (int64_t g = (int64_t)xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv; g < total; g += stride) {
+    const int64_t node = g / nseg;
+    const int seg = (int)(g - node * nseg);
+    const int b = (int)(node / per);
+    const int64_t rem = node - (int64_t)b * per;
+    const int k = (int)(rem / p.WP);
+    const int i = (int)(rem - (int64_t)k * p.WP);
+    const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
+    if (!utt_dims_ok(p, T64, U64)) continue;
+    const int T = (int)T64, U = (int)U64;
+    if (k >= T + U) continue;
+    const int u = diag_ulo(k, T) + i;
+    if (u > min(k, U)) continue;
+    const int t = k - u;
 
-  int y = -1;
-  if (u < U) {
-    const int64_t yy = p.labels[(int64_t)b * p.lab_stride + u];
-    if (yy >= 0 && yy < p.V) y = (int)yy;
-  }
-  const int V = p.V;
-  const ET* row = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
-  const RowCover rc = row_cover<TI>(row, V);
-  const int c0 = seg * 64 * NCH;
+    int y = -1;
+    if (u < U) {
+      const int64_t yy = p.labels[(int64_t)b * p.lab_stride + u];
+      if (yy >= 0 && yy < p.V) y = (int)yy;
+    }
+    const int V = p.V;
+    const ET* row = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
+    const RowCover rc = row_cover<TI>(row, V);
+    const int c0 = seg * 64 * NCH;
 
-  uint4 v[NCH];
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = c0 + lane + 64 * j;
-    v[j] = c < rc.nch ? rc.base[c] : neg_inf_chunk<TI>();
-  }
-  float* rs = (float*)(p.rstat + rem + (int64_t)b * per);
-  const int cb = (rc.head + p.blank) / EPC, sb = (rc.head + p.blank) % EPC;
-  const int cy = y >= 0 ? (rc.head + y) / EPC : -1, sy = y >= 0 ? (rc.head + y) % EPC : 0;
-  MaxAcc<TI> mx;
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = c0 + lane + 64 * j;
-    if (c == 0 || c == rc.nch - 1) {
-#pragma unroll
+    uint4 v[NCH];
+  #pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = c0 + lane + 64 * j;
+      v[j] = c < rc.nch ? rc.base[c] : neg_inf_chunk<TI>();
+    }
+    float* rs = (float*)(p.rstat + rem + (int64_t)b * per);
+    const int cb = (rc.head + p.blank) / EPC, sb = (rc.head + p.blank) % EPC;
+    const int cy = y >= 0 ? (rc.head + y) / EPC : -1, sy = y >= 0 ? (rc.head + y) % EPC : 0;
+    MaxAcc<TI> mx;
+  #pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = c0 + lane + 64 * j;
+      if (c == 0 || c == rc.nch - 1) {
+  #pragma unroll
+        for (int s = 0; s < EPC; ++s) {
+          const int e = c * EPC + s - rc.head;
+          if (e < 0 || e >= V) chunk_set<TI>(v[j], s, TI::kNegInf);
+        }
+      }
+      if (c == cb) rs[2] = TI::get(v[j], sb);
+      if (c == cy) rs[3] = TI::get(v[j], sy);
+      mx.add(v[j].x);
+      mx.add(v[j].y);
+      mx.add(v[j].z);
+      mx.add(v[j].w);
+    }
+    // lane-local exp sum relative to the lane's own maximum
+    const float ml = mx.value();
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  #pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+  #pragma unroll
       for (int s = 0; s < EPC; ++s) {
-        const int e = c * EPC + s - rc.head;
-        if (e < 0 || e >= V) chunk_set<TI>(v[j], s, TI::kNegInf);
+        const float e2 = __builtin_amdgcn_exp2f((TI::get(v[j], s) - ml) * kLog2e);
+        if ((s & 3) == 0) a0 += e2;
+        else if ((s & 3) == 1) a1 += e2;
+        else if ((s & 3) == 2) a2 += e2;
+        else a3 += e2;
       }
     }
-    if (c == cb) rs[2] = TI::get(v[j], sb);
-    if (c == cy) rs[3] = TI::get(v[j], sy);
-    mx.add(v[j].x);
-    mx.add(v[j].y);
-    mx.add(v[j].z);
-    mx.add(v[j].w);
-  }
-  // lane-local exp sum relative to the lane's own maximum
-  const float ml = mx.value();
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-#pragma unroll
-    for (int s = 0; s < EPC; ++s) {
-      const float e2 = __builtin_amdgcn_exp2f((TI::get(v[j], s) - ml) * kLog2e);
-      if ((s & 3) == 0) a0 += e2;
-      else if ((s & 3) == 1) a1 += e2;
-      else if ((s & 3) == 2) a2 += e2;
-      else a3 += e2;
+    float acc = (a0 + a1) + (a2 + a3);
+    if (!(ml > -__builtin_inff())) acc = 0.f;  // a lane holding only masked slots
+    const float mw = wave_max_f32(ml);
+    const float scaled = acc > 0.f ? acc * __builtin_amdgcn_exp2f((ml - mw) * kLog2e) : 0.f;
+    const double S = wave_sum_f64((double)scaled);
+    if (lane == 0) {
+      float* part = p.part + (rem + (int64_t)b * per) * 2 * nseg + 2 * seg;
+      part[0] = mw;
+      part[1] = (float)S;
+      if (seg == 0 && y < 0) rs[3] = -__builtin_inff();
     }
-  }
-  float acc = (a0 + a1) + (a2 + a3);
-  if (!(ml > -__builtin_inff())) acc = 0.f;  // a lane holding only masked slots
-  const float mw = wave_max_f32(ml);
-  const float scaled = acc > 0.f ? acc * __builtin_amdgcn_exp2f((ml - mw) * kLog2e) : 0.f;
-  const double S = wave_sum_f64((double)scaled);
-  if (lane == 0) {
-    float* part = p.part + (rem + (int64_t)b * per) * 2 * nseg + 2 * seg;
-    part[0] = mw;
-    part[1] = (float)S;
-    if (seg == 0 && y < 0) rs[3] = -__builtin_inff();
   }
 }
 
@@ -309,7 +315,9 @@ hipError_t launch_rows_t(const Params& p, bool aligned, hipStream_t st, int whic
   const int nch = p.nch;
   const int64_t nodes = which == 0 ? (int64_t)p.B * p.KD * p.WP : (int64_t)p.B * p.Tmax * p.U1max;
   const int64_t waves = nodes * p.nseg;
-  const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+  int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (which == 0 && blocks > kRowStatBlocks) blocks = kRowStatBlocks;  // persistent row statistics
+  const dim3 grid((unsigned)blocks);
   if (which == 0) {
 #define TDT_RS(N) \
   case N: hipLaunchKernelGGL((k_row_partial<TI, N>), grid, dim3(256), 0, st, p); break;
