@@ -720,7 +720,9 @@ __device__ bool sweep_fast_mw(const Params& p, int b, int T, int U, int tid, dou
         if (!((unsigned)(k - u0 - r) < Tl[r])) a[r] = 0.0;
         trouble |= out_of_range(a[r]);
       }
-      if (ks + 1 < nsteps) load_w(ks + 1);  // the records of the next step, during the exchange
+      // the records of the next step, during the exchange (unconditional: past the last
+      // step the offsets fall outside this utterance's records and read zeros)
+      load_w(ks + 1);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         h[r][ph] = a[r];
@@ -737,7 +739,9 @@ __device__ bool sweep_fast_mw(const Params& p, int b, int T, int U, int tid, dou
       const int par = (ks & 1) * 1024;
       xm[par + tid] = ALPHA ? a[R - 1] : a[0];
       xe[par + tid] = sc;
-      __syncthreads();
+      // barrier on the LDS exchange only: __syncthreads() would also wait for every
+      // outstanding global load, including the prefetches of later steps
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       const int src = ALPHA ? tid - 1 : tid + 1;
       const bool has = src >= 0 && src < nt;
       const double m = has ? xm[par + src] : 0.0;
