@@ -88,6 +88,9 @@ EDGE = {
     # standard deviation 400: weights far below 2^-300 (extended-range lattice path)
     "huge_logits_extended_range": lambda: make_case(2, [40, 31], [12, 9], 17, [0, 1, 2], "f32", seed=54,
                                                     scale=400.0, reduction="none"),
+    # more than 256 labels with weights far below 2^-300: the multi-wave extended-range sweep
+    "huge_logits_multiwave": lambda: make_case(1, [24], [300], 9, [0, 1, 2], "f32", seed=55, scale=400.0,
+                                               reduction="sum"),
     "ragged_padded_f16": lambda: make_case(5, None, None, 129, [0, 1, 2, 3, 4], "f16", seed=52, Tmax=70, U1max=30,
                                            T_range=(1, 70), U_range=(0, 29), reduction="mean", extra_cols=3),
 }
