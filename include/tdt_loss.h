@@ -114,10 +114,15 @@ int tdt_loss_workspace_size(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_
  *                    NULL together with grad_dur_logits for a forward-only call.  Every
  *                    element of the [B, T_max, U1_max, V] view is written (zeros in
  *                    padding), so it may start uninitialised.  May share a buffer with
- *                    grad_dur_logits (e.g. two slices of one joint gradient) but must
- *                    not overlap the logits.
+ *                    grad_dur_logits (e.g. two slices of one joint gradient).  In place:
+ *                    grad_logits may be the logits view itself (same pointer and
+ *                    strides); the logits are then overwritten by their gradient, which
+ *                    saves a logits-sized buffer (the memory saving the page "tdt-loss:
+ *                    add TDT loss kernel" reports for fine-tuning, comment "What's in
+ *                    it").  Any other overlap of a gradient view with a logits view
+ *                    returns TDT_ERR_INVALID_ARGUMENT.
  *   grad_dur_logits  gradient w.r.t. dur_logits [B, T_max, U1_max, D], strides
- *                    grad_dur_strides[0..2].
+ *                    grad_dur_strides[0..2]; may likewise be the dur_logits view itself.
  *   utt_status       int32 [B] status bits, or NULL.
  *   workspace        device scratch of at least tdt_loss_workspace_size() bytes,
  *                    256-byte aligned; its contents need no initialisation and are
@@ -158,6 +163,34 @@ int tdt_loss_fwd_bwd_timed(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_m
                            float* loss_out, void* grad_logits, const int64_t* grad_strides, void* grad_dur_logits,
                            const int64_t* grad_dur_strides, int32_t* utt_status, void* workspace,
                            size_t workspace_bytes, void* stream, void* const* events, int32_t num_events);
+
+/*
+ * Gradient of a loss computed earlier by a forward-only tdt_loss_fwd_bwd call (both
+ * gradient pointers NULL), for autograd-style use where the upstream gradient is known
+ * only later.  Stream-ordered on `stream`; runs the coefficient kernel and the gradient
+ * pass (the last two kernels of the launch sequence above) on the state the forward call
+ * left in `workspace`, so between the two calls the workspace must be untouched, and
+ * logits, dur_logits, labels, the two length arrays and every size, durations, blank,
+ * sigma and reduction must be the same (contents included).  Nothing is checked on the
+ * device against the forward call: other values give meaningless gradients.
+ *
+ *   grad_loss        device float, the upstream gradient d(objective)/d(loss_out): [B]
+ *                    for TDT_REDUCTION_NONE (utterance b's gradient is scaled by
+ *                    grad_loss[b]), else [1]; NULL means 1.  It multiplies the
+ *                    per-utterance weights w_b in float64, so grad_loss = 1 gives the
+ *                    bits of tdt_loss_fwd_bwd's gradients.
+ *   grad_logits, grad_dur_logits  required; the same rules as in tdt_loss_fwd_bwd
+ *                    (in place allowed).
+ * The loss and the status array are not written.  Returns TDT_OK or a negative
+ * TDT_ERR_* code (nothing is launched then).
+ */
+int tdt_loss_backward(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, const void* logits,
+                      const int64_t* logits_strides, const void* dur_logits, const int64_t* dur_strides,
+                      int32_t num_durations, const int64_t* labels, int64_t labels_stride,
+                      const int64_t* logit_lengths, const int64_t* label_lengths, const int32_t* durations,
+                      int32_t blank, double sigma, int32_t reduction, const float* grad_loss, void* grad_logits,
+                      const int64_t* grad_strides, void* grad_dur_logits, const int64_t* grad_dur_strides,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static string naming a return code. */
 const char* tdt_loss_status_string(int status);

@@ -41,6 +41,15 @@ SIGNATURES = {
         _i32p, _i32, _f64, _i32, _vp, _vp, _i64p, _vp, _i64p, _vp, _vp, ctypes.c_size_t, _vp,
         ctypes.POINTER(ctypes.c_void_p), _i32,
     ]),
+    "tdt_loss_backward": (ctypes.c_int, [
+        _i32, _i64, _i64, _i64, _i64,       # dtype, B, T_max, U1_max, V
+        _vp, _i64p, _vp, _i64p, _i32,       # logits, strides, dur_logits, strides, num_durations
+        _vp, _i64, _vp, _vp,                # labels, labels_stride, logit_lengths, label_lengths
+        _i32p, _i32, _f64, _i32,            # durations (host), blank, sigma, reduction
+        _vp,                                # grad_loss
+        _vp, _i64p, _vp, _i64p,             # grad_logits, strides, grad_dur_logits, strides
+        _vp, ctypes.c_size_t, _vp,          # workspace, workspace_bytes, stream
+    ]),
     "tdt_loss_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tdt_loss_abi_version": (ctypes.c_int, []),
 }
@@ -110,4 +119,18 @@ def fwd_bwd_raw(dtype, B, T_max, U1_max, V, logits, lstr, dur, dstr, D, labels, 
         loss,
         glog, i64_array(gstr) if gstr is not None else None, gdur, i64_array(gdstr) if gdstr is not None else None,
         status, ws, ctypes.c_size_t(int(ws_bytes)), stream, *extra,
+    )
+
+
+def backward_raw(dtype, B, T_max, U1_max, V, logits, lstr, dur, dstr, D, labels, lab_stride, tlen, ulen,
+                 durations, blank, sigma, reduction, grad_loss, glog, gstr, gdur, gdstr, ws, ws_bytes, stream) -> int:
+    """Direct call of tdt_loss_backward with raw integers / pointers (None for NULL)."""
+    return lib().tdt_loss_backward(
+        int(dtype), int(B), int(T_max), int(U1_max), int(V),
+        logits, i64_array(lstr), dur, i64_array(dstr), int(D),
+        labels, int(lab_stride), tlen, ulen,
+        i32_array(durations), int(blank), float(sigma), int(reduction),
+        grad_loss,
+        glog, i64_array(gstr) if gstr is not None else None, gdur, i64_array(gdstr) if gdstr is not None else None,
+        ws, ctypes.c_size_t(int(ws_bytes)), stream,
     )

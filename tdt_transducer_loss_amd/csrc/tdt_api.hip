@@ -1,7 +1,8 @@
 // Host side of the C ABI declared in include/tdt_loss.h: argument validation, workspace
 // layout and the launch sequence.  On the caller's stream the kernels run
 //   row partials -> node weights -> lattice (alpha || beta) -> coefficients and loss
-//   reduction -> gradient  (forward only: ... -> lattice -> loss reduction).
+//   reduction -> gradient  (forward only: ... -> lattice -> loss reduction; a later
+//   backward call on the same workspace: coefficients -> gradient).
 #include <math.h>
 #include <string.h>
 
@@ -120,18 +121,45 @@ extern "C" int tdt_loss_workspace_size(int32_t dtype, int64_t B, int64_t T_max, 
 
 namespace {
 
-int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, const void* logits,
-                 const int64_t* logits_strides, const void* dur_logits, const int64_t* dur_strides,
-                 int32_t num_durations, const int64_t* labels, int64_t labels_stride, const int64_t* logit_lengths,
-                 const int64_t* label_lengths, const int32_t* durations, int32_t blank, double sigma,
-                 int32_t reduction, float* loss_out, void* grad_logits, const int64_t* grad_strides,
-                 void* grad_dur_logits, const int64_t* grad_dur_strides, int32_t* utt_status, void* workspace,
-                 size_t workspace_bytes, void* stream, void* const* events, int32_t num_events) {
+// Byte range [lo, hi) touched by a [B, T, U1, C] view with element strides s[0..2] and a
+// unit last stride.
+struct Extent {
+  __int128 lo, hi;
+};
+
+Extent view_extent(const void* ptr, const int64_t* s, int64_t B, int64_t T, int64_t U1, int64_t C, size_t elt) {
+  const int64_t n[3] = {B, T, U1};
+  __int128 lo = 0, hi = C;
+  for (int d = 0; d < 3; ++d) {
+    const __int128 off = (__int128)(n[d] - 1) * s[d];
+    if (off < 0) lo += off;
+    else hi += off;
+  }
+  const __int128 base = (__int128)(uintptr_t)ptr;
+  return Extent{base + lo * (__int128)elt, base + hi * (__int128)elt};
+}
+
+bool overlap(const Extent& a, const Extent& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool same_view(const void* a, const int64_t* sa, const void* b, const int64_t* sb) {
+  return a == b && sa[0] == sb[0] && sa[1] == sb[1] && sa[2] == sb[2];
+}
+
+// Validates the arguments shared by every entry point and fills the kernel parameters.
+// `grads`: gradient views are given (required when need_grads).
+int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, const void* logits,
+            const int64_t* logits_strides, const void* dur_logits, const int64_t* dur_strides, int32_t num_durations,
+            const int64_t* labels, int64_t labels_stride, const int64_t* logit_lengths, const int64_t* label_lengths,
+            const int32_t* durations, int32_t blank, double sigma, int32_t reduction, float* loss_out,
+            bool need_loss, bool need_grads, void* grad_logits, const int64_t* grad_strides, void* grad_dur_logits,
+            const int64_t* grad_dur_strides, int32_t* utt_status, void* workspace, size_t workspace_bytes,
+            Params* pp, bool* grads_out, bool* aligned_out) {
   if (dtype < 0 || dtype > 2) return TDT_ERR_UNSUPPORTED_DTYPE;
   if (reduction < 0 || reduction > 4) return TDT_ERR_INVALID_ARGUMENT;
   if (!logits || !logits_strides || !dur_logits || !dur_strides || !labels || !logit_lengths || !label_lengths ||
-      !loss_out || !workspace)
+      !workspace)
     return TDT_ERR_INVALID_ARGUMENT;
+  if (need_loss && !loss_out) return TDT_ERR_INVALID_ARGUMENT;
   if (V < 1) return TDT_ERR_INVALID_ARGUMENT;
   if (blank < 0 || blank >= V) return TDT_ERR_INVALID_ARGUMENT;
   if (!isfinite(sigma)) return TDT_ERR_INVALID_ARGUMENT;
@@ -139,18 +167,33 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
   const bool grads = grad_logits != nullptr || grad_dur_logits != nullptr;
   if (grads && (!grad_logits || !grad_dur_logits || !grad_strides || !grad_dur_strides))
     return TDT_ERR_INVALID_ARGUMENT;
+  if (need_grads && !grads) return TDT_ERR_INVALID_ARGUMENT;
   const int maxd = check_durations(durations, num_durations);
   if (maxd < 0) return maxd;
   Layout L;
   int rc = make_layout(dtype, B, T_max, U1_max, V, num_durations, maxd, &L);
   if (rc != TDT_OK) return rc;
+  const size_t elt = dtype == 0 ? 4 : 2;
+  if (grads) {
+    // a gradient view is either exactly its logits view (in place) or disjoint from both
+    // logits views
+    const Extent et = view_extent(logits, logits_strides, B, T_max, U1_max, V, elt);
+    const Extent ed = view_extent(dur_logits, dur_strides, B, T_max, U1_max, num_durations, elt);
+    if (!same_view(grad_logits, grad_strides, logits, logits_strides)) {
+      const Extent eg = view_extent(grad_logits, grad_strides, B, T_max, U1_max, V, elt);
+      if (overlap(eg, et) || overlap(eg, ed)) return TDT_ERR_INVALID_ARGUMENT;
+    }
+    if (!same_view(grad_dur_logits, grad_dur_strides, dur_logits, dur_strides)) {
+      const Extent eg = view_extent(grad_dur_logits, grad_dur_strides, B, T_max, U1_max, num_durations, elt);
+      if (overlap(eg, et) || overlap(eg, ed)) return TDT_ERR_INVALID_ARGUMENT;
+    }
+  }
   if (workspace_bytes < L.total) return TDT_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned_to(workspace, 256)) return TDT_ERR_BAD_STRIDE;
-  const size_t elt = dtype == 0 ? 4 : 2;
   if (!aligned_to(logits, elt) || !aligned_to(dur_logits, elt)) return TDT_ERR_BAD_STRIDE;
   if (grads && (!aligned_to(grad_logits, elt) || !aligned_to(grad_dur_logits, elt))) return TDT_ERR_BAD_STRIDE;
 
-  Params p;
+  Params& p = *pp;
   memset(&p, 0, sizeof p);
   p.B = (int)B;
   p.Tmax = (int)T_max;
@@ -226,20 +269,40 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
     aligned = ((uintptr_t)logits % 16) == ((uintptr_t)grad_logits % 16);
     for (int d = 0; d < 3; ++d) aligned = aligned && (((logits_strides[d] - grad_strides[d]) * e) % 16 == 0);
   }
+  *grads_out = grads;
+  *aligned_out = aligned;
+  return TDT_OK;
+}
+
+hipError_t launch_rows(const Params& p, bool aligned, hipStream_t s, int which) {
+  return p.dtype == 0 ? tdt::launch_rows_f32(p, aligned, s, which)
+                      : (p.dtype == 1 ? tdt::launch_rows_f16(p, aligned, s, which)
+                                      : tdt::launch_rows_bf16(p, aligned, s, which));
+}
+
+int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, const void* logits,
+                 const int64_t* logits_strides, const void* dur_logits, const int64_t* dur_strides,
+                 int32_t num_durations, const int64_t* labels, int64_t labels_stride, const int64_t* logit_lengths,
+                 const int64_t* label_lengths, const int32_t* durations, int32_t blank, double sigma,
+                 int32_t reduction, float* loss_out, void* grad_logits, const int64_t* grad_strides,
+                 void* grad_dur_logits, const int64_t* grad_dur_strides, int32_t* utt_status, void* workspace,
+                 size_t workspace_bytes, void* stream, void* const* events, int32_t num_events) {
+  Params p;
+  bool grads = false, aligned = false;
+  const int rc = prepare(dtype, B, T_max, U1_max, V, logits, logits_strides, dur_logits, dur_strides, num_durations,
+                         labels, labels_stride, logit_lengths, label_lengths, durations, blank, sigma, reduction,
+                         loss_out, true, false, grad_logits, grad_strides, grad_dur_logits, grad_dur_strides,
+                         utt_status, workspace, workspace_bytes, &p, &grads, &aligned);
+  if (rc != TDT_OK) return rc;
 
   hipStream_t st = (hipStream_t)stream;
-  auto rows = [&](const Params& q, int which, hipStream_t s) {
-    return dtype == 0 ? tdt::launch_rows_f32(q, aligned, s, which)
-                      : (dtype == 1 ? tdt::launch_rows_f16(q, aligned, s, which)
-                                    : tdt::launch_rows_bf16(q, aligned, s, which));
-  };
   // events: 4 = {start, end, before the gradient pass, after it}; 7 = phase boundaries
   const bool phases = num_events == 7;
   auto rec = [&](int i) {
     if (events && i < num_events && events[i]) (void)hipEventRecord((hipEvent_t)events[i], st);
   };
   rec(0);
-  if (rows(p, 0, st) != hipSuccess) return TDT_ERR_HIP;
+  if (launch_rows(p, aligned, st, 0) != hipSuccess) return TDT_ERR_HIP;
   if (phases) rec(1);
   if (tdt::launch_lattice_side(p, 0, st) != hipSuccess) return TDT_ERR_HIP;
   if (phases) rec(2);
@@ -247,7 +310,7 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
   if (phases) rec(3);
   if (grads && tdt::launch_lattice_side(p, 2, st) != hipSuccess) return TDT_ERR_HIP;
   rec(phases ? 4 : 2);
-  if (grads && rows(p, 1, st) != hipSuccess) return TDT_ERR_HIP;
+  if (grads && launch_rows(p, aligned, st, 1) != hipSuccess) return TDT_ERR_HIP;
   rec(phases ? 5 : 3);
   // with gradients the coefficient kernel has reduced the loss already
   if (!grads && tdt::launch_lattice_side(p, 3, st) != hipSuccess) return TDT_ERR_HIP;
@@ -286,4 +349,26 @@ extern "C" int tdt_loss_fwd_bwd_timed(int32_t dtype, int64_t B, int64_t T_max, i
                       labels, labels_stride, logit_lengths, label_lengths, durations, blank, sigma, reduction,
                       loss_out, grad_logits, grad_strides, grad_dur_logits, grad_dur_strides, utt_status, workspace,
                       workspace_bytes, stream, events, num_events);
+}
+
+extern "C" int tdt_loss_backward(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,
+                                 const void* logits, const int64_t* logits_strides, const void* dur_logits,
+                                 const int64_t* dur_strides, int32_t num_durations, const int64_t* labels,
+                                 int64_t labels_stride, const int64_t* logit_lengths, const int64_t* label_lengths,
+                                 const int32_t* durations, int32_t blank, double sigma, int32_t reduction,
+                                 const float* grad_loss, void* grad_logits, const int64_t* grad_strides,
+                                 void* grad_dur_logits, const int64_t* grad_dur_strides, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  Params p;
+  bool grads = false, aligned = false;
+  const int rc = prepare(dtype, B, T_max, U1_max, V, logits, logits_strides, dur_logits, dur_strides, num_durations,
+                         labels, labels_stride, logit_lengths, label_lengths, durations, blank, sigma, reduction,
+                         nullptr, false, true, grad_logits, grad_strides, grad_dur_logits, grad_dur_strides,
+                         nullptr, workspace, workspace_bytes, &p, &grads, &aligned);
+  if (rc != TDT_OK) return rc;
+  p.gscale = grad_loss;
+  hipStream_t st = (hipStream_t)stream;
+  if (tdt::launch_lattice_side(p, 2, st) != hipSuccess) return TDT_ERR_HIP;
+  if (launch_rows(p, aligned, st, 1) != hipSuccess) return TDT_ERR_HIP;
+  return TDT_OK;
 }

@@ -49,8 +49,9 @@ struct Params {
   int Btot;
   const int64_t* Ulen_tot;
   // outputs
-  float* loss;
+  float* loss;     // NULL: the loss is not written (gradient-only call)
   int32_t* ustatus;
+  const float* gscale;  // gradient scale per utterance ([B], reduction none) or [1]; NULL = 1
   void* gtok;
   int64_t gs0, gs1, gs2;
   void* gdur;

@@ -917,12 +917,13 @@ __device__ void reduce_loss(const Params& p) {
 
 // A group of NG lanes works on one node (as in the node weights): lane d handles the
 // blank and the label move of duration value d; the group sums give O, c_blank, c_label.
-// The first work-group also reduces the loss (the lattice has finished every log P).
+// The first work-group also reduces the loss (the lattice has finished every log P) unless
+// the call writes no loss.  An upstream gradient (chain rule) scales w_b.
 template <int DM>
 __global__ __launch_bounds__(256) void k_coef(const Params p) {
   constexpr int NW = 2 * DM + 1;
   constexpr int NG = DM < 8 ? 8 : (DM < 16 ? 16 : 32);
-  if (blockIdx.x == 0 && threadIdx.x == 0) reduce_loss(p);
+  if (p.loss && blockIdx.x == 0 && threadIdx.x == 0) reduce_loss(p);
   const int64_t gt = (int64_t)xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
   const int j = threadIdx.x & (NG - 1);
   const int64_t g = gt / NG;
@@ -973,7 +974,7 @@ __global__ __launch_bounds__(256) void k_coef(const Params p) {
     cl += __shfl_xor(cl, o, NG);
   }
   const double O = cb + cl;
-  const double wgt = p.wts[b];
+  const double wgt = p.gscale ? p.wts[b] * (double)p.gscale[p.red == 0 ? b : 0] : p.wts[b];
   const double* pr = p.pr + pos * p.NPR;
   float* rec = p.rec + pos * p.RS;
   if (j == 0) {

@@ -26,7 +26,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert {"tdt_loss_fwd_bwd", "tdt_loss_workspace_size", "tdt_loss_status_string",
-            "tdt_loss_abi_version", "tdt_loss_fwd_bwd_timed"} <= names
+            "tdt_loss_abi_version", "tdt_loss_fwd_bwd_timed", "tdt_loss_backward"} <= names
     lib = _native.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -103,3 +103,56 @@ def test_timed_entry_rejects_bad_event_lists(n_events):
                                     FAKE, _native.i32_array([0, 1, 2]), 8, 0.0, 3, FAKE, None, None, None, None,
                                     None, FAKE, ctypes.c_size_t(1 << 40), None, evs, n_events)
     assert rc == _native.TDT_ERR_INVALID_ARGUMENT
+
+
+# Gradient views against the logits views of _call's shape (B 2, T 10, U1 5, V 9, D 3,
+# rows of 450/45/9 elements; bf16): the token logits span FAKE .. FAKE + 900 B.
+@pytest.mark.parametrize("over,code", [
+    # in place (the same pointer and strides): accepted, then stopped by the empty workspace
+    (dict(glog=FAKE, gstr=[450, 45, 9], gdur=FAKE + 4096, gdstr=[450, 45, 9]), _native.TDT_ERR_WORKSPACE_TOO_SMALL),
+    # separate buffers: accepted likewise
+    (dict(glog=FAKE + 8192, gstr=[450, 45, 9], gdur=FAKE + 12288, gdstr=[450, 45, 9]),
+     _native.TDT_ERR_WORKSPACE_TOO_SMALL),
+    # token gradient shifted by one element into the logits: rejected
+    (dict(glog=FAKE + 2, gstr=[450, 45, 9], gdur=FAKE + 12288, gdstr=[450, 45, 9]),
+     _native.TDT_ERR_INVALID_ARGUMENT),
+    # same pointer, other strides: not in place, overlaps: rejected
+    (dict(glog=FAKE, gstr=[900, 90, 18], gdur=FAKE + 12288, gdstr=[450, 45, 9]), _native.TDT_ERR_INVALID_ARGUMENT),
+    # duration gradient over the token logits: rejected
+    (dict(glog=FAKE + 8192, gstr=[450, 45, 9], gdur=FAKE + 100, gdstr=[450, 45, 9]),
+     _native.TDT_ERR_INVALID_ARGUMENT),
+    # duration gradient just past the end of the duration logits: accepted
+    (dict(glog=FAKE + 8192, gstr=[450, 45, 9], gdur=FAKE + 4096 + 2 * (450 + 9 * 45 + 4 * 9 + 3),
+          gdstr=[450, 45, 9]), _native.TDT_ERR_WORKSPACE_TOO_SMALL),
+    # ... and one element earlier: rejected
+    (dict(glog=FAKE + 8192, gstr=[450, 45, 9], gdur=FAKE + 4096 + 2 * (450 + 9 * 45 + 4 * 9 + 2),
+          gdstr=[450, 45, 9]), _native.TDT_ERR_INVALID_ARGUMENT),
+])
+def test_gradient_overlap_rules(over, code):
+    assert _call(**over) == code
+
+
+def _bwd(**over):
+    args = dict(dtype=2, B=2, T_max=10, U1_max=5, V=9, logits=FAKE, lstr=[450, 45, 9], dur=FAKE + 4096,
+                dstr=[450, 45, 9], D=3, labels=FAKE, lab_stride=4, tlen=FAKE, ulen=FAKE, durations=[0, 1, 2],
+                blank=8, sigma=0.0, reduction=3, grad_loss=None, glog=FAKE + 8192, gstr=[450, 45, 9],
+                gdur=FAKE + 12288, gdstr=[450, 45, 9], ws=FAKE, ws_bytes=0, stream=None)
+    args.update(over)
+    return _native.backward_raw(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(), _native.TDT_ERR_WORKSPACE_TOO_SMALL),
+    (dict(grad_loss=FAKE), _native.TDT_ERR_WORKSPACE_TOO_SMALL),
+    (dict(glog=None, gstr=None, gdur=None, gdstr=None), _native.TDT_ERR_INVALID_ARGUMENT),  # gradients required
+    (dict(gdur=None), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(dtype=5), _native.TDT_ERR_UNSUPPORTED_DTYPE),
+    (dict(reduction=7), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(blank=9), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(durations=[1, 1, 2]), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(glog=FAKE + 2), _native.TDT_ERR_INVALID_ARGUMENT),  # overlaps the logits
+    (dict(glog=FAKE, gdur=FAKE + 4096), _native.TDT_ERR_WORKSPACE_TOO_SMALL),  # in place
+    (dict(ws_bytes=1 << 40, ws=FAKE + 8), _native.TDT_ERR_BAD_STRIDE),
+])
+def test_backward_rejects_invalid_arguments(over, code):
+    assert _bwd(**over) == code
