@@ -17,7 +17,8 @@ using tdt::Params;
 
 struct Layout {
   int KD, WP, DM, NW, NPR, RS, nseg, nch;
-  int RW;
+  int RW, UW;
+  size_t off_pwin, off_pwout, pw_bytes;
   size_t off_rstat, off_part, off_pr, off_wout, off_win, off_ar, off_br, off_rec;
   size_t off_logp, off_logpa, off_wts, off_pm, off_pe, off_uok, off_xflag;
   size_t total;
@@ -63,6 +64,9 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
   // the lattice addresses one utterance's weight records with 32-bit byte offsets
   if ((size_t)L->KD * (size_t)L->WP * (size_t)L->RW > (size_t)0x7fffffff) return TDT_ERR_UNSUPPORTED;
   if (NP > ((size_t)1 << 40)) return TDT_ERR_UNSUPPORTED;
+  // the row passes index (position, segment) pairs with 32-bit integers
+  if (NP * (size_t)L->nseg >= ((size_t)1 << 31)) return TDT_ERR_UNSUPPORTED;
+  if ((size_t)B * (size_t)Tmax * (size_t)U1max * (size_t)L->nseg >= ((size_t)1 << 31)) return TDT_ERR_UNSUPPORTED;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -77,6 +81,13 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
   L->off_ar = take(NP * 16);
   L->off_br = take(NP * 16);
   L->off_rec = take(NP * (size_t)L->RS * 4);
+  // slot-major plain weights for the single-wave sweep (up to 256 labels + 1), addressed
+  // with 32-bit byte offsets per utterance
+  L->UW = (int)((U1max + 3) & ~(int64_t)3);
+  const size_t pw_utt = (size_t)L->KD * (size_t)L->NW * (size_t)L->UW * 8;
+  L->pw_bytes = (U1max <= 256 && pw_utt <= (size_t)0x7fffffff) ? pw_utt * (size_t)B : 0;
+  L->off_pwin = take(L->pw_bytes);
+  L->off_pwout = take(L->pw_bytes);
   L->off_logp = take((size_t)B * 8);
   L->off_logpa = take((size_t)B * 8);
   L->off_wts = take((size_t)B * 8);
@@ -212,6 +223,11 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   p.nseg = L.nseg;
   p.nch = L.nch;
   p.sigma = sigma;
+  p.fd_nseg = tdt::make_fastdiv((uint32_t)L.nseg);
+  p.fd_wp = tdt::make_fastdiv((uint32_t)L.WP);
+  p.fd_kdwp = tdt::make_fastdiv((uint32_t)L.KD * (uint32_t)L.WP);
+  p.fd_u1 = tdt::make_fastdiv((uint32_t)U1_max);
+  p.fd_tu1 = tdt::make_fastdiv((uint32_t)T_max * (uint32_t)U1_max);
   for (int d = 0; d <= tdt::kMaxDval; ++d) p.didx[d] = -1;
   for (int i = 0; i < num_durations; ++i) {
     p.dval[i] = durations[i];
@@ -253,6 +269,9 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   p.br = ws + L.off_br;
   p.RW = L.RW;
   p.rec = (float*)(ws + L.off_rec);
+  p.UW = L.UW;
+  p.pwin = L.pw_bytes ? (double*)(ws + L.off_pwin) : nullptr;
+  p.pwout = L.pw_bytes ? (double*)(ws + L.off_pwout) : nullptr;
   p.logp = (double*)(ws + L.off_logp);
   p.logpa = (double*)(ws + L.off_logpa);
   p.wts = (double*)(ws + L.off_wts);

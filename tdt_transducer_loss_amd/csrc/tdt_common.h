@@ -21,6 +21,23 @@ constexpr double kLn2Hi = 6.93147180369123816490e-01;  // ln2 with 32 trailing z
 constexpr double kLn2Lo = 1.90821492927058770002e-10;
 constexpr double kLog2eD = 1.4426950408889634074;
 
+// Division of a non-negative int below 2^31 by a fixed divisor d:
+//   n / d = (mulhi(n, m) + n) >> s,  s = ceil(log2 d),  m = floor(2^32 (2^s - d) / d) + 1
+// (Granlund and Montgomery, "Division by invariant integers using multiplication",
+// PLDI 1994; the add cannot overflow for n < 2^31).
+struct FastDiv {
+  uint32_t m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while (((uint64_t)1 << s) < d) ++s;
+  const uint64_t m = (((uint64_t)1 << 32) * (((uint64_t)1 << s) - d)) / d + 1;
+  return FastDiv{(uint32_t)m, s};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.s; }
+
 // Everything the kernels of one call need, passed by value.
 //
 // Workspace layout.  Per utterance b the lattice nodes are stored by anti-diagonal:
@@ -31,6 +48,7 @@ struct Params {
   int B, Tmax, U1max, V, D, blank, red, dtype;
   int KD, WP, DM, NW, NPR, RS;
   int nseg, nch;  // row segments per row, 16-byte chunks per lane per segment
+  FastDiv fd_nseg, fd_wp, fd_kdwp, fd_u1, fd_tu1;  // by nseg, WP, KD*WP, U1max, Tmax*U1max
   double sigma;
   int dval[kMaxD];          // duration value of index i
   int didx[kMaxDval + 1];   // index of duration value d, -1 when absent
@@ -57,8 +75,8 @@ struct Params {
   void* gdur;
   int64_t gds0, gds1, gds2;
   // workspace, per position
-  float4* rstat;  // {m, K, h_blank, h_label}: m = row maximum, K = log2 sum 2^((x - m) log2e)
-  float* part;    // [2 * nseg] per row segment: its maximum m and its sum 2^((x - m) log2e)
+  float4* rstat;  // {c, K, h_blank, h_label}: log-sum-exp of the row = lse(c, K), see row_lse
+  float* part;    // [2 * nseg] per row segment: its shift c and its sum 2^(x log2e - c), see k_row_partial
   double* pr;     // [NPR]: softmax(h)_blank, softmax(h)_label, softmax(g) by duration value 0..DM
   char* wout;     // [positions] weight records of the moves out of each node (RW bytes)
   char* win;      // [positions] weight records of the moves into each node
@@ -66,6 +84,9 @@ struct Params {
   char* br;       // [positions] beta, same records
   int RW;         // bytes per weight record
   float* rec;     // [RS] per-node record of the gradient pass
+  double* pwin;   // slot-major plain weights of the moves into / out of each node,
+  double* pwout;  //   [b][k][slot][u] (NULL when U1max > 256)
+  int UW;         // labels per row of pwin / pwout
   // workspace, per utterance
   double* logp;   // log P from beta(0,0)
   double* logpa;  // log P from the alpha terminal (diagnostic)
@@ -130,6 +151,13 @@ __device__ __forceinline__ Ext ext_sum(const Ext (&t)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) s += ldexp(t[i].m, t[i].e - E);
   return ext_norm(s, E);
+}
+
+// Log-sum-exp of a row from its statistics {c, K}: 32-bit logits keep c as the row
+// maximum (the sum is taken of 2^((x - c) log2e)), 16-bit logits keep c in base-2 units
+// (the sum is taken of 2^(x log2e - c)); K = log2 of the sum.
+__device__ __forceinline__ double row_lse(bool base2, double c, double K) {
+  return base2 ? (c + K) * kLn2 : c + K * kLn2;
 }
 
 // ---- lattice layout ----
@@ -255,6 +283,57 @@ __device__ __forceinline__ void chunk_set(uint4& c, int s, uint32_t bitsv) {
 }
 
 // ---- wave reductions (64 lanes) ----
+// DPP forms: quad swaps, then the half-row and row mirrors leave every lane of a 16-lane
+// row holding the row's result; the four rows are combined from lanes 0, 16, 32, 48.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const long long b = __double_as_longlong(x);
+  const int lo = dpp_i<CTRL>((int)b), hi = dpp_i<CTRL>((int)(b >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  const long long b = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_readlane((int)b, l), hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+// maximum over the wave, uniform result
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+  return fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)), fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
+}
+// maximum of ints over the wave, uniform result
+constexpr int kNoExp = -(1 << 30);
+__device__ __forceinline__ int wave_max_i32(int x) {
+  x = max(x, dpp_i<0xB1>(x));
+  x = max(x, dpp_i<0x4E>(x));
+  x = max(x, dpp_i<0x141>(x));
+  x = max(x, dpp_i<0x140>(x));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+// sum over the wave, uniform result (a fixed order: deterministic)
+__device__ __forceinline__ double wave_sum_dpp(double x) {
+  x += dpp_d<0xB1>(x);
+  x += dpp_d<0x4E>(x);
+  x += dpp_d<0x141>(x);
+  x += dpp_d<0x140>(x);
+  return (readlane_d(x, 0) + readlane_d(x, 16)) + (readlane_d(x, 32) + readlane_d(x, 48));
+}
+
 __device__ __forceinline__ float wave_max_f32(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));

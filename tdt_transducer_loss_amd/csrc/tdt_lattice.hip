@@ -67,6 +67,13 @@ __device__ __forceinline__ bool wrec_put_weight(char* rec, int NW, int s, Ext w)
   return n.e < -299 || n.e > 300;
 }
 
+// Slot-major copy of the plain float64 weights for the single-wave sweep (empty when the
+// utterances have more than 256 labels): [b][k][slot][u], rows of UW labels, so that one
+// load of a slot for the lanes of a wave reads consecutive bytes.
+__device__ __forceinline__ void pw_put(double* pw, const Params& p, int b, int k, int s, int u, Ext w) {
+  if (pw) pw[(((int64_t)b * p.KD + k) * p.NW + s) * p.UW + u] = w.m == 0.0 ? 0.0 : ldexp(w.m, w.e);
+}
+
 __device__ __forceinline__ Ext wrec_get(const char* rec, int NW, int s) {
   return Ext{((const double*)rec)[s], ((const int*)(rec + 8 * NW))[s] - kWBias};
 }
@@ -131,27 +138,30 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
   const int64_t dbase = (int64_t)b * p.ds0 + (int64_t)t * p.ds1 + (int64_t)u * p.ds2;
   const double gl = has ? (double)load_dur(p, dbase + idx) : -__builtin_inf();
 
-  // log-sum-exp of the token logits from the row-segment partials (lane s: segment s)
+  // log-sum-exp of the token logits from the row-segment partials (lane s: segment s);
+  // 16-bit logits keep their shifts in base-2 units (see k_row_partial).  A NaN partial
+  // (logits beyond the float range of the shift) propagates.
+  const bool base2 = p.dtype != 0;
+  const float F = base2 ? 1.f : kLog2e;
   const float* part = p.part + pos * 2 * p.nseg;
   float ms = -__builtin_inff();
   float ps = 0.f;
   for (int s2 = j; s2 < p.nseg; s2 += NG) {
     const float m2 = part[2 * s2], p2 = part[2 * s2 + 1];
-    if (p2 > 0.f) {
+    if (!(p2 <= 0.f)) {
       const float mn = fmaxf(ms, m2);
-      ps = (ps > 0.f ? ps * __builtin_amdgcn_exp2f((ms - mn) * kLog2e) : 0.f) +
-           p2 * __builtin_amdgcn_exp2f((m2 - mn) * kLog2e);
+      ps = (ps != 0.f ? ps * __builtin_amdgcn_exp2f((ms - mn) * F) : 0.f) + p2 * __builtin_amdgcn_exp2f((m2 - mn) * F);
       ms = mn;
     }
   }
   float mx = ms;
 #pragma unroll
   for (int o = NG / 2; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, NG));
-  double S = ps > 0.f ? (double)ps * exp2(((double)ms - (double)mx) * kLog2eD) : 0.0;
+  double S = ps != 0.f ? (double)ps * exp2(((double)ms - (double)mx) * (base2 ? 1.0 : kLog2eD)) : 0.0;
 #pragma unroll
   for (int o = NG / 2; o >= 1; o >>= 1) S += __shfl_xor(S, o, NG);
   const double K = log2(S);
-  const double L = (double)mx + K * kLn2;  // natural-log normaliser
+  const double L = row_lse(base2, (double)mx, K);  // natural-log normaliser
   const float4 rs = p.rstat[pos];
   const double lb = (double)rs.z - L;
   const double ly = (u < U && rs.w > -__builtin_inff()) ? (double)rs.w - L : -__builtin_inf();
@@ -189,20 +199,30 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
       const bool ok = has && (inside || (t + d == T && u == U));
       const Ext wb = ok ? ext_mul(eb, ed) : ext_zero();
       wide |= wrec_put_weight(orec, NW, d - 1, wb);
+      pw_put(p.pwout, p, b, k, d - 1, u, wb);
       if (inside) {  // incoming slot of (t+d, u)
         const int k2 = k + d;
         wrec_put_weight(wrec(p.win, p, ub + (int64_t)k2 * p.WP + (u - diag_ulo(k2, T))), NW, d - 1, wb);
+        pw_put(p.pwin, p, b, k2, d - 1, u, wb);
       }
-      if (t - d < 0) wrec_put(irec, NW, d - 1, ext_zero());  // no source for this slot
+      if (t - d < 0) {  // no source for this slot
+        wrec_put(irec, NW, d - 1, ext_zero());
+        pw_put(p.pwin, p, b, k, d - 1, u, ext_zero());
+      }
     }
     const bool inside = u < U && t + d < T;
     const Ext wl = (has && inside) ? ext_mul(ey, ed) : ext_zero();
     wide |= wrec_put_weight(orec, NW, DM + d, wl);
+    pw_put(p.pwout, p, b, k, DM + d, u, wl);
     if (inside) {  // incoming slot of (t+d, u+1)
       const int k2 = k + d + 1;
       wrec_put_weight(wrec(p.win, p, ub + (int64_t)k2 * p.WP + (u + 1 - diag_ulo(k2, T))), NW, DM + d, wl);
+      pw_put(p.pwin, p, b, k2, DM + d, u + 1, wl);
     }
-    if (u == 0 || t - d < 0) wrec_put(irec, NW, DM + d, ext_zero());
+    if (u == 0 || t - d < 0) {
+      wrec_put(irec, NW, DM + d, ext_zero());
+      pw_put(p.pwin, p, b, k, DM + d, u, ext_zero());
+    }
   }
   if (wide) atomicOr(p.xflag + b, 1);
 }
@@ -422,11 +442,12 @@ __device__ void sweep(const Params& p, int b, int T, int U, int tid, double* xm,
 }
 
 // ------------------------------------------------------------------------------------
-// Plain-float64 sweep (one wave, one label index per lane).  Lane u keeps its values as
-// plain float64 numbers x relative to a lane scale: value = x * 2^sc.  Every S steps
-// each lane shifts its rings and sc so that its newest value is near 1; a neighbour's
-// value arrives with the neighbour's scale and is converted once.  A step is then
-// DM + (DM + 1) fused multiply-adds on plain numbers.  Every move weight of the
+// Plain-float64 sweep (one wave, R label indices per lane).  Every lane keeps its values
+// as plain float64 numbers x relative to one wave-wide scale: value = x * 2^sc.  Every S
+// steps the wave shifts its rings and sc so that the largest value of two steps back is
+// near 1; a neighbour's value arrives in the same scale, so the step's serial chain is
+// the lane shift and the fused multiply-adds: DM + (DM + 1) per label on plain numbers.
+// Values far below the wave's largest underflow.  Every move weight of the
 // utterance lies in [2^-300, 2^300] (checked by the node-weight kernel).  Mass lost to
 // underflow (or an overflow) cannot be seen step by step without cost; it is caught
 // afterwards by comparing log P from the two directions, each of which would lose a
@@ -445,29 +466,41 @@ struct WMant {  // the NW plain-float64 weights of a record (its first 8*NW byte
   }
 };
 
-// Record buffers of the plain sweep: as many as fit about 240 VGPRs (R records of
-// 2*DM+1 float64 per buffer), from {12, 6, 3, 2}; 0 when even 2 do not fit in 200 (the
-// extended-range sweep is used then).
+// Record buffers of the plain sweep, from {6, 3, 2}: as many as fit about 240 VGPRs (R
+// labels of 2*DM+1 float64 per buffer) and keep the loads of NB-1 steps in flight within
+// the 6-bit memory counter (per step: one load per slot, two per slot for R = 4, and R
+// stores); 0 when even 2 do not fit in 200 VGPRs (the extended-range sweep is used then).
 template <int DM, int R>
 __host__ __device__ constexpr int fast_buffers() {
-  constexpr int per = R * 2 * (2 * DM + 1);  // VGPRs of one buffer
-  return 12 * per <= 240 ? 12 : (6 * per <= 240 ? 6 : (3 * per <= 240 ? 3 : (2 * per <= 200 ? 2 : 0)));
+  constexpr int NW = 2 * DM + 1;
+  constexpr int per = R * 2 * NW;                        // VGPRs of one buffer
+  constexpr int ops = NW * (R == 4 ? 2 : 1) + R;         // memory instructions per step
+  constexpr int steps = 60 / ops;                        // steps in flight
+  return (6 * per <= 240 && steps >= 5) ? 6
+         : (3 * per <= 240 && steps >= 2) ? 3
+         : (2 * per <= 200 && steps >= 1) ? 2 : 0;
 }
 
+// The NW weights of R consecutive labels, loaded slot by slot from the slot-major copy.
+template <int DM, int R>
+struct WPlain {
+  static constexpr int NW = 2 * DM + 1;
+  double v[NW][R];
+};
+
 template <int DM, int R, bool ALPHA>
-__device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, lds_int* prog, double* lp_out) {
+__device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, double* lp_out) {
   constexpr int S = ring_size<DM>();
-  constexpr int RWB = rec_bytes(DM);
-  // record buffers, prefetched NB-1 steps ahead (a few microseconds for R = 1: the
-  // records stay reachable at full HBM latency even when L2 lost them)
+  // weight buffers, prefetched NB-1 steps ahead
   constexpr int NB = fast_buffers<DM, R>();
   constexpr int UL = NB > S ? NB : S;  // steps unrolled per iteration
   static_assert(NB >= 2 && UL % S == 0 && UL % NB == 0, "unroll must hold whole rings and buffer rounds");
   const int nsteps = T + U;
-  const int WP = p.WP;
+  const int WP = p.WP, UW = p.UW;
   const int64_t nrec = (int64_t)p.KD * WP;
+  const int64_t npw = (int64_t)p.KD * p.NW * UW;  // plain weights of one utterance
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((ALPHA ? p.win : p.wout) + b * nrec * RWB), (short)0, (int)(nrec * RWB), 0x00020000);
+      (void*)((ALPHA ? p.pwin : p.pwout) + b * npw), (short)0, (int)(npw * 8), 0x00020000);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((ALPHA ? p.ar : p.br) + b * nrec * 16), (short)0, (int)(nrec * 16), 0x00020000);
   const int u0 = lane * R;  // labels u0 .. u0 + R - 1 of this lane
@@ -481,25 +514,32 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, lds_i
 #pragma unroll
     for (int r = 0; r < R; ++r) h[r][s] = 0.0;
   }
-  int sc = 0;
-  bool started = false;  // the lane holds a non-zero value, so its scale is fixed
+  int sc = 0;  // one scale for the whole wave: a value is x * 2^sc in every lane
   if (!ALPHA && u0 <= U && U < u0 + R) {  // beta(T, U): the terminal
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (u0 + r == U) h[r][S - 1] = 1.0;
-    started = true;
   }
-  WMant<DM> wb[NB][R];
-  auto load_w = [&](int ks, WMant<DM> (&w)[R]) {
+  WPlain<DM, R> wb[NB];
+  auto load_w = [&](int ks, WPlain<DM, R>& w) {
     const int k = ALPHA ? ks : nsteps - 1 - ks;
-    const int base = k * WP - diag_ulo(k, T) + u0;
+    constexpr int NW = 2 * DM + 1;
+    int off = (k * NW * UW + u0) * 8;
+    asm volatile("" : "+v"(off));
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      int off = (base + r) * RWB;
-      asm volatile("" : "+v"(off));
+    for (int sl = 0; sl < NW; ++sl) {
+      const int o = off + sl * UW * 8;
+      if constexpr (R == 1) {
+        const u32x2v x = __builtin_amdgcn_raw_buffer_load_b64(wr, o, 0, 0);
+        w.v[sl][0] = __builtin_bit_cast(double, ((uint64_t)x.y << 32) | x.x);
+      } else {
 #pragma unroll
-      for (int j = 0; j < WMant<DM>::NQ; ++j) w[r].q[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16 * j, 0, 0);
-      w[r].tail = __builtin_amdgcn_raw_buffer_load_b64(wr, off + 16 * WMant<DM>::NQ, 0, 0);
+        for (int r2 = 0; r2 < R; r2 += 2) {
+          const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(wr, o + 8 * r2, 0, 0);
+          w.v[sl][r2] = __builtin_bit_cast(double, ((uint64_t)x.y << 32) | x.x);
+          w.v[sl][r2 + 1] = __builtin_bit_cast(double, ((uint64_t)x.w << 32) | x.z);
+        }
+      }
     }
   };
   // past the last step the loads fall outside this utterance's records (zeros) or hit
@@ -512,12 +552,14 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, lds_i
 #pragma unroll
     for (int q = 0; q < UL; ++q) {
       const int ph = q % S;  // ring slot
-      if (ph == 0) {  // keep the lane's largest newest value near 1 (a zero lane shifts by 0)
-        double big = fabs(h[0][S - 1]);
+      if (ph == 0) {  // keep the wave's largest value of two steps back near 1
+        double big = fabs(h[0][S - 2]);
 #pragma unroll
-        for (int r = 1; r < R; ++r) big = fmax(big, fabs(h[r][S - 1]));
+        for (int r = 1; r < R; ++r) big = fmax(big, fabs(h[r][S - 2]));
         int ex;
         (void)frexp(big, &ex);
+        ex = wave_max_i32(big != 0.0 ? ex : kNoExp);
+        if (ex == kNoExp) ex = 0;  // an all-zero wave keeps its scale
         sc += ex;
 #pragma unroll
         for (int s2 = 0; s2 < S; ++s2) {
@@ -533,13 +575,13 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, lds_i
       double a[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const WMant<DM>& w = wb[q % NB][r];
+        const WPlain<DM, R>& w = wb[q % NB];
         // own moves (durations 1..DM), and the neighbour label's moves (durations 0..DM):
         // label u-1 (alpha) or u+1 (beta), in this lane or from the next lane over
         double c0 = 0.0, c1 = 0.0, c2 = 0.0, c3 = 0.0;
 #pragma unroll
         for (int d = 1; d <= DM; ++d) {
-          const double x = h[r][(ph - d + 4 * S) % S] * w.get(d - 1);
+          const double x = h[r][(ph - d + 4 * S) % S] * w.v[d - 1][r];
           if (d & 1) c0 += x; else c1 += x;
         }
 #pragma unroll
@@ -547,15 +589,11 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, lds_i
           const int sl = (ph - 1 - d + 4 * S) % S;
           const double src = ALPHA ? (r > 0 ? h[r > 0 ? r - 1 : 0][sl] : nb[sl])
                                    : (r < R - 1 ? h[r < R - 1 ? r + 1 : 0][sl] : nb[sl]);
-          const double x = src * w.get(DM + d);
+          const double x = src * w.v[DM + d][r];
           if (d & 1) c3 += x; else c2 += x;
         }
         a[r] = (c0 + c1) + (c2 + c3);
-        if (ALPHA && ks == 0 && u0 + r == 0) {
-          a[r] = 1.0;
-          sc = 0;
-          started = true;
-        }
+        if (ALPHA && ks == 0 && u0 + r == 0) a[r] = 1.0;  // alpha(0, 0), at scale 0
         if (!((unsigned)(k - u0 - r) < Tl[r])) a[r] = 0.0;
       }
 #pragma unroll
@@ -568,27 +606,16 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, lds_i
         const uint64_t mb = __builtin_bit_cast(uint64_t, ma);
         __builtin_amdgcn_raw_buffer_store_b128(u32x4v{(uint32_t)mb, (uint32_t)(mb >> 32), (uint32_t)eo, 0u}, xr, o, 0,
                                                0);
-        started = started || a[r] != 0.0;
       }
       // lane exchange: alpha passes its last label's value to the next lane, beta its
       // first label's value to the previous lane
       const double out = ALPHA ? a[R - 1] : a[0];
       const long long bits = __double_as_longlong(out);
-      int lo = (int)(bits & 0xffffffffll), hi = (int)(bits >> 32), e = sc;
+      int lo = (int)(bits & 0xffffffffll), hi = (int)(bits >> 32);
       constexpr int ctl = ALPHA ? 0x138 : 0x130;  // wave_shr:1 / wave_shl:1
       lo = __builtin_amdgcn_update_dpp(0, lo, ctl, 0xf, 0xf, false);
       hi = __builtin_amdgcn_update_dpp(0, hi, ctl, 0xf, 0xf, false);
-      e = __builtin_amdgcn_update_dpp(0, e, ctl, 0xf, 0xf, false);
-      const double m = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
-      {  // an empty lane takes a scale that puts its first input near 1 (the sender's
-         // own scale may be stale at the wavefront, far from the value it sends)
-        int em;
-        (void)frexp(m, &em);  // 0 for a zero
-        if (!started) sc = e + em;
-      }
-      started = started || m != 0.0;
-      nb[ph] = ldexp(m, e - sc);
-      __hip_atomic_store(prog, ks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      nb[ph] = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);  // same scale
     }
   }
   if (ALPHA) {
@@ -867,10 +894,11 @@ __global__ __launch_bounds__(SW ? 256 : (R <= 4 ? 768 : 1024)) void k_lattice(co
     const bool alpha = (wv & 1) == 0;
     lds_int* prog = (lds_int*)&s_prog[wv & 1];
     if constexpr (fast_buffers<DM, R>() > 0) {
-      if (!p.xflag[b]) {
-        if (wv == 0) sweep_fast<DM, R, true>(p, b, T, U, lane, prog, &s_lp[0]);
-        else if (wv == 1) sweep_fast<DM, R, false>(p, b, T, U, lane, prog, &s_lp[1]);
-        else l2_warm(p, b, T + U, alpha, lane, prog);
+      if (!p.xflag[b] && p.pwin) {
+        // no L2 warm-up here: the slot-major weights are read in few cache lines per step,
+        // and a helper's loads cost the chains more than the misses they save
+        if (wv == 0) sweep_fast<DM, R, true>(p, b, T, U, lane, &s_lp[0]);
+        else if (wv == 1) sweep_fast<DM, R, false>(p, b, T, U, lane, &s_lp[1]);
         __syncthreads();
         const double la = s_lp[0], lb = s_lp[1];
         if (la == lb || fabs(la - lb) <= 1e-9) return;
@@ -987,8 +1015,14 @@ __global__ __launch_bounds__(256) void k_coef(const Params p) {
       Gb -= wgt * cl;
       y = -1;
     }
-    rec[0] = (float)(wgt * O * exp2(-(double)rs.y));
-    rec[1] = rs.x;
+    const double wO = wgt * O;
+    if (p.dtype == 0) {  // A = w O 2^-K and the row maximum
+      rec[0] = (float)(wO * exp2(-(double)rs.y));
+      rec[1] = rs.x;
+    } else {  // the sign of w O and C = c + K - log2|w O| (base 2)
+      rec[0] = wO < 0.0 ? -1.f : 1.f;
+      rec[1] = (float)((double)rs.x + (double)rs.y - log2(fabs(wO)));
+    }
     rec[2] = (float)Gb;
     rec[3] = (float)Gy;
     rec[4] = __int_as_float(y);

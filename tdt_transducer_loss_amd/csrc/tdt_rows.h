@@ -7,8 +7,8 @@
 //                  kernel of the same comment).
 //
 // A row of V elements is covered by the 16-byte aligned chunks that overlap it (an
-// aligned chunk holding a byte of the row never leaves that row's page); head and tail
-// slots are masked on reads and written slot by slot.  A row is split into `nseg`
+// aligned chunk holding a byte of the row never leaves that row's page); the first and
+// last chunk are read element by element and written slot by slot.  A row is split into `nseg`
 // segments of 64 x NCH chunks, one 64-lane wave per segment, so that a wave keeps at
 // most 8 chunks (32 VGPRs) of raw data in flight and many waves fit on each SIMD.
 #pragma once
@@ -28,8 +28,10 @@ __device__ __forceinline__ uint4 neg_inf_chunk() {
 
 // Running maximum of the raw chunk words, in a form that shares no arithmetic with the
 // float decode of the exp pass (so the compiler keeps only the raw words alive).
-//   fp32: float max;  fp16: packed half max;  bf16: packed int16 max of order-preserving
-//   keys (negative values get their magnitude bits flipped).
+//   fp32: float max;  fp16: packed half max;  bf16: packed signed-int16 max of the raw
+//   words, exact when the lane holds a non-negative value (non-negative bf16 values order
+//   like their bit patterns); a segment with no non-negative value takes an exact second
+//   pass over order-preserving keys (negative values get their magnitude bits flipped).
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
@@ -56,10 +58,20 @@ struct MaxAcc<F16> {
 template <>
 struct MaxAcc<BF16> {
   s16x2 m = {(short)-32768, (short)-32768};
+  __device__ __forceinline__ void add(uint32_t w) { m = __builtin_elementwise_max(m, __builtin_bit_cast(s16x2, w)); }
+  // the lane's maximum when it is non-negative, else -inf
+  __device__ __forceinline__ float value() const {
+    const short k = m.x > m.y ? m.x : m.y;
+    return k >= 0 ? __uint_as_float(((uint32_t)(uint16_t)k) << 16) : -__builtin_inff();
+  }
+};
+
+// exact bf16 maximum of raw words through order-preserving keys
+struct KeyMaxBF16 {
+  s16x2 m = {(short)-32768, (short)-32768};
   __device__ __forceinline__ void add(uint32_t w) {
     const s16x2 x = __builtin_bit_cast(s16x2, w);
-    const s16x2 key = x ^ ((x >> (short)15) & (short)0x7fff);
-    m = __builtin_elementwise_max(m, key);
+    m = __builtin_elementwise_max(m, x ^ ((x >> (short)15) & (short)0x7fff));
   }
   __device__ __forceinline__ float value() const {
     const short k = m.x > m.y ? m.x : m.y;
@@ -86,12 +98,23 @@ __device__ __forceinline__ RowCover row_cover(const void* row, int V) {
   return rc;
 }
 
+// Exponent (base 2) of one element relative to the segment's shift:
+//   fp32:   (x - c) log2e with c the segment maximum (exact difference, one rounding);
+//   16-bit: fma(x, log2e, -c) with c = round(maximum * log2e) (one instruction; c is
+//           stored, so the sum and every later use of it agree on the same shift).
+template <typename TI>
+__device__ __forceinline__ float expo(float x, float c) {
+  if constexpr (TI::kEpc == 4) return (x - c) * kLog2e;
+  else return __builtin_fmaf(x, kLog2e, -c);
+}
+
 // Partial log-sum-exp of one row segment.  Writes, per (node, segment):
-//   part[2*seg] = m = segment maximum, part[2*seg + 1] = sum 2^((h - m) log2e)
+//   part[2*seg] = c, part[2*seg + 1] = sum 2^expo(h, c)
 // (floats, in a [positions][2*nseg] array), and the blank / label logits into rstat.
-// Exponents are formed as (h - m) * log2e: the difference is small for the elements
-// that carry the sum, so the rounding of log2e and of the product stays far below a
-// float32 ulp of the result whatever the magnitude of the logits.
+// A segment is NCH windows of 64 16-byte chunks, one chunk per lane per window; windows
+// that hold no chunk of the row are skipped.  The first and the last chunk of the row
+// (which may hold elements of other rows) are left out of the chunk windows and read
+// element by element, one element per lane, so the windows need no per-element masks.
 template <typename TI, int NCH>
 __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
   constexpr int EPC = TI::kEpc;
@@ -102,114 +125,167 @@ __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
     for (int i = threadIdx.x; i < p.B; i += blockDim.x) p.xflag[i] = 0;
   // persistent: a fixed grid of waves walks the (position, segment) space, skipping
   // positions outside their utterance in a few instructions (ragged batches leave most
-  // of the padded space empty)
-  const int nseg = p.nseg;
-  const int64_t per = (int64_t)p.KD * p.WP;
-  const int64_t total = (int64_t)p.B * per * nseg;
-  const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t g = (int64_t)xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv; g < total; g += stride) {
-    const int64_t node = g / nseg;
+  // of the padded space empty); the host keeps this space below 2^31
+  const uint32_t nseg = (uint32_t)p.nseg, WP = (uint32_t)p.WP;
+  const uint32_t per = (uint32_t)p.KD * WP;
+  const uint32_t total = (uint32_t)p.B * per * nseg;
+  const uint32_t stride = gridDim.x * kWavesPerBlock;
+  for (uint32_t g = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv; g < total; g += stride) {
+    const uint32_t node = fdiv(g, p.fd_nseg);
     const int seg = (int)(g - node * nseg);
-    const int b = (int)(node / per);
-    const int64_t rem = node - (int64_t)b * per;
-    const int k = (int)(rem / p.WP);
-    const int i = (int)(rem - (int64_t)k * p.WP);
+    const uint32_t b = fdiv(node, p.fd_kdwp);
+    const uint32_t rem = node - b * per;
+    const uint32_t k = fdiv(rem, p.fd_wp);
+    const int i = (int)(rem - k * WP);
     const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
     if (!utt_dims_ok(p, T64, U64)) continue;
     const int T = (int)T64, U = (int)U64;
-    if (k >= T + U) continue;
-    const int u = diag_ulo(k, T) + i;
-    if (u > min(k, U)) continue;
-    const int t = k - u;
+    if ((int)k >= T + U) continue;
+    const int u = diag_ulo((int)k, T) + i;
+    if (u > min((int)k, U)) continue;
+    const int t = (int)k - u;
 
-    int y = -1;
-    if (u < U) {
-      const int64_t yy = p.labels[(int64_t)b * p.lab_stride + u];
-      if (yy >= 0 && yy < p.V) y = (int)yy;
-    }
     const int V = p.V;
     const ET* row = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
     const RowCover rc = row_cover<TI>(row, V);
+    const int nch = rc.nch;
     const int c0 = seg * 64 * NCH;
-
+    const int nwin = (nch - c0 + 63) >> 6;  // windows of this segment holding chunks (may exceed NCH)
+    // range-checked loads: chunks at or past the end of the row read as zero bits (and
+    // are masked below)
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)rc.base, (short)0, nch * 16, 0x00020000);
     uint4 v[NCH];
-  #pragma unroll
+#pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int c = c0 + lane + 64 * j;
-      v[j] = c < rc.nch ? rc.base[c] : neg_inf_chunk<TI>();
+      if (j < nwin) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (c0 + lane + 64 * j) * 16, 0, 0);
+        v[j] = make_uint4(x.x, x.y, x.z, x.w);
+      }
     }
-    float* rs = (float*)(p.rstat + rem + (int64_t)b * per);
-    const int cb = (rc.head + p.blank) / EPC, sb = (rc.head + p.blank) % EPC;
-    const int cy = y >= 0 ? (rc.head + y) / EPC : -1, sy = y >= 0 ? (rc.head + y) % EPC : 0;
-    MaxAcc<TI> mx;
-  #pragma unroll
+    // the first and the last chunk of the row, element by element: elements [0, eh) in
+    // the segment holding chunk 0, elements [V - et, V) in the segment holding chunk nch-1
+    const int eh = c0 == 0 ? min(V, EPC - rc.head) : 0;
+    const bool tail_here = nch > 1 && nch - 1 >= c0 && nch - 1 < c0 + 64 * NCH;
+    const int et = tail_here ? V - ((nch - 1) * EPC - rc.head) : 0;
+    float xe = -__builtin_inff();
+    if (lane < eh) xe = TI::load(row, lane);
+    else if (lane - eh < et) xe = TI::load(row, V - et + (lane - eh));
+    // the blank and label logits, by the segment that holds their chunk
+    const int seg_span = 64 * NCH;
+    float4* rs = p.rstat + rem + (int64_t)b * per;
+    if (lane == 0) {
+      if ((rc.head + p.blank) / EPC / seg_span == seg) ((float*)rs)[2] = TI::load(row, p.blank);
+      int y = -1;
+      if (u < U) {
+        const int64_t yy = p.labels[(int64_t)b * p.lab_stride + u];
+        if (yy >= 0 && yy < V) y = (int)yy;
+      }
+      if (y >= 0 ? (rc.head + y) / EPC / seg_span == seg : seg == 0)
+        ((float*)rs)[3] = y >= 0 ? TI::load(row, y) : -__builtin_inff();
+    }
+    // chunk 0, chunk nch-1 and chunks past the row hold no element for the windows
+#pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int c = c0 + lane + 64 * j;
-      if (c == 0 || c == rc.nch - 1) {
-  #pragma unroll
+      const int cw = c0 + 64 * j;
+      if (j < nwin && (cw == 0 || cw + 63 >= nch - 1)) {
+        const int c = cw + lane;
+        if (c == 0 || c >= nch - 1) v[j] = neg_inf_chunk<TI>();
+      }
+    }
+    MaxAcc<TI> mx;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      if (j < nwin) {
+        mx.add(v[j].x);
+        mx.add(v[j].y);
+        mx.add(v[j].z);
+        mx.add(v[j].w);
+      }
+    }
+    float mw = wave_max_dpp(fmaxf(mx.value(), xe));
+    if constexpr (__is_same(TI, BF16)) {
+      if (!(mw >= 0.f)) {  // no non-negative value in the segment: exact maximum from keys
+        KeyMaxBF16 km;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          if (j < nwin) {
+            km.add(v[j].x);
+            km.add(v[j].y);
+            km.add(v[j].z);
+            km.add(v[j].w);
+          }
+        }
+        mw = wave_max_dpp(fmaxf(km.value(), xe));
+      }
+    }
+    // the shift: the maximum itself (fp32) or maximum * log2e rounded to float (16-bit)
+    const float c = EPC == 4 ? mw : mw * kLog2e;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      if (j < nwin) {
+#pragma unroll
         for (int s = 0; s < EPC; ++s) {
-          const int e = c * EPC + s - rc.head;
-          if (e < 0 || e >= V) chunk_set<TI>(v[j], s, TI::kNegInf);
+          const float e2 = __builtin_amdgcn_exp2f(expo<TI>(TI::get(v[j], s), c));
+          if ((s & 3) == 0) a0 += e2;
+          else if ((s & 3) == 1) a1 += e2;
+          else if ((s & 3) == 2) a2 += e2;
+          else a3 += e2;
         }
       }
-      if (c == cb) rs[2] = TI::get(v[j], sb);
-      if (c == cy) rs[3] = TI::get(v[j], sy);
-      mx.add(v[j].x);
-      mx.add(v[j].y);
-      mx.add(v[j].z);
-      mx.add(v[j].w);
     }
-    // lane-local exp sum relative to the lane's own maximum
-    const float ml = mx.value();
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-  #pragma unroll
-      for (int s = 0; s < EPC; ++s) {
-        const float e2 = __builtin_amdgcn_exp2f((TI::get(v[j], s) - ml) * kLog2e);
-        if ((s & 3) == 0) a0 += e2;
-        else if ((s & 3) == 1) a1 += e2;
-        else if ((s & 3) == 2) a2 += e2;
-        else a3 += e2;
-      }
-    }
-    float acc = (a0 + a1) + (a2 + a3);
-    if (!(ml > -__builtin_inff())) acc = 0.f;  // a lane holding only masked slots
-    const float mw = wave_max_f32(ml);
-    const float scaled = acc > 0.f ? acc * __builtin_amdgcn_exp2f((ml - mw) * kLog2e) : 0.f;
-    const double S = wave_sum_f64((double)scaled);
+    float acc = ((a0 + a1) + (a2 + a3)) + __builtin_amdgcn_exp2f(expo<TI>(xe, c));
+    const bool empty = !(mw > -__builtin_inff());  // every slot masked: an empty segment
+    if (empty) acc = 0.f;
+    double S = wave_sum_dpp((double)acc);
+    // 16-bit logits beyond about 2.3e38 in magnitude leave no float shift: NaN partial
+    if (!empty && !(__builtin_fabsf(c) < __builtin_inff())) S = __builtin_nan("");
     if (lane == 0) {
-      float* part = p.part + (rem + (int64_t)b * per) * 2 * nseg + 2 * seg;
-      part[0] = mw;
+      float* part = p.part + ((int64_t)rem + (int64_t)b * per) * 2 * nseg + 2 * seg;
+      part[0] = empty ? -__builtin_inff() : c;
       part[1] = (float)S;
-      if (seg == 0 && y < 0) rs[3] = -__builtin_inff();
     }
   }
 }
 
+// Gradient value w O softmax(h)_v of one element from its node's record:
+//   fp32:   A 2^((x - m) log2e),  A = w O 2^-K, m the row maximum;
+//   16-bit: 2^(x log2e - C),      C = c + K - log2|w O| (one fma and one exp2), with the
+//           sign of w O (held in A) applied by the caller.
+template <typename TI>
+__device__ __forceinline__ float grad_val(float x, float A, float m) {
+  if constexpr (TI::kEpc == 4) return A * __builtin_amdgcn_exp2f((x - m) * kLog2e);
+  else return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -m));
+}
+
 // Gradient of one row segment (natural node order over the padded [B, Tmax, U1max]):
-//   grad_v = w O softmax(h)_v  computed as  A' * 2^((h_v - m) log2e),  A' = w O 2^-K,
-// with the blank and label columns and the D duration gradients taken from the per-node
-// record (computed in float64 from the lattice).  Padded nodes and utterances without
-// gradient get zeros.  ALIGNED: the logits row and the gradient row have the same
-// address modulo 16 bytes (then both use the same chunks); otherwise each lane walks
-// single elements.
+// grad_val for every column, with the blank and label columns and the D duration
+// gradients taken from the per-node record (computed in float64 from the lattice).
+// Padded nodes and utterances without gradient get zeros.  ALIGNED: the logits row and
+// the gradient row have the same address modulo 16 bytes (then both use the same
+// chunks); otherwise each lane walks single elements.  The host keeps
+// B * Tmax * U1max * nseg below 2^31.
 template <typename TI, int NCH, bool ALIGNED>
 __global__ __launch_bounds__(256) void k_grad(const Params p) {
   constexpr int EPC = TI::kEpc;
   using ET = typename TI::T;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t g = (int64_t)xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
-  const int nseg = p.nseg;
-  const int64_t node = g / nseg;
+  // nodes in reverse order: the row-statistics pass read the last utterances last, so
+  // their rows are the ones still held in the last-level cache when this pass starts
+  const uint32_t nseg = (uint32_t)p.nseg;
+  const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
+  const uint32_t total = (uint32_t)p.B * per * nseg;
+  const uint32_t gf = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
+  if (gf >= total) return;
+  const uint32_t g = total - 1 - gf;
+  const uint32_t node = fdiv(g, p.fd_nseg);
   const int seg = (int)(g - node * nseg);
-  const int64_t per = (int64_t)p.Tmax * p.U1max;
-  const int b = (int)(node / per);
-  if (b >= p.B) return;
-  const int64_t rem = node - (int64_t)b * per;
-  const int t = (int)(rem / p.U1max);
-  const int u = (int)(rem - (int64_t)t * p.U1max);
+  const uint32_t b = fdiv(node, p.fd_tu1);
+  const uint32_t rem = node - b * per;
+  const int t = (int)fdiv(rem, p.fd_u1);
+  const int u = (int)(rem - (uint32_t)t * (uint32_t)p.U1max);
   const int V = p.V;
 
   bool valid = false;
@@ -253,24 +329,35 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
     }
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int c = c0 + lane + 64 * j;
+      const int cw = c0 + 64 * j;  // first chunk of the window
+      if (cw >= nch) break;
+      const int c = cw + lane;
       if (c >= nch) continue;
       float o[EPC];
+      if (valid) {
 #pragma unroll
-      for (int s = 0; s < EPC; ++s)
-        o[s] = valid ? A * __builtin_amdgcn_exp2f((TI::get(v[j], s) - m) * kLog2e) : 0.f;
-      if (valid && c == cb) {
+        for (int s = 0; s < EPC; ++s) o[s] = grad_val<TI>(TI::get(v[j], s), A, m);
+        if (EPC == 8 && A < 0.f) {  // 16-bit: a negative w O (upstream gradient)
 #pragma unroll
-        for (int s = 0; s < EPC; ++s)
-          if (s == sb) o[s] = Gb;
-      }
-      if (valid && c == cy) {
+          for (int s = 0; s < EPC; ++s) o[s] = -o[s];
+        }
+        if ((unsigned)(cb - cw) < 64u && c == cb) {
 #pragma unroll
-        for (int s = 0; s < EPC; ++s)
-          if (s == sy) o[s] = Gy;
+          for (int s = 0; s < EPC; ++s)
+            if (s == sb) o[s] = Gb;
+        }
+        if ((unsigned)(cy - cw) < 64u && c == cy) {
+#pragma unroll
+          for (int s = 0; s < EPC; ++s)
+            if (s == sy) o[s] = Gy;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < EPC; ++s) o[s] = 0.f;
       }
       const int e0 = c * EPC - head;
-      if (e0 >= 0 && e0 + EPC <= V) {
+      // windows away from the row's first and last chunk store whole chunks
+      if ((cw > 0 && cw + 63 < nch - 1) || (e0 >= 0 && e0 + EPC <= V)) {
         const uint4 q = TI::pack(o);
         __builtin_nontemporal_store(u32x4{q.x, q.y, q.z, q.w}, (u32x4*)(obase + c));
       } else {
@@ -288,7 +375,8 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
     for (int e = seg * span + lane; e < e_end; e += 64) {
       float o = 0.f;
       if (valid) {
-        o = A * __builtin_amdgcn_exp2f((TI::load(irow, e) - m) * kLog2e);
+        o = grad_val<TI>(TI::load(irow, e), A, m);
+        if (EPC == 8 && A < 0.f) o = -o;
         if (e == p.blank) o = Gb;
         if (e == ycol) o = Gy;
       }
