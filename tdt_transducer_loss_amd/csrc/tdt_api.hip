@@ -20,7 +20,7 @@ struct Layout {
   int RW, UW;
   size_t off_pwin, off_pwout, pw_bytes;
   size_t off_rstat, off_part, off_pr, off_wout, off_win, off_ar, off_br, off_rec;
-  size_t off_logp, off_logpa, off_wts, off_pm, off_pe, off_uok, off_xflag;
+  size_t off_logp, off_logpa, off_wts, off_pm, off_pe, off_uok, off_xflag, off_lpx, off_lcnt;
   size_t total;
 };
 
@@ -84,7 +84,7 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
   // slot-major plain weights for the single-wave sweep (up to 256 labels + 1), addressed
   // with 32-bit byte offsets per utterance
   L->UW = (int)((U1max + 3) & ~(int64_t)3);
-  const size_t pw_utt = (size_t)L->KD * (size_t)L->NW * (size_t)L->UW * 8;
+  const size_t pw_utt = (size_t)L->KD * (size_t)((L->NW + 1) / 2) * (size_t)L->UW * 16;
   L->pw_bytes = (U1max <= 256 && pw_utt <= (size_t)0x7fffffff) ? pw_utt * (size_t)B : 0;
   L->off_pwin = take(L->pw_bytes);
   L->off_pwout = take(L->pw_bytes);
@@ -95,6 +95,8 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
   L->off_pe = take((size_t)B * 4);
   L->off_uok = take((size_t)B * 4);
   L->off_xflag = take((size_t)B * 4);
+  L->off_lpx = take((size_t)B * 16);
+  L->off_lcnt = take((size_t)B * 4);
   L->total = o;
   return TDT_OK;
 }
@@ -279,6 +281,8 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   p.pe = (int*)(ws + L.off_pe);
   p.uok = (int*)(ws + L.off_uok);
   p.xflag = (int*)(ws + L.off_xflag);
+  p.lpx = (double*)(ws + L.off_lpx);
+  p.lcnt = (int*)(ws + L.off_lcnt);
 
   // Row and gradient chunks coincide when the logits and gradient rows share their
   // address modulo 16 bytes for every node.

@@ -84,8 +84,8 @@ struct Params {
   char* br;       // [positions] beta, same records
   int RW;         // bytes per weight record
   float* rec;     // [RS] per-node record of the gradient pass
-  double* pwin;   // slot-major plain weights of the moves into / out of each node,
-  double* pwout;  //   [b][k][slot][u] (NULL when U1max > 256)
+  double* pwin;   // plain weights of the moves into / out of each node, by slot pair:
+  double* pwout;  //   [b][k][slot / 2][u][slot % 2] (NULL when U1max > 256)
   int UW;         // labels per row of pwin / pwout
   // workspace, per utterance
   double* logp;   // log P from beta(0,0)
@@ -95,6 +95,8 @@ struct Params {
   int* pe;
   int* uok;       // 1: gradients are written from the lattice, 0: zeros
   int* xflag;     // 1: some move weight lies outside [2^-300, 2^300] (extended-range sweep only)
+  double* lpx;    // [2]: log P of the plain single-wave sweep, alpha and beta
+  int* lcnt;      // plain single-wave sweeps finished (zeroed by the row-statistics pass)
 };
 
 // ---- extended-range non-negative numbers: value = m * 2^e ----

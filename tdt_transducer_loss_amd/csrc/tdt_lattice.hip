@@ -67,11 +67,16 @@ __device__ __forceinline__ bool wrec_put_weight(char* rec, int NW, int s, Ext w)
   return n.e < -299 || n.e > 300;
 }
 
-// Slot-major copy of the plain float64 weights for the single-wave sweep (empty when the
-// utterances have more than 256 labels): [b][k][slot][u], rows of UW labels, so that one
-// load of a slot for the lanes of a wave reads consecutive bytes.
+// Slot-pair-major copy of the plain float64 weights for the single-wave sweep (empty when
+// the utterances have more than 256 labels): [b][k][slot / 2][u][slot % 2], rows of UW
+// labels, so that one 16-byte load per lane fetches two slots of its label and the lanes
+// of a wave read consecutive bytes.
+__host__ __device__ constexpr int slot_pairs(int NW) { return (NW + 1) / 2; }
+
 __device__ __forceinline__ void pw_put(double* pw, const Params& p, int b, int k, int s, int u, Ext w) {
-  if (pw) pw[(((int64_t)b * p.KD + k) * p.NW + s) * p.UW + u] = w.m == 0.0 ? 0.0 : ldexp(w.m, w.e);
+  if (pw)
+    pw[((((int64_t)b * p.KD + k) * slot_pairs(p.NW) + (s >> 1)) * p.UW + u) * 2 + (s & 1)] =
+        w.m == 0.0 ? 0.0 : ldexp(w.m, w.e);
 }
 
 __device__ __forceinline__ Ext wrec_get(const char* rec, int NW, int s) {
@@ -468,13 +473,13 @@ struct WMant {  // the NW plain-float64 weights of a record (its first 8*NW byte
 
 // Record buffers of the plain sweep, from {6, 3, 2}: as many as fit about 240 VGPRs (R
 // labels of 2*DM+1 float64 per buffer) and keep the loads of NB-1 steps in flight within
-// the 6-bit memory counter (per step: one load per slot, two per slot for R = 4, and R
-// stores); 0 when even 2 do not fit in 200 VGPRs (the extended-range sweep is used then).
+// the 6-bit memory counter (per step: one load per slot pair and label, and R stores); 0
+// when even 2 do not fit in 200 VGPRs (the extended-range sweep is used then).
 template <int DM, int R>
 __host__ __device__ constexpr int fast_buffers() {
   constexpr int NW = 2 * DM + 1;
   constexpr int per = R * 2 * NW;                        // VGPRs of one buffer
-  constexpr int ops = NW * (R == 4 ? 2 : 1) + R;         // memory instructions per step
+  constexpr int ops = slot_pairs(NW) * R + R;            // memory instructions per step
   constexpr int steps = 60 / ops;                        // steps in flight
   return (6 * per <= 240 && steps >= 5) ? 6
          : (3 * per <= 240 && steps >= 2) ? 3
@@ -498,7 +503,7 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, doubl
   const int nsteps = T + U;
   const int WP = p.WP, UW = p.UW;
   const int64_t nrec = (int64_t)p.KD * WP;
-  const int64_t npw = (int64_t)p.KD * p.NW * UW;  // plain weights of one utterance
+  const int64_t npw = (int64_t)p.KD * slot_pairs(p.NW) * UW * 2;  // plain weights of one utterance
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((ALPHA ? p.pwin : p.pwout) + b * npw), (short)0, (int)(npw * 8), 0x00020000);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
@@ -523,22 +528,16 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, doubl
   WPlain<DM, R> wb[NB];
   auto load_w = [&](int ks, WPlain<DM, R>& w) {
     const int k = ALPHA ? ks : nsteps - 1 - ks;
-    constexpr int NW = 2 * DM + 1;
-    int off = (k * NW * UW + u0) * 8;
+    constexpr int NW = 2 * DM + 1, NP = slot_pairs(NW);
+    int off = (k * NP * UW + u0) * 16;
     asm volatile("" : "+v"(off));
 #pragma unroll
-    for (int sl = 0; sl < NW; ++sl) {
-      const int o = off + sl * UW * 8;
-      if constexpr (R == 1) {
-        const u32x2v x = __builtin_amdgcn_raw_buffer_load_b64(wr, o, 0, 0);
-        w.v[sl][0] = __builtin_bit_cast(double, ((uint64_t)x.y << 32) | x.x);
-      } else {
+    for (int pr = 0; pr < NP; ++pr) {
 #pragma unroll
-        for (int r2 = 0; r2 < R; r2 += 2) {
-          const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(wr, o + 8 * r2, 0, 0);
-          w.v[sl][r2] = __builtin_bit_cast(double, ((uint64_t)x.y << 32) | x.x);
-          w.v[sl][r2 + 1] = __builtin_bit_cast(double, ((uint64_t)x.w << 32) | x.z);
-        }
+      for (int r = 0; r < R; ++r) {
+        const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(wr, off + (pr * UW + r) * 16, 0, 0);
+        w.v[2 * pr][r] = __builtin_bit_cast(double, ((uint64_t)x.y << 32) | x.x);
+        if (2 * pr + 1 < NW) w.v[2 * pr + 1][r] = __builtin_bit_cast(double, ((uint64_t)x.w << 32) | x.z);
       }
     }
   };
@@ -832,25 +831,24 @@ __device__ void l2_warm(const Params& p, int b, int nsteps, bool alpha, int lane
   if (acc == 0x9e3779b9u && p.B < 0) p.uok[0] = (int)acc;  // keeps the touching loads alive
 }
 
-// Lattice kernel.  SW (U1max <= 256): one 256-thread work-group per utterance, wave 0
-// the alpha chain, wave 1 the beta chain, waves 2 and 3 their L2 warm-up.  Where its
-// registers fit (fast_buffers), the chains first run the plain-float64 sweep; if log P
-// from the alpha side and from the beta side differ by more than 1e-9 (rounding alone
-// stays below 1e-12: both sides sum the same probability mass in float64), both
-// directions are redone with the extended-range sweep.  Otherwise one work-group of up to
-// 768 threads (1024 for R = 8) per (utterance, direction), with the range-checked
-// multi-wave plain sweep where its registers fit (fast_mw_ok) and the extended-range
-// sweep after it or instead of it.
+// Lattice kernel, one work-group per (utterance, direction).  SW (U1max <= 256): 128
+// threads, wave 0 the chain; the plain-float64 sweep where its registers fit
+// (fast_buffers), checked by the agreement of log P from the two directions, and the
+// extended-range sweep (wave 1 keeping its records warm in L2) otherwise or when the
+// check fails.  Longer label sequences: up to 768 threads (1024 for R = 8) with the
+// range-checked multi-wave plain sweep where its registers fit (fast_mw_ok) and the
+// extended-range sweep after it or instead of it.
 template <int DM, int R, bool SW>
-__global__ __launch_bounds__(SW ? 256 : (R <= 4 ? 768 : 1024)) void k_lattice(const Params p) {
+__global__ __launch_bounds__(SW ? 128 : (R <= 4 ? 768 : 1024)) void k_lattice(const Params p) {
   __shared__ double xm[SW ? 1 : 2 * 1024];
   __shared__ int xe[SW ? 1 : 2 * 1024];
   __shared__ unsigned long long s_sumU;
   __shared__ int s_prog[2];
   __shared__ double s_lp[2];
-  const int b = SW ? blockIdx.x : blockIdx.x >> 1;
-  const int dir = SW ? -1 : (blockIdx.x & 1);
-  const bool alpha_side = dir != 1, beta_side = dir != 0;
+  __shared__ int s_redo;
+  const int b = blockIdx.x >> 1;
+  const int dir = blockIdx.x & 1;  // 0: alpha, 1: beta
+  const bool alpha_side = dir == 0, beta_side = dir == 1;
   const int tid = threadIdx.x, nt = blockDim.x;
   const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
   int status = 0;
@@ -890,25 +888,54 @@ __global__ __launch_bounds__(SW ? 256 : (R <= 4 ? 768 : 1024)) void k_lattice(co
     return;
   }
   if constexpr (SW) {
+    // one direction per work-group: wave 0 runs the chain, wave 1 keeps the records of
+    // the extended-range sweep warm in L2
     const int wv = tid >> 6, lane = tid & (kWave - 1);
-    const bool alpha = (wv & 1) == 0;
-    lds_int* prog = (lds_int*)&s_prog[wv & 1];
+    lds_int* prog = (lds_int*)&s_prog[0];
     if constexpr (fast_buffers<DM, R>() > 0) {
       if (!p.xflag[b] && p.pwin) {
-        // no L2 warm-up here: the slot-major weights are read in few cache lines per step,
-        // and a helper's loads cost the chains more than the misses they save
-        if (wv == 0) sweep_fast<DM, R, true>(p, b, T, U, lane, &s_lp[0]);
-        else if (wv == 1) sweep_fast<DM, R, false>(p, b, T, U, lane, &s_lp[1]);
+        if (wv == 0) {
+          if (alpha_side) sweep_fast<DM, R, true>(p, b, T, U, lane, &s_lp[0]);
+          else sweep_fast<DM, R, false>(p, b, T, U, lane, &s_lp[0]);
+        }
         __syncthreads();
-        const double la = s_lp[0], lb = s_lp[1];
-        if (la == lb || fabs(la - lb) <= 1e-9) return;
-        if (tid == 0) s_prog[0] = s_prog[1] = -1;
+        // The direction that finishes second compares the two log P values (both sum
+        // the same probability mass; rounding alone stays below 1e-12) and, when they
+        // differ by more than 1e-9, redoes both directions with the extended-range sweep.
+        // The counter was zeroed by the row-statistics pass of this call.
+        if (tid == 0) {
+          __hip_atomic_store(p.lpx + 2 * b + dir, s_lp[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int old = __hip_atomic_fetch_add(p.lcnt + b, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+          int redo = 0;
+          if (old == 1) {
+            const double other =
+                __hip_atomic_load(p.lpx + 2 * b + (dir ^ 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            redo = (s_lp[0] == other || fabs(s_lp[0] - other) <= 1e-9) ? 0 : 1;
+          }
+          s_redo = redo;
+        }
         __syncthreads();
+        if (!s_redo) return;
+        for (int pass = 0; pass < 2; ++pass) {
+          if (tid == 0) s_prog[0] = -1;
+          __syncthreads();
+          if (wv == 0) {
+            if (pass == 0) sweep<DM, R, true, true>(p, b, T, U, lane, xm, xe, prog);
+            else sweep<DM, R, true, false>(p, b, T, U, lane, xm, xe, prog);
+          } else {
+            l2_warm(p, b, T + U, pass == 0, lane, prog);
+          }
+          __syncthreads();
+        }
+        return;
       }
     }
-    if (wv == 0) sweep<DM, R, true, true>(p, b, T, U, lane, xm, xe, prog);
-    else if (wv == 1) sweep<DM, R, true, false>(p, b, T, U, lane, xm, xe, prog);
-    else l2_warm(p, b, T + U, alpha, lane, prog);
+    if (wv == 0) {
+      if (alpha_side) sweep<DM, R, true, true>(p, b, T, U, lane, xm, xe, prog);
+      else sweep<DM, R, true, false>(p, b, T, U, lane, xm, xe, prog);
+    } else {
+      l2_warm(p, b, T + U, alpha_side, lane, prog);
+    }
   } else {
     if constexpr (fast_mw_ok<DM, R>()) {
       if (!p.xflag[b]) {
@@ -1042,13 +1069,13 @@ __global__ void k_reduce(const Params p) {
 template <int DM>
 static hipError_t launch_lattice_dm(const Params& p, hipStream_t st) {
   const int u1 = p.U1max;
-  const dim3 grid(2 * p.B), grid_sw(p.B);
+  const dim3 grid(2 * p.B);  // one work-group per (utterance, direction)
   if (u1 <= 64) {
-    hipLaunchKernelGGL((k_lattice<DM, 1, true>), grid_sw, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_lattice<DM, 1, true>), grid, dim3(128), 0, st, p);
   } else if (u1 <= 128) {
-    hipLaunchKernelGGL((k_lattice<DM, 2, true>), grid_sw, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_lattice<DM, 2, true>), grid, dim3(128), 0, st, p);
   } else if (u1 <= 256) {
-    hipLaunchKernelGGL((k_lattice<DM, 4, true>), grid_sw, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_lattice<DM, 4, true>), grid, dim3(128), 0, st, p);
   } else {
     // at most 768 threads for R <= 4 (about 170 VGPRs per lane), 1024 for R = 8
     int R = u1 <= 768 ? 1 : u1 <= 1536 ? 2 : u1 <= 3072 ? 4 : 8;

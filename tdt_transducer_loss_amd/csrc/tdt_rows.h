@@ -121,8 +121,11 @@ __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
   using ET = typename TI::T;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (blockIdx.x == 0)  // the node-weight kernel that follows sets these flags
-    for (int i = threadIdx.x; i < p.B; i += blockDim.x) p.xflag[i] = 0;
+  if (blockIdx.x == 0)  // flags the node-weight kernel and the lattice of this call set
+    for (int i = threadIdx.x; i < p.B; i += blockDim.x) {
+      p.xflag[i] = 0;
+      p.lcnt[i] = 0;
+    }
   // persistent: a fixed grid of waves walks the (position, segment) space, skipping
   // positions outside their utterance in a few instructions (ragged batches leave most
   // of the padded space empty); the host keeps this space below 2^31
