@@ -70,7 +70,10 @@ typedef enum {
 #define TDT_UTT_INFEASIBLE 8       /* no alignment exists */
 
 /* Limits of this build: 1 <= num_durations <= 16, duration values in [0, 16] with at
- * least one > 0, U1_max <= 8192. */
+ * least one > 0, U1_max <= 8192, and fewer than 2^31 (lattice position, row segment)
+ * pairs per call, a row segment being up to 512 16-byte chunks of a logits row (beyond
+ * these: TDT_ERR_UNSUPPORTED).  bf16 logits whose row maximum exceeds about 2.3e38 in
+ * magnitude give their utterance a NaN loss. */
 #define TDT_MAX_DURATIONS 16
 #define TDT_MAX_DURATION_VALUE 16
 #define TDT_MAX_U1 8192
