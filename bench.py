@@ -12,9 +12,10 @@ cache.
 Prints one JSON line: value = algorithmic GB/s of the whole step (two reads of every
 valid lattice row and one write of every gradient row, V + D elements each), the
 roofline of the dominant kernel (the gradient pass, timed with HIP events the library
-records on the stream right before and after its launch in every timed step), a
-per-kernel breakdown from a second loop with events between all kernels, and the
-float64 CPU oracle timed on the host on the same workload.
+records on the stream right before and after its launch in every EVERY-th timed step:
+an event between two kernels stalls the stream for a few microseconds, so the other
+steps carry none), a per-kernel breakdown from a second loop with events between all
+kernels, and the float64 CPU oracle timed on the host on the same workload.
 """
 from __future__ import annotations
 
@@ -54,6 +55,7 @@ class HipEvents:
         self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.events = []
 
     def create(self) -> int:
@@ -63,6 +65,11 @@ class HipEvents:
             raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
         self.events.append(ev.value)
         return ev.value
+
+    def record(self, ev: int, stream: int) -> None:
+        rc = self.lib.hipEventRecord(self.ct.c_void_p(ev), self.ct.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed(self, a: int, b: int) -> float:
         ms = self.ct.c_float()
@@ -104,8 +111,10 @@ def measured_traffic(path: str):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--event-every", type=int, default=5,
+                    help="record the gradient-kernel events in every N-th timed step")
     ap.add_argument("--config", type=int, default=2, help="workload id in tdt_inputs.CONFIGS")
     ap.add_argument("--rotate", type=int, default=3, help="input/gradient buffer sets cycled over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -182,20 +191,25 @@ def main() -> int:
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: K steps.  The library records events[0]/[1] around the whole step
-    # and events[2]/[3] right around the gradient kernel; the step time is the host
-    # clock over the region.
+    # Timed region: K steps.  In every EVERY-th step the library records events[2]/[3]
+    # right around the gradient kernel (events[0]/[1] left out); two more events bracket
+    # the whole region.  The step time is the host clock over the region.
     K = args.steps
-    evs, handles = make_events(K, 4)
+    every = max(1, args.event_every)
+    sampled = [i for i in range(K) if i % every == 0]
+    gevs = {i: [None, None, hip.create(), hip.create()] for i in sampled}
+    region = [hip.create(), hip.create()]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    hip.record(region[0], stream.cuda_stream)
     for i in range(K):
-        step(i, handles[i])
+        step(i, gevs.get(i))
+    hip.record(region[1], stream.cuda_stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
-    grad_ms = sum(hip.elapsed(row[2], row[3]) for row in evs) / K  # average gradient-kernel launch
-    event_ms = sum(hip.elapsed(row[0], row[1]) for row in evs) / K
+    grad_ms = sum(hip.elapsed(e[2], e[3]) for e in gevs.values()) / len(gevs)  # average gradient-kernel launch
+    event_ms = hip.elapsed(region[0], region[1]) / K
 
     # Per-kernel breakdown (diagnostic, outside the timed region): events between all
     # kernels of the step.
@@ -254,7 +268,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "k_grad (gradient pass)",
-                     "kernel_ms": round(grad_ms, 4), "launches_per_step": 1, "bytes_per_launch": int(grad_bytes)},
+                     "kernel_ms": round(grad_ms, 4), "launches_per_step": 1, "bytes_per_launch": int(grad_bytes),
+                     "timed_launches": len(gevs)},
         "event_ms_per_step": round(event_ms, 4),
         "kernel_ms": {k: round(v, 4) for k, v in phase_ms.items()},
         "kernel_sum_ms": round(serial_ms, 4),
