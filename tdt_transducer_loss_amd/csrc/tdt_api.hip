@@ -81,11 +81,11 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
   L->off_ar = take(NP * 16);
   L->off_br = take(NP * 16);
   L->off_rec = take(NP * (size_t)L->RS * 4);
-  // slot-major plain weights for the single-wave sweep (up to 256 labels + 1), addressed
-  // with 32-bit byte offsets per utterance
+  // slot-pair-major plain weights for the plain sweeps, addressed with 32-bit byte
+  // offsets per utterance (without them the extended-range sweep runs)
   L->UW = (int)((U1max + 3) & ~(int64_t)3);
   const size_t pw_utt = (size_t)L->KD * (size_t)((L->NW + 1) / 2) * (size_t)L->UW * 16;
-  L->pw_bytes = (U1max <= 256 && pw_utt <= (size_t)0x7fffffff) ? pw_utt * (size_t)B : 0;
+  L->pw_bytes = pw_utt <= (size_t)0x7fffffff ? pw_utt * (size_t)B : 0;
   L->off_pwin = take(L->pw_bytes);
   L->off_pwout = take(L->pw_bytes);
   L->off_logp = take((size_t)B * 8);

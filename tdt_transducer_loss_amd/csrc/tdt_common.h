@@ -85,7 +85,7 @@ struct Params {
   int RW;         // bytes per weight record
   float* rec;     // [RS] per-node record of the gradient pass
   double* pwin;   // plain weights of the moves into / out of each node, by slot pair:
-  double* pwout;  //   [b][k][slot / 2][u][slot % 2] (NULL when U1max > 256)
+  double* pwout;  //   [b][k][slot / 2][u][slot % 2] (NULL when too large)
   int UW;         // labels per row of pwin / pwout
   // workspace, per utterance
   double* logp;   // log P from beta(0,0)

@@ -67,10 +67,10 @@ __device__ __forceinline__ bool wrec_put_weight(char* rec, int NW, int s, Ext w)
   return n.e < -299 || n.e > 300;
 }
 
-// Slot-pair-major copy of the plain float64 weights for the single-wave sweep (empty when
-// the utterances have more than 256 labels): [b][k][slot / 2][u][slot % 2], rows of UW
-// labels, so that one 16-byte load per lane fetches two slots of its label and the lanes
-// of a wave read consecutive bytes.
+// Slot-pair-major copy of the plain float64 weights for the plain sweeps (empty when one
+// utterance's copy would exceed 2 GB): [b][k][slot / 2][u][slot % 2], rows of UW labels,
+// so that one 16-byte load per lane fetches two slots of its label and the lanes of a wave
+// read consecutive bytes.
 __host__ __device__ constexpr int slot_pairs(int NW) { return (NW + 1) / 2; }
 
 __device__ __forceinline__ void pw_put(double* pw, const Params& p, int b, int k, int s, int u, Ext w) {
@@ -458,19 +458,6 @@ __device__ void sweep(const Params& p, int b, int T, int U, int tid, double* xm,
 // afterwards by comparing log P from the two directions, each of which would lose a
 // different share of it, and the caller then redoes both with the extended-range sweep.
 // Alpha/beta records are written in extended form.
-template <int DM>
-struct WMant {  // the NW plain-float64 weights of a record (its first 8*NW bytes)
-  static constexpr int NW = 2 * DM + 1;
-  static constexpr int NQ = NW / 2;  // full 16-byte words; NW is odd
-  u32x4v q[NQ];
-  u32x2v tail;
-  __device__ __forceinline__ double get(int s) const {
-    const uint32_t lo = s < 2 * NQ ? q[s >> 1][(s & 1) * 2] : tail.x;
-    const uint32_t hi = s < 2 * NQ ? q[s >> 1][(s & 1) * 2 + 1] : tail.y;
-    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-  }
-};
-
 // Record buffers of the plain sweep, from {6, 3, 2}: as many as fit about 240 VGPRs (R
 // labels of 2*DM+1 float64 per buffer) and keep the loads of NB-1 steps in flight within
 // the 6-bit memory counter (per step: one load per slot pair and label, and R stores); 0
@@ -655,13 +642,13 @@ __device__ __forceinline__ bool out_of_range(double x) {  // non-zero and outsid
 template <int DM, int R, bool ALPHA>
 __device__ bool sweep_fast_mw(const Params& p, int b, int T, int U, int tid, double* xm, int* xe) {
   constexpr int S = ring_size<DM>();
-  constexpr int RWB = rec_bytes(DM);
   const int nt = blockDim.x;
   const int nsteps = T + U;
-  const int WP = p.WP;
+  const int WP = p.WP, UW = p.UW;
   const int64_t nrec = (int64_t)p.KD * WP;
+  const int64_t npw = (int64_t)p.KD * slot_pairs(p.NW) * UW * 2;  // plain weights of one utterance
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((ALPHA ? p.win : p.wout) + b * nrec * RWB), (short)0, (int)(nrec * RWB), 0x00020000);
+      (void*)((ALPHA ? p.pwin : p.pwout) + b * npw), (short)0, (int)(npw * 8), 0x00020000);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((ALPHA ? p.ar : p.br) + b * nrec * 16), (short)0, (int)(nrec * 16), 0x00020000);
   const int u0 = tid * R;
@@ -683,16 +670,19 @@ __device__ bool sweep_fast_mw(const Params& p, int b, int T, int U, int tid, dou
       if (u0 + r == U) h[r][S - 1] = 1.0;
     started = true;
   }
-  WMant<DM> w[R];
+  WPlain<DM, R> w;  // the slot-pair-major plain weights of this lane's labels
   auto load_w = [&](int ks) {
     const int k = ALPHA ? ks : nsteps - 1 - ks;
-    const int base = k * WP - diag_ulo(k, T) + u0;
+    constexpr int NW = 2 * DM + 1, NP = slot_pairs(NW);
+    const int off = (k * NP * UW + u0) * 16;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int off = (base + r) * RWB;
+    for (int pr = 0; pr < NP; ++pr) {
 #pragma unroll
-      for (int j = 0; j < WMant<DM>::NQ; ++j) w[r].q[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16 * j, 0, 0);
-      w[r].tail = __builtin_amdgcn_raw_buffer_load_b64(wr, off + 16 * WMant<DM>::NQ, 0, 0);
+      for (int r = 0; r < R; ++r) {
+        const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(wr, off + (pr * UW + r) * 16, 0, 0);
+        w.v[2 * pr][r] = __builtin_bit_cast(double, ((uint64_t)x.y << 32) | x.x);
+        if (2 * pr + 1 < NW) w.v[2 * pr + 1][r] = __builtin_bit_cast(double, ((uint64_t)x.w << 32) | x.z);
+      }
     }
   };
   load_w(0);
@@ -726,7 +716,7 @@ __device__ bool sweep_fast_mw(const Params& p, int b, int T, int U, int tid, dou
         double c0 = 0.0, c1 = 0.0, c2 = 0.0, c3 = 0.0;
 #pragma unroll
         for (int d = 1; d <= DM; ++d) {
-          const double x = h[r][(ph - d + 4 * S) % S] * w[r].get(d - 1);
+          const double x = h[r][(ph - d + 4 * S) % S] * w.v[d - 1][r];
           if (d & 1) c0 += x; else c1 += x;
         }
 #pragma unroll
@@ -734,7 +724,7 @@ __device__ bool sweep_fast_mw(const Params& p, int b, int T, int U, int tid, dou
           const int sl = (ph - 1 - d + 4 * S) % S;
           const double src = ALPHA ? (r > 0 ? h[r > 0 ? r - 1 : 0][sl] : nb[sl])
                                    : (r < R - 1 ? h[r < R - 1 ? r + 1 : 0][sl] : nb[sl]);
-          const double x = src * w[r].get(DM + d);
+          const double x = src * w.v[DM + d][r];
           if (d & 1) c3 += x; else c2 += x;
         }
         a[r] = (c0 + c1) + (c2 + c3);
@@ -938,7 +928,7 @@ __global__ __launch_bounds__(SW ? 128 : (R <= 4 ? 768 : 1024)) void k_lattice(co
     }
   } else {
     if constexpr (fast_mw_ok<DM, R>()) {
-      if (!p.xflag[b]) {
+      if (!p.xflag[b] && p.pwin) {
         const bool trouble = dir == 0 ? sweep_fast_mw<DM, R, true>(p, b, T, U, tid, xm, xe)
                                       : sweep_fast_mw<DM, R, false>(p, b, T, U, tid, xm, xe);
         if (!trouble) return;
