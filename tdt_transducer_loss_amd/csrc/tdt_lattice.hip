@@ -96,12 +96,11 @@ __device__ __forceinline__ Ext xrec_get(const char* base, int64_t pos) {
 // plus softmax(h)_blank, softmax(h)_label and softmax(g) for the gradient.  A group of
 // NG = 8, 16 or 32 lanes (at least DM + 1) works on one lattice position: lane d of the
 // group handles duration value d, lanes 0..3 the per-node exponentials, so the float64
-// work of a node is spread over its group.  Every record of the padded [B][KD][WP]
-// layout is written: moves that leave the lattice, absent durations, moves with no
-// source and positions outside the utterance hold the zero weight, so the sweeps read
-// any in-range record without predicates.  Slot s of the incoming record of n is written
-// by the source of that move, or zeroed by n itself when the source does not exist
-// (exactly one writer per slot).
+// work of a node is spread over its group.  Every record of a node in the lattice is
+// written: moves that leave the lattice, absent durations and moves with no source hold
+// the zero weight, so the sweeps read the records of active nodes without predicates.
+// Slot s of the incoming record of n is written by the source of that move, or zeroed by
+// n itself when the source does not exist (exactly one writer per slot).
 template <int DM>
 __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
   constexpr int NW = 2 * DM + 1;
@@ -124,17 +123,10 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
   const int u = dims ? diag_ulo(k, T) + i : 0;
   const bool valid = dims && k < T + U && u <= min(k, U);
   const int d = j;
-  if (!valid) {
-    if (d <= DM) {
-      if (d >= 1) {
-        wrec_put(orec, NW, d - 1, ext_zero());
-        wrec_put(irec, NW, d - 1, ext_zero());
-      }
-      wrec_put(orec, NW, DM + d, ext_zero());
-      wrec_put(irec, NW, DM + d, ext_zero());
-    }
-    return;
-  }
+  // positions outside the utterance write nothing: every slot of a node in the lattice
+  // is written by the source of its move or zeroed by the node itself, and the sweeps
+  // discard whatever lanes outside the lattice compute
+  if (!valid) return;
   const int t = k - u;
 
   // the duration logit of this lane, loaded first
