@@ -882,9 +882,12 @@ __global__ __launch_bounds__(SW ? 128 : (R <= 4 ? 768 : 1024)) void k_lattice(co
         }
         __syncthreads();
         // The direction that finishes second compares the two log P values (both sum
-        // the same probability mass; rounding alone stays below 1e-12) and, when they
-        // differ by more than 1e-9, redoes both directions with the extended-range sweep.
-        // The counter was zeroed by the row-statistics pass of this call.
+        // the same probability mass; rounding alone stays below 1e-12) and, unless both
+        // are finite and differ by at most 1e-9, redoes both directions with the
+        // extended-range sweep: mass lost to underflow differs between the directions, and
+        // when it is all of it both read -inf, which only the extended sweep can tell
+        // from an utterance without alignments.  The counter was zeroed by the
+        // row-statistics pass of this call.
         if (tid == 0) {
           __hip_atomic_store(p.lpx + 2 * b + dir, s_lp[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const int old = __hip_atomic_fetch_add(p.lcnt + b, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
@@ -892,7 +895,8 @@ __global__ __launch_bounds__(SW ? 128 : (R <= 4 ? 768 : 1024)) void k_lattice(co
           if (old == 1) {
             const double other =
                 __hip_atomic_load(p.lpx + 2 * b + (dir ^ 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            redo = (s_lp[0] == other || fabs(s_lp[0] - other) <= 1e-9) ? 0 : 1;
+            const double mine = s_lp[0];
+            redo = (isfinite(mine) && isfinite(other) && fabs(mine - other) <= 1e-9) ? 0 : 1;
           }
           s_redo = redo;
         }

@@ -61,6 +61,16 @@ def test_long_label_config_sampled():
     assert zs <= 0.05
 
 
+def _plain_sweep_underflow():
+    # blank logits 200 above the rest: every move weight stays above 2^-300 (the plain
+    # single-wave sweep runs: 151 labels, four per lane), but the lattice values of one
+    # anti-diagonal span tens of thousands of binary orders, beyond any one float64 scale,
+    # so the plain sweeps underflow and the extended-range sweep redoes both directions
+    case = make_case(2, [40, 30], [150, 20], 5, [0, 1, 2], "f32", seed=57, reduction="none")
+    case.joint[..., 4] += 200.0
+    return case
+
+
 EDGE = {
     "no_labels": lambda: make_case(3, [7, 5, 9], [0, 0, 0], 11, [0, 1, 2, 3, 4], "f32", seed=41, sigma=0.1,
                                    reduction="sum", U1max=2),
@@ -91,6 +101,7 @@ EDGE = {
     # more than 256 labels with weights far below 2^-300: the multi-wave extended-range sweep
     "huge_logits_multiwave": lambda: make_case(1, [24], [300], 9, [0, 1, 2], "f32", seed=55, scale=400.0,
                                                reduction="sum"),
+    "plain_sweep_underflow_redo": _plain_sweep_underflow,
     "ragged_padded_f16": lambda: make_case(5, None, None, 129, [0, 1, 2, 3, 4], "f16", seed=52, Tmax=70, U1max=30,
                                            T_range=(1, 70), U_range=(0, 29), reduction="mean", extra_cols=3),
 }
