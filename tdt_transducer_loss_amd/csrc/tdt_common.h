@@ -317,16 +317,6 @@ __device__ __forceinline__ float wave_max_dpp(float x) {
   x = fmaxf(x, dpp_f<0x140>(x));  // row_mirror
   return fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)), fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
 }
-// maximum of ints over the wave, uniform result
-constexpr int kNoExp = -(1 << 30);
-__device__ __forceinline__ int wave_max_i32(int x) {
-  x = max(x, dpp_i<0xB1>(x));
-  x = max(x, dpp_i<0x4E>(x));
-  x = max(x, dpp_i<0x141>(x));
-  x = max(x, dpp_i<0x140>(x));
-  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
-             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
-}
 // sum over the wave, uniform result (a fixed order: deterministic)
 __device__ __forceinline__ double wave_sum_dpp(double x) {
   x += dpp_d<0xB1>(x);

@@ -439,12 +439,12 @@ __device__ void sweep(const Params& p, int b, int T, int U, int tid, double* xm,
 }
 
 // ------------------------------------------------------------------------------------
-// Plain-float64 sweep (one wave, R label indices per lane).  Every lane keeps its values
-// as plain float64 numbers x relative to one wave-wide scale: value = x * 2^sc.  Every S
-// steps the wave shifts its rings and sc so that the largest value of two steps back is
-// near 1; a neighbour's value arrives in the same scale, so the step's serial chain is
-// the lane shift and the fused multiply-adds: DM + (DM + 1) per label on plain numbers.
-// Values far below the wave's largest underflow.  Every move weight of the
+// Plain-float64 sweep (one wave, R label indices per lane).  Lane u keeps its values as
+// plain float64 numbers x relative to a lane scale: value = x * 2^sc.  Every S steps
+// each lane shifts its rings and sc so that its newest value is near 1; a neighbour's
+// value arrives with the neighbour's scale and is converted once, so values of different
+// labels on one anti-diagonal may lie any number of binary orders apart.  A step is then
+// DM + (DM + 1) fused multiply-adds per label on plain numbers.  Every move weight of the
 // utterance lies in [2^-300, 2^300] (checked by the node-weight kernel).  Mass lost to
 // underflow (or an overflow) cannot be seen step by step without cost; it is caught
 // afterwards by comparing log P from the two directions, each of which would lose a
@@ -498,11 +498,13 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, doubl
 #pragma unroll
     for (int r = 0; r < R; ++r) h[r][s] = 0.0;
   }
-  int sc = 0;  // one scale for the whole wave: a value is x * 2^sc in every lane
+  int sc = 0;             // the lane's scale: a value is x * 2^sc
+  bool started = false;   // the lane holds a non-zero value, so its scale is fixed
   if (!ALPHA && u0 <= U && U < u0 + R) {  // beta(T, U): the terminal
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (u0 + r == U) h[r][S - 1] = 1.0;
+    started = true;
   }
   WPlain<DM, R> wb[NB];
   auto load_w = [&](int ks, WPlain<DM, R>& w) {
@@ -530,14 +532,12 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, doubl
 #pragma unroll
     for (int q = 0; q < UL; ++q) {
       const int ph = q % S;  // ring slot
-      if (ph == 0) {  // keep the wave's largest value of two steps back near 1
-        double big = fabs(h[0][S - 2]);
+      if (ph == 0) {  // keep the lane's largest newest value near 1 (a zero lane shifts by 0)
+        double big = fabs(h[0][S - 1]);
 #pragma unroll
-        for (int r = 1; r < R; ++r) big = fmax(big, fabs(h[r][S - 2]));
+        for (int r = 1; r < R; ++r) big = fmax(big, fabs(h[r][S - 1]));
         int ex;
         (void)frexp(big, &ex);
-        ex = wave_max_i32(big != 0.0 ? ex : kNoExp);
-        if (ex == kNoExp) ex = 0;  // an all-zero wave keeps its scale
         sc += ex;
 #pragma unroll
         for (int s2 = 0; s2 < S; ++s2) {
@@ -571,7 +571,11 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, doubl
           if (d & 1) c3 += x; else c2 += x;
         }
         a[r] = (c0 + c1) + (c2 + c3);
-        if (ALPHA && ks == 0 && u0 + r == 0) a[r] = 1.0;  // alpha(0, 0), at scale 0
+        if (ALPHA && ks == 0 && u0 + r == 0) {  // alpha(0, 0)
+          a[r] = 1.0;
+          sc = 0;
+          started = true;
+        }
         if (!((unsigned)(k - u0 - r) < Tl[r])) a[r] = 0.0;
       }
 #pragma unroll
@@ -584,16 +588,26 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, doubl
         const uint64_t mb = __builtin_bit_cast(uint64_t, ma);
         __builtin_amdgcn_raw_buffer_store_b128(u32x4v{(uint32_t)mb, (uint32_t)(mb >> 32), (uint32_t)eo, 0u}, xr, o, 0,
                                                0);
+        started = started || a[r] != 0.0;
       }
       // lane exchange: alpha passes its last label's value to the next lane, beta its
       // first label's value to the previous lane
       const double out = ALPHA ? a[R - 1] : a[0];
       const long long bits = __double_as_longlong(out);
-      int lo = (int)(bits & 0xffffffffll), hi = (int)(bits >> 32);
+      int lo = (int)(bits & 0xffffffffll), hi = (int)(bits >> 32), e = sc;
       constexpr int ctl = ALPHA ? 0x138 : 0x130;  // wave_shr:1 / wave_shl:1
       lo = __builtin_amdgcn_update_dpp(0, lo, ctl, 0xf, 0xf, false);
       hi = __builtin_amdgcn_update_dpp(0, hi, ctl, 0xf, 0xf, false);
-      nb[ph] = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);  // same scale
+      e = __builtin_amdgcn_update_dpp(0, e, ctl, 0xf, 0xf, false);
+      const double m = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
+      {  // an empty lane takes a scale that puts its first input near 1 (the sender's
+         // own scale may be stale at the wavefront, far from the value it sends)
+        int em;
+        (void)frexp(m, &em);  // 0 for a zero
+        if (!started) sc = e + em;
+      }
+      started = started || m != 0.0;
+      nb[ph] = ldexp(m, e - sc);  // into this lane's scale
     }
   }
   if (ALPHA) {

@@ -62,10 +62,11 @@ def test_long_label_config_sampled():
 
 
 def _plain_sweep_underflow():
-    # blank logits 200 above the rest: every move weight stays above 2^-300 (the plain
-    # single-wave sweep runs: 151 labels, four per lane), but the lattice values of one
-    # anti-diagonal span tens of thousands of binary orders, beyond any one float64 scale,
-    # so the plain sweeps underflow and the extended-range sweep redoes both directions
+    # blank logits 200 above the rest: every move weight stays above 2^-300, so the plain
+    # single-wave sweep runs (151 labels, four per lane sharing one scale), but each label
+    # costs about 2^-290 and the four values of a lane drift beyond the float64 range:
+    # mass is lost to underflow, the two directions' log P disagree and the extended-range
+    # sweep redoes both (with the redo switched off the gradients are off by 2e-3)
     case = make_case(2, [40, 30], [150, 20], 5, [0, 1, 2], "f32", seed=57, reduction="none")
     case.joint[..., 4] += 200.0
     return case
