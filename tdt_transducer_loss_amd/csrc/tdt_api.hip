@@ -226,8 +226,6 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   p.nch = L.nch;
   p.sigma = sigma;
   p.fd_nseg = tdt::make_fastdiv((uint32_t)L.nseg);
-  p.fd_wp = tdt::make_fastdiv((uint32_t)L.WP);
-  p.fd_kdwp = tdt::make_fastdiv((uint32_t)L.KD * (uint32_t)L.WP);
   p.fd_u1 = tdt::make_fastdiv((uint32_t)U1_max);
   p.fd_tu1 = tdt::make_fastdiv((uint32_t)T_max * (uint32_t)U1_max);
   for (int d = 0; d <= tdt::kMaxDval; ++d) p.didx[d] = -1;

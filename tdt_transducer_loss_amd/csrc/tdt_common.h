@@ -48,7 +48,7 @@ struct Params {
   int B, Tmax, U1max, V, D, blank, red, dtype;
   int KD, WP, DM, NW, NPR, RS;
   int nseg, nch;  // row segments per row, 16-byte chunks per lane per segment
-  FastDiv fd_nseg, fd_wp, fd_kdwp, fd_u1, fd_tu1;  // by nseg, WP, KD*WP, U1max, Tmax*U1max
+  FastDiv fd_nseg, fd_u1, fd_tu1;  // by nseg, U1max, Tmax*U1max
   double sigma;
   int dval[kMaxD];          // duration value of index i
   int didx[kMaxDval + 1];   // index of duration value d, -1 when absent

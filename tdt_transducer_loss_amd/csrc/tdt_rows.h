@@ -126,27 +126,29 @@ __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
       p.xflag[i] = 0;
       p.lcnt[i] = 0;
     }
-  // persistent: a fixed grid of waves walks the (position, segment) space, skipping
-  // positions outside their utterance in a few instructions (ragged batches leave most
-  // of the padded space empty); the host keeps this space below 2^31
-  const uint32_t nseg = (uint32_t)p.nseg, WP = (uint32_t)p.WP;
-  const uint32_t per = (uint32_t)p.KD * WP;
+  // persistent: a fixed grid of waves walks the (node, segment) space of the padded
+  // [B, Tmax, U1max] rows in memory order, skipping nodes outside their utterance in a
+  // few instructions (ragged batches leave most of the padded space empty); the host
+  // keeps this space below 2^31
+  const uint32_t nseg = (uint32_t)p.nseg;
+  const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
+  const int64_t dper = (int64_t)p.KD * p.WP;  // lattice positions per utterance
   const uint32_t total = (uint32_t)p.B * per * nseg;
   const uint32_t stride = gridDim.x * kWavesPerBlock;
   for (uint32_t g = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv; g < total; g += stride) {
     const uint32_t node = fdiv(g, p.fd_nseg);
     const int seg = (int)(g - node * nseg);
-    const uint32_t b = fdiv(node, p.fd_kdwp);
-    const uint32_t rem = node - b * per;
-    const uint32_t k = fdiv(rem, p.fd_wp);
-    const int i = (int)(rem - k * WP);
+    const uint32_t b = fdiv(node, p.fd_tu1);
+    const uint32_t nrem = node - b * per;
+    const int t = (int)fdiv(nrem, p.fd_u1);
+    const int u = (int)(nrem - (uint32_t)t * (uint32_t)p.U1max);
     const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
     if (!utt_dims_ok(p, T64, U64)) continue;
     const int T = (int)T64, U = (int)U64;
-    if ((int)k >= T + U) continue;
-    const int u = diag_ulo((int)k, T) + i;
-    if (u > min((int)k, U)) continue;
-    const int t = (int)k - u;
+    if (t >= T || u > U) continue;
+    const int k = t + u;
+    // its lattice position (b, k, i): the anti-diagonal layout of the workspace
+    const uint32_t rem = (uint32_t)k * (uint32_t)p.WP + (uint32_t)(u - diag_ulo(k, T));
 
     const int V = p.V;
     const ET* row = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
     else if (lane - eh < et) xe = TI::load(row, V - et + (lane - eh));
     // the blank and label logits, by the segment that holds their chunk
     const int seg_span = 64 * NCH;
-    float4* rs = p.rstat + rem + (int64_t)b * per;
+    float4* rs = p.rstat + rem + (int64_t)b * dper;
     if (lane == 0) {
       if ((rc.head + p.blank) / EPC / seg_span == seg) ((float*)rs)[2] = TI::load(row, p.blank);
       int y = -1;
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
     // 16-bit logits beyond about 2.3e38 in magnitude leave no float shift: NaN partial
     if (!empty && !(__builtin_fabsf(c) < __builtin_inff())) S = __builtin_nan("");
     if (lane == 0) {
-      float* part = p.part + ((int64_t)rem + (int64_t)b * per) * 2 * nseg + 2 * seg;
+      float* part = p.part + ((int64_t)rem + (int64_t)b * dper) * 2 * nseg + 2 * seg;
       part[0] = empty ? -__builtin_inff() : c;
       part[1] = (float)S;
     }
