@@ -18,7 +18,13 @@
 namespace tdt {
 
 constexpr int kWavesPerBlock = 4;   // 256-thread work-groups
-constexpr int kRowStatBlocks = 4096;  // grid of the persistent row-statistics pass (16K waves)
+// Grid of the persistent row-statistics pass: about two (node, segment) tasks per wave,
+// at most 12288 blocks (48K waves).  Measured at B4 T200 U40 V8193 bf16 (98,400 tasks):
+// 4096 blocks 109 us, 12288 (two tasks per wave) 102 us, 16384 (one or two) 118 us,
+// 32768 (one) 109 us.
+constexpr int kRowStatBlocks = 12288;
+constexpr int kRowStatTasksPerWave = 2;
+static_assert(kRowStatBlocks % 8 == 0, "whole rounds of the eight XCDs");
 
 template <typename TI>
 __device__ __forceinline__ uint4 neg_inf_chunk() {
@@ -406,10 +412,13 @@ inline void pick_segments(int64_t V, int epc, int* nch, int* nseg) {
 template <typename TI>
 hipError_t launch_rows_t(const Params& p, bool aligned, hipStream_t st, int which) {
   const int nch = p.nch;
-  const int64_t nodes = which == 0 ? (int64_t)p.B * p.KD * p.WP : (int64_t)p.B * p.Tmax * p.U1max;
+  const int64_t nodes = (int64_t)p.B * p.Tmax * p.U1max;  // both passes walk the padded rows
   const int64_t waves = nodes * p.nseg;
   int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (which == 0 && blocks > kRowStatBlocks) blocks = kRowStatBlocks;  // persistent row statistics
+  if (which == 0) {  // persistent row statistics
+    blocks = (waves + kRowStatTasksPerWave * kWavesPerBlock - 1) / (kRowStatTasksPerWave * kWavesPerBlock);
+    if (blocks > kRowStatBlocks) blocks = kRowStatBlocks;
+  }
   const dim3 grid((unsigned)blocks);
   if (which == 0) {
 #define TDT_RS(N) \
