@@ -16,7 +16,7 @@ namespace {
 using tdt::Params;
 
 struct Layout {
-  int KD, WP, DM, NW, NPR, RS, nseg, nch;
+  int KD, WP, DM, NW, NPR, RS, nseg, nch, gnseg, gnch;
   int RW, UW;
   size_t off_pwin, off_pwout, pw_bytes;
   size_t off_rstat, off_part, off_pr, off_wout, off_win, off_ar, off_br, off_rec;
@@ -58,7 +58,8 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
   L->NW = 2 * L->DM + 1;
   L->NPR = L->DM + 3;
   L->RS = 5 + D;
-  tdt::pick_segments(V, dtype == 0 ? 4 : 8, &L->nch, &L->nseg);
+  tdt::pick_segments(V, dtype == 0 ? 4 : 8, tdt::kRowWindows, &L->nch, &L->nseg);
+  tdt::pick_segments(V, dtype == 0 ? 4 : 8, tdt::kGradWindows, &L->gnch, &L->gnseg);
   const size_t NP = (size_t)B * (size_t)L->KD * (size_t)L->WP;
   L->RW = tdt::rec_bytes(L->DM);
   // the lattice addresses one utterance's weight records with 32-bit byte offsets
@@ -66,7 +67,8 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
   if (NP > ((size_t)1 << 40)) return TDT_ERR_UNSUPPORTED;
   // the row passes index (position, segment) pairs with 32-bit integers
   if (NP * (size_t)L->nseg >= ((size_t)1 << 31)) return TDT_ERR_UNSUPPORTED;
-  if ((size_t)B * (size_t)Tmax * (size_t)U1max * (size_t)L->nseg >= ((size_t)1 << 31)) return TDT_ERR_UNSUPPORTED;
+  const size_t segs = (size_t)(L->nseg > L->gnseg ? L->nseg : L->gnseg);
+  if ((size_t)B * (size_t)Tmax * (size_t)U1max * segs >= ((size_t)1 << 31)) return TDT_ERR_UNSUPPORTED;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -224,8 +226,11 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   p.RS = L.RS;
   p.nseg = L.nseg;
   p.nch = L.nch;
+  p.gnseg = L.gnseg;
+  p.gnch = L.gnch;
   p.sigma = sigma;
   p.fd_nseg = tdt::make_fastdiv((uint32_t)L.nseg);
+  p.fd_gnseg = tdt::make_fastdiv((uint32_t)L.gnseg);
   p.fd_u1 = tdt::make_fastdiv((uint32_t)U1_max);
   p.fd_tu1 = tdt::make_fastdiv((uint32_t)T_max * (uint32_t)U1_max);
   for (int d = 0; d <= tdt::kMaxDval; ++d) p.didx[d] = -1;

@@ -47,8 +47,9 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umul
 struct Params {
   int B, Tmax, U1max, V, D, blank, red, dtype;
   int KD, WP, DM, NW, NPR, RS;
-  int nseg, nch;  // row segments per row, 16-byte chunks per lane per segment
-  FastDiv fd_nseg, fd_u1, fd_tu1;  // by nseg, U1max, Tmax*U1max
+  int nseg, nch;    // row-statistics pass: segments per row, 64-chunk windows per segment
+  int gnseg, gnch;  // the same for the gradient pass
+  FastDiv fd_nseg, fd_gnseg, fd_u1, fd_tu1;  // by nseg, gnseg, U1max, Tmax*U1max
   double sigma;
   int dval[kMaxD];          // duration value of index i
   int didx[kMaxDval + 1];   // index of duration value d, -1 when absent

@@ -286,13 +286,13 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
   // one wave per (node, segment), nodes in reverse order (the row-statistics pass ends on
   // the last rows; measured the same as natural order, and a persistent grid of two tasks
   // per wave was slower: 183 vs 180 us at B4 T200 U40 V8193 bf16, 434 vs 371 us in fp32)
-  const uint32_t nseg = (uint32_t)p.nseg;
+  const uint32_t nseg = (uint32_t)p.gnseg;
   const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
   const uint32_t total = (uint32_t)p.B * per * nseg;
   const uint32_t gf = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
   if (gf >= total) return;
   const uint32_t g = total - 1 - gf;
-  const uint32_t node = fdiv(g, p.fd_nseg);
+  const uint32_t node = fdiv(g, p.fd_gnseg);
   const int seg = (int)(g - node * nseg);
   const uint32_t b = fdiv(node, p.fd_tu1);
   const uint32_t rem = node - b * per;
@@ -401,10 +401,19 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
   }
 }
 
-// Segment split of a row of V elements: nseg segments of 64 x nch chunks, nch <= 8.
-inline void pick_segments(int64_t V, int epc, int* nch, int* nseg) {
+// Segment split of a row of V elements: nseg segments of 64 x nch chunks, nch <= maxw
+// (<= 8).  The row-statistics pass takes segments of up to 8 windows of 64 chunks, the
+// gradient pass of up to 4.  Measured (ms per step, gradient pass us) for a maximum of
+// 2 / 3 / 4 / 6 gradient windows: B4 T200 U40 V8193 bf16 0.338 173 / 0.333 170 /
+// 0.333 170 / 0.341 179; the same in fp32 0.618 350 / 0.635 368 / 0.635 367 / 0.635 367;
+// the ragged fp16 batch 1.177 660 / 1.006 489 / 1.005 489 / 1.005 488.  The
+// row-statistics pass with 4 windows: 146 vs 102 us.
+constexpr int kRowWindows = 8;
+constexpr int kGradWindows = 4;
+
+inline void pick_segments(int64_t V, int epc, int maxw, int* nch, int* nseg) {
   const int64_t chunks = (V + epc - 1) / epc + 1;
-  int64_t s = (chunks + 64 * 8 - 1) / (64 * 8);
+  int64_t s = (chunks + 64 * maxw - 1) / (64 * maxw);
   int64_t n = (chunks + 64 * s - 1) / (64 * s);
   *nseg = (int)s;
   *nch = (int)n;
@@ -412,9 +421,9 @@ inline void pick_segments(int64_t V, int epc, int* nch, int* nseg) {
 
 template <typename TI>
 hipError_t launch_rows_t(const Params& p, bool aligned, hipStream_t st, int which) {
-  const int nch = p.nch;
+  const int nch = which == 0 ? p.nch : p.gnch;
   const int64_t nodes = (int64_t)p.B * p.Tmax * p.U1max;  // both passes walk the padded rows
-  const int64_t waves = nodes * p.nseg;
+  const int64_t waves = nodes * (which == 0 ? p.nseg : p.gnseg);
   int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
   if (which == 0) {  // persistent row statistics
     blocks = (waves + kRowStatTasksPerWave * kWavesPerBlock - 1) / (kRowStatTasksPerWave * kWavesPerBlock);
