@@ -239,13 +239,16 @@ def main() -> int:
         import oracle
 
         c = case.to("cpu")
-        t = time.perf_counter()
-        oracle.run(c.tok, c.dur, c.labels, c.logit_lengths, c.label_lengths, c.durations, c.blank, c.sigma,
-                   c.reduction)
-        dt = time.perf_counter() - t
+        runs = []
+        for _ in range(3):
+            t = time.perf_counter()
+            oracle.run(c.tok, c.dur, c.labels, c.logit_lengths, c.label_lengths, c.durations, c.blank, c.sigma,
+                       c.reduction)
+            runs.append(time.perf_counter() - t)
+        dt = sorted(runs)[1]
         cpu = {"value": round(alg / dt / 1e9, 4), "unit": "GB/s", "ms": round(dt * 1e3, 1),
                "cores": oracle.max_threads(), "kind": "oracle",
-               "sample": f"the full workload (B={B}) once, float64 loss and gradient, OpenMP"}
+               "sample": f"the full workload (B={B}), median of 3 runs, float64 loss and gradient, OpenMP"}
 
     out = {
         "metric": METRIC,
