@@ -8,9 +8,11 @@
 //
 // A row of V elements is covered by the 16-byte aligned chunks that overlap it (an
 // aligned chunk holding a byte of the row never leaves that row's page); the first and
-// last chunk are read element by element and written slot by slot.  A row is split into `nseg`
-// segments of 64 x NCH chunks, one 64-lane wave per segment, so that a wave keeps at
-// most 8 chunks (32 VGPRs) of raw data in flight and many waves fit on each SIMD.
+// last chunk are read element by element and written slot by slot.  Each pass splits a
+// row into segments of up to NCH windows of 64 chunks (NCH <= 8 for the row statistics,
+// <= 4 for the gradient pass: pick_segments), one 64-lane wave per segment, so that a
+// wave keeps at most 8 chunks (32 VGPRs) of raw data in flight and many waves fit on each
+// SIMD.
 #pragma once
 
 #include "tdt_common.h"
