@@ -72,6 +72,14 @@ def _plain_sweep_underflow():
     return case
 
 
+def _all_negative(dtype):
+    # every token logit below zero (shifted by -60; the loss is unchanged by the shift): the
+    # bf16 row maximum of every segment comes from the order-preserving key pass
+    case = make_case(2, [9, 7], [3, 4], 3000, [0, 1, 2, 4], dtype, seed=58, scale=2.0, reduction="none")
+    case.joint[..., :3000] -= 60.0
+    return case
+
+
 EDGE = {
     "no_labels": lambda: make_case(3, [7, 5, 9], [0, 0, 0], 11, [0, 1, 2, 3, 4], "f32", seed=41, sigma=0.1,
                                    reduction="sum", U1max=2),
@@ -103,6 +111,8 @@ EDGE = {
     "huge_logits_multiwave": lambda: make_case(1, [24], [300], 9, [0, 1, 2], "f32", seed=55, scale=400.0,
                                                reduction="sum"),
     "plain_sweep_underflow_redo": _plain_sweep_underflow,
+    "all_negative_logits_bf16": lambda: _all_negative("bf16"),
+    "all_negative_logits_f16": lambda: _all_negative("f16"),
     "ragged_padded_f16": lambda: make_case(5, None, None, 129, [0, 1, 2, 3, 4], "f16", seed=52, Tmax=70, U1max=30,
                                            T_range=(1, 70), U_range=(0, 29), reduction="mean", extra_cols=3),
 }
