@@ -306,8 +306,10 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
   float A = 0.f, m = 0.f, Gb = 0.f, Gy = 0.f;
   int ycol = -1;
   const float* rec = nullptr;
-  if (p.uok[b]) {
-    const int T = (int)p.Tlen[b], U = (int)p.Ulen[b];
+  // the three per-utterance words in one round trip (an ok utterance has valid lengths)
+  const int ok = p.uok[b];
+  const int T = (int)p.Tlen[b], U = (int)p.Ulen[b];
+  if (ok) {
     if (t < T && u <= U) {
       valid = true;
       const int k = t + u;
