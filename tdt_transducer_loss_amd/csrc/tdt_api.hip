@@ -17,7 +17,7 @@ using tdt::Params;
 
 struct Layout {
   int KD, WP, DM, NW, NPR, RS, nseg, nch, gnseg, gnch;
-  int RW, UW;
+  int RW, UW, PR;
   size_t off_pwin, off_pwout, pw_bytes;
   size_t off_rstat, off_part, off_pr, off_wout, off_win, off_ar, off_br, off_rec;
   size_t off_logp, off_logpa, off_wts, off_pm, off_pe, off_uok, off_xflag, off_lpx, off_lcnt;
@@ -85,7 +85,11 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
   L->off_rec = take(NP * (size_t)L->RS * 4);
   // slot-pair-major plain weights for the plain sweeps, addressed with 32-bit byte
   // offsets per utterance (without them the extended-range sweep runs)
-  L->UW = (int)((U1max + 3) & ~(int64_t)3);
+  // labels per lane of the plain sweep that reads the copy (the lattice launcher's choice)
+  L->PR = U1max <= 256 ? (U1max <= 64 ? 1 : U1max <= 128 ? 2 : 4)
+                       : (U1max <= 768 ? 1 : U1max <= 1536 ? 2 : U1max <= 3072 ? 4 : 8);
+  const int64_t uq = L->PR > 4 ? L->PR : 4;  // rows hold whole bands of UW / PR columns
+  L->UW = (int)((U1max + uq - 1) / uq * uq);
   const size_t pw_utt = (size_t)L->KD * (size_t)((L->NW + 1) / 2) * (size_t)L->UW * 16;
   L->pw_bytes = pw_utt <= (size_t)0x7fffffff ? pw_utt * (size_t)B : 0;
   L->off_pwin = take(L->pw_bytes);
@@ -275,6 +279,7 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   p.RW = L.RW;
   p.rec = (float*)(ws + L.off_rec);
   p.UW = L.UW;
+  p.PR = L.PR;
   p.pwin = L.pw_bytes ? (double*)(ws + L.off_pwin) : nullptr;
   p.pwout = L.pw_bytes ? (double*)(ws + L.off_pwout) : nullptr;
   p.logp = (double*)(ws + L.off_logp);

@@ -87,7 +87,10 @@ struct Params {
   float* rec;     // [RS] per-node record of the gradient pass
   double* pwin;   // plain weights of the moves into / out of each node, by slot pair:
   double* pwout;  //   [b][k][slot / 2][u][slot % 2] (NULL when too large)
-  int UW;         // labels per row of pwin / pwout
+  int UW;         // labels per row of pwin / pwout (a multiple of 4 and of PR)
+  int PR;         // labels per lane of the plain sweep reading them: label u is stored at
+                  //   (u % PR) * (UW / PR) + u / PR, so that the lanes of one load read
+                  //   consecutive 16-byte pairs
   // workspace, per utterance
   double* logp;   // log P from beta(0,0)
   double* logpa;  // log P from the alpha terminal (diagnostic)

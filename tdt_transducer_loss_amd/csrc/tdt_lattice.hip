@@ -68,15 +68,18 @@ __device__ __forceinline__ bool wrec_put_weight(char* rec, int NW, int s, Ext w)
 }
 
 // Slot-pair-major copy of the plain float64 weights for the plain sweeps (empty when one
-// utterance's copy would exceed 2 GB): [b][k][slot / 2][u][slot % 2], rows of UW labels,
-// so that one 16-byte load per lane fetches two slots of its label and the lanes of a wave
-// read consecutive bytes.
+// utterance's copy would exceed 2 GB): [b][k][slot / 2][column][slot % 2], rows of UW
+// columns, label u in column (u % PR) * (UW / PR) + u / PR, so that one 16-byte load per
+// lane fetches two slots of one of its R = PR labels and the lanes of a wave read
+// consecutive bytes.
 __host__ __device__ constexpr int slot_pairs(int NW) { return (NW + 1) / 2; }
 
 __device__ __forceinline__ void pw_put(double* pw, const Params& p, int b, int k, int s, int u, Ext w) {
-  if (pw)
-    pw[((((int64_t)b * p.KD + k) * slot_pairs(p.NW) + (s >> 1)) * p.UW + u) * 2 + (s & 1)] =
+  if (pw) {
+    const int col = (u % p.PR) * (p.UW / p.PR) + u / p.PR;  // label u of lane u / PR
+    pw[((((int64_t)b * p.KD + k) * slot_pairs(p.NW) + (s >> 1)) * p.UW + col) * 2 + (s & 1)] =
         w.m == 0.0 ? 0.0 : ldexp(w.m, w.e);
+  }
 }
 
 __device__ __forceinline__ Ext wrec_get(const char* rec, int NW, int s) {
@@ -510,13 +513,13 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, doubl
   auto load_w = [&](int ks, WPlain<DM, R>& w) {
     const int k = ALPHA ? ks : nsteps - 1 - ks;
     constexpr int NW = 2 * DM + 1, NP = slot_pairs(NW);
-    int off = (k * NP * UW + u0) * 16;
+    int off = (k * NP * UW + lane) * 16;  // label u0 + r in column r * (UW / R) + lane
     asm volatile("" : "+v"(off));
 #pragma unroll
     for (int pr = 0; pr < NP; ++pr) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(wr, off + (pr * UW + r) * 16, 0, 0);
+        const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(wr, off + (pr * UW + r * (UW / R)) * 16, 0, 0);
         w.v[2 * pr][r] = __builtin_bit_cast(double, ((uint64_t)x.y << 32) | x.x);
         if (2 * pr + 1 < NW) w.v[2 * pr + 1][r] = __builtin_bit_cast(double, ((uint64_t)x.w << 32) | x.z);
       }
@@ -680,12 +683,12 @@ __device__ bool sweep_fast_mw(const Params& p, int b, int T, int U, int tid, dou
   auto load_w = [&](int ks) {
     const int k = ALPHA ? ks : nsteps - 1 - ks;
     constexpr int NW = 2 * DM + 1, NP = slot_pairs(NW);
-    const int off = (k * NP * UW + u0) * 16;
+    const int off = (k * NP * UW + tid) * 16;  // label u0 + r in column r * (UW / R) + tid
 #pragma unroll
     for (int pr = 0; pr < NP; ++pr) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(wr, off + (pr * UW + r) * 16, 0, 0);
+        const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(wr, off + (pr * UW + r * (UW / R)) * 16, 0, 0);
         w.v[2 * pr][r] = __builtin_bit_cast(double, ((uint64_t)x.y << 32) | x.x);
         if (2 * pr + 1 < NW) w.v[2 * pr + 1][r] = __builtin_bit_cast(double, ((uint64_t)x.w << 32) | x.z);
       }
