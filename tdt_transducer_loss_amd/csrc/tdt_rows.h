@@ -262,6 +262,170 @@ __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
   }
 }
 
+// Row statistics for short segments (at most 4 windows): the same task as
+// k_row_partial, split into its loads (row_task_load) and its reductions
+// (row_task_finish), so that a wave issues the loads of both of its tasks before reducing
+// either.  With longer segments the second task's registers cost more occupancy than the
+// overlap gains (B4 T200 U40 V8193 bf16, 6-window segments: 107 vs 104 us; the ragged fp16
+// batch, 3-window segments: 200 vs 210 us; B2 T1000 U1500 V1025 bf16: 2.17 vs 2.38 ms).
+template <typename TI, int NCH>
+struct RowTask {
+  bool ok;  // a node of its utterance's lattice (wave-uniform)
+  int seg, c0, nwin, nch;
+  uint32_t b, rem;  // utterance and lattice position (anti-diagonal workspace layout)
+  uint4 v[NCH];
+  float xe;
+};
+
+template <typename TI, int NCH>
+__device__ __forceinline__ void row_task_load(const Params& p, uint32_t g, uint32_t total, int lane,
+                                              RowTask<TI, NCH>& tk) {
+  constexpr int EPC = TI::kEpc;
+  using ET = typename TI::T;
+  tk.ok = false;
+  if (g >= total) return;
+  const uint32_t nseg = (uint32_t)p.nseg;
+  const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
+  const uint32_t node = fdiv(g, p.fd_nseg);
+  const int seg = (int)(g - node * nseg);
+  const uint32_t b = fdiv(node, p.fd_tu1);
+  const uint32_t nrem = node - b * per;
+  const int t = (int)fdiv(nrem, p.fd_u1);
+  const int u = (int)(nrem - (uint32_t)t * (uint32_t)p.U1max);
+  const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
+  if (!utt_dims_ok(p, T64, U64)) return;
+  const int T = (int)T64, U = (int)U64;
+  if (t >= T || u > U) return;
+  const int k = t + u;
+  tk.ok = true;
+  tk.seg = seg;
+  tk.b = b;
+  tk.rem = (uint32_t)k * (uint32_t)p.WP + (uint32_t)(u - diag_ulo(k, T));
+  const int V = p.V;
+  const ET* row = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
+  const RowCover rc = row_cover<TI>(row, V);
+  const int nch = rc.nch;
+  const int c0 = seg * 64 * NCH;
+  const int nwin = (nch - c0 + 63) >> 6;
+  tk.nch = nch;
+  tk.c0 = c0;
+  tk.nwin = nwin;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)rc.base, (short)0, nch * 16, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    if (j < nwin) {
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (c0 + lane + 64 * j) * 16, 0, 0);
+      tk.v[j] = make_uint4(x.x, x.y, x.z, x.w);
+    }
+  }
+  const int eh = c0 == 0 ? min(V, EPC - rc.head) : 0;
+  const bool tail_here = nch > 1 && nch - 1 >= c0 && nch - 1 < c0 + 64 * NCH;
+  const int et = tail_here ? V - ((nch - 1) * EPC - rc.head) : 0;
+  tk.xe = -__builtin_inff();
+  if (lane < eh) tk.xe = TI::load(row, lane);
+  else if (lane - eh < et) tk.xe = TI::load(row, V - et + (lane - eh));
+  const int seg_span = 64 * NCH;
+  float4* rs = p.rstat + tk.rem + (int64_t)b * p.KD * p.WP;
+  if (lane == 0) {
+    if ((rc.head + p.blank) / EPC / seg_span == seg) ((float*)rs)[2] = TI::load(row, p.blank);
+    int y = -1;
+    if (u < U) {
+      const int64_t yy = p.labels[(int64_t)b * p.lab_stride + u];
+      if (yy >= 0 && yy < V) y = (int)yy;
+    }
+    if (y >= 0 ? (rc.head + y) / EPC / seg_span == seg : seg == 0)
+      ((float*)rs)[3] = y >= 0 ? TI::load(row, y) : -__builtin_inff();
+  }
+}
+
+template <typename TI, int NCH>
+__device__ __forceinline__ void row_task_finish(const Params& p, int lane, RowTask<TI, NCH>& tk) {
+  constexpr int EPC = TI::kEpc;
+  if (!tk.ok) return;
+  const int c0 = tk.c0, nwin = tk.nwin, nch = tk.nch;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int cw = c0 + 64 * j;
+    if (j < nwin && (cw == 0 || cw + 63 >= nch - 1)) {
+      const int c = cw + lane;
+      if (c == 0 || c >= nch - 1) tk.v[j] = neg_inf_chunk<TI>();
+    }
+  }
+  MaxAcc<TI> mx;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    if (j < nwin) {
+      mx.add(tk.v[j].x);
+      mx.add(tk.v[j].y);
+      mx.add(tk.v[j].z);
+      mx.add(tk.v[j].w);
+    }
+  }
+  const float xe = tk.xe;
+  float mw = wave_max_dpp(fmaxf(mx.value(), xe));
+  if constexpr (__is_same(TI, BF16)) {
+    if (!(mw >= 0.f)) {
+      KeyMaxBF16 km;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        if (j < nwin) {
+          km.add(tk.v[j].x);
+          km.add(tk.v[j].y);
+          km.add(tk.v[j].z);
+          km.add(tk.v[j].w);
+        }
+      }
+      mw = wave_max_dpp(fmaxf(km.value(), xe));
+    }
+  }
+  const float c = EPC == 4 ? mw : mw * kLog2e;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    if (j < nwin) {
+#pragma unroll
+      for (int s = 0; s < EPC; ++s) {
+        const float e2 = __builtin_amdgcn_exp2f(expo<TI>(TI::get(tk.v[j], s), c));
+        if ((s & 3) == 0) a0 += e2;
+        else if ((s & 3) == 1) a1 += e2;
+        else if ((s & 3) == 2) a2 += e2;
+        else a3 += e2;
+      }
+    }
+  }
+  float acc = ((a0 + a1) + (a2 + a3)) + __builtin_amdgcn_exp2f(expo<TI>(xe, c));
+  const bool empty = !(mw > -__builtin_inff());
+  if (empty) acc = 0.f;
+  double S = wave_sum_dpp((double)acc);
+  if (!empty && !(__builtin_fabsf(c) < __builtin_inff())) S = __builtin_nan("");
+  if (lane == 0) {
+    float* part = p.part + ((int64_t)tk.rem + (int64_t)tk.b * p.KD * p.WP) * 2 * p.nseg + 2 * tk.seg;
+    part[0] = empty ? -__builtin_inff() : c;
+    part[1] = (float)S;
+  }
+}
+
+template <typename TI, int NCH>
+__global__ __launch_bounds__(256) void k_row_partial2(const Params p) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (blockIdx.x == 0)  // flags the node-weight kernel and the lattice of this call set
+    for (int i = threadIdx.x; i < p.B; i += blockDim.x) {
+      p.xflag[i] = 0;
+      p.lcnt[i] = 0;
+    }
+  const uint32_t total = (uint32_t)p.B * (uint32_t)p.Tmax * (uint32_t)p.U1max * (uint32_t)p.nseg;
+  const uint32_t stride = gridDim.x * kWavesPerBlock;
+  for (uint32_t g = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv; g < total; g += 2 * stride) {
+    RowTask<TI, NCH> t0, t1;
+    row_task_load<TI, NCH>(p, g, total, lane, t0);
+    row_task_load<TI, NCH>(p, g + stride, total, lane, t1);
+    row_task_finish<TI, NCH>(p, lane, t0);
+    row_task_finish<TI, NCH>(p, lane, t1);
+  }
+}
+
 // Gradient value w O softmax(h)_v of one element from its node's record:
 //   fp32:   A 2^((x - m) log2e),  A = w O 2^-K, m the row maximum;
 //   16-bit: 2^(x log2e - C),      C = c + K - log2|w O| (one fma and one exp2), with the
@@ -435,10 +599,14 @@ hipError_t launch_rows_t(const Params& p, bool aligned, hipStream_t st, int whic
   }
   const dim3 grid((unsigned)blocks);
   if (which == 0) {
+#define TDT_RS2(N) \
+  case N: hipLaunchKernelGGL((k_row_partial2<TI, N>), grid, dim3(256), 0, st, p); break;
 #define TDT_RS(N) \
   case N: hipLaunchKernelGGL((k_row_partial<TI, N>), grid, dim3(256), 0, st, p); break;
-    switch (nch) { TDT_RS(1) TDT_RS(2) TDT_RS(3) TDT_RS(4) TDT_RS(5) TDT_RS(6) TDT_RS(7) default: TDT_RS(8) }
+    // short segments: the two-task form (see k_row_partial2)
+    switch (nch) { TDT_RS2(1) TDT_RS2(2) TDT_RS2(3) TDT_RS2(4) TDT_RS(5) TDT_RS(6) TDT_RS(7) default: TDT_RS(8) }
 #undef TDT_RS
+#undef TDT_RS2
   } else {
 #define TDT_GR(N)                                                                           \
   case N:                                                                                   \
