@@ -989,11 +989,13 @@ __global__ __launch_bounds__(256) void k_coef(const Params p) {
   const int b = (int)(g / per);
   // whole groups leave together below: every condition depends on the position only
   if (b >= p.B) return;
-  if (!p.uok[b]) return;
+  // the three per-utterance words in one round trip (an ok utterance has valid lengths)
+  const int ok = p.uok[b];
+  const int T = (int)p.Tlen[b], U = (int)p.Ulen[b];
+  if (!ok) return;
   const int64_t rem = g - (int64_t)b * per;
   const int k = (int)(rem / p.WP);
   const int i = (int)(rem - (int64_t)k * p.WP);
-  const int T = (int)p.Tlen[b], U = (int)p.Ulen[b];
   if (k >= T + U) return;
   const int u = diag_ulo(k, T) + i;
   if (u > min(k, U)) return;
