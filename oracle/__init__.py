@@ -62,6 +62,16 @@ def _load():
             + [vp] * 6 + [vp] * 8 + [vp, vp] + [vp, i64, vp, vp, ctypes.c_int]
         )
         lib.tdt_oracle_max_threads.restype = ctypes.c_int
+        lib.tdt_oracle_open.restype = ctypes.c_void_p
+        lib.tdt_oracle_open.argtypes = (
+            [ctypes.c_int] + [i64] * 5 + [vp, i64, i64, i64, vp, i64, i64, i64]
+            + [vp, i64, vp, vp, vp, ctypes.c_int32, ctypes.c_double, ctypes.c_int]
+            + [vp, vp, vp, ctypes.c_int]
+        )
+        lib.tdt_oracle_rows.restype = ctypes.c_int
+        lib.tdt_oracle_rows.argtypes = [vp, i64, i64, vp, vp]
+        lib.tdt_oracle_close.restype = None
+        lib.tdt_oracle_close.argtypes = [vp]
         _lib = lib
     return _lib
 
@@ -149,3 +159,69 @@ def run(tok: torch.Tensor, dur: torch.Tensor, labels: torch.Tensor, logit_length
         out["rows_dur"] = out["rows_dur"].reshape(-1, D)
     out["loss"] = float(out["loss"][0])
     return out
+
+
+class Session:
+    """The oracle's lattice, posteriors and losses of one batch, computed once; gradient
+    rows are then produced a range of padded node indices at a time (for batches whose
+    full float64 gradient would not fit in host memory).  Rows are bit-identical to the
+    matching rows of :func:`run`'s ``grad_tok`` / ``grad_dur``.
+
+    Arguments as in :func:`run`.  Use as a context manager; the input tensors are kept
+    alive by the session."""
+
+    def __init__(self, tok, dur, labels, logit_lengths, label_lengths, durations, blank, sigma=0.0,
+                 reduction="mean_volume", threads: int = 0):
+        lib = _load()
+        assert tok.device.type == "cpu" and dur.device.type == "cpu"
+        assert tok.dtype == dur.dtype and tok.dtype in _DTYPES
+        assert tok.dim() == 4 and dur.dim() == 4 and tok.stride(3) == 1 and dur.stride(3) == 1
+        B, Tmax, U1max, V = tok.shape
+        D = dur.shape[3]
+        labels = labels.to(torch.int64).contiguous()
+        if labels.dim() == 1:
+            labels = labels.reshape(B, -1)
+        self._keep = (tok, dur, labels, logit_lengths.to(torch.int64).contiguous(),
+                      label_lengths.to(torch.int64).contiguous(),
+                      np.ascontiguousarray(np.asarray(list(durations), dtype=np.int32)))
+        _, _, labels, Tl, Ul, dd = self._keep
+        assert dd.shape[0] == D
+        self.B, self.Tmax, self.U1max, self.V, self.D = B, Tmax, U1max, V, D
+        self.loss_utt = np.zeros(B)
+        loss = np.zeros(1)
+        self.status = np.zeros(B, dtype=np.int32)
+        self._h = lib.tdt_oracle_open(
+            _DTYPES[tok.dtype], B, Tmax, U1max, V, D,
+            _ptr(tok), tok.stride(0), tok.stride(1), tok.stride(2),
+            _ptr(dur), dur.stride(0), dur.stride(1), dur.stride(2),
+            _ptr(labels), labels.stride(0), _ptr(Tl), _ptr(Ul), _ptr(dd), int(blank), float(sigma),
+            REDUCTIONS[reduction], _ptr(self.loss_utt), _ptr(loss), _ptr(self.status), int(threads))
+        self.loss = float(loss[0])
+
+    @property
+    def nodes(self) -> int:
+        return self.B * self.Tmax * self.U1max
+
+    def rows(self, first: int, count: int, tok: bool = True, dur: bool = True):
+        """Gradient rows of padded node indices [first, first + count): (tok [count, V],
+        dur [count, D]) float64 arrays (None where not asked for)."""
+        rt = np.zeros((count, self.V)) if tok else None
+        rd = np.zeros((count, self.D)) if dur else None
+        rc = _load().tdt_oracle_rows(self._h, int(first), int(count), _ptr(rt), _ptr(rd))
+        if rc != 0:
+            raise IndexError(f"rows [{first}, {first + count}) outside the batch")
+        return rt, rd
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _load().tdt_oracle_close(self._h)
+            self._h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        self.close()

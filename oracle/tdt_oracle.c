@@ -260,23 +260,27 @@ typedef struct {
   double* cdur;   /* [.][D] posterior expected number of moves of duration index i out of n */
 } node_out_t;
 
+/* Posteriors of the moves out of every node of one utterance, indexed by t*(U+1) + u. */
+typedef struct {
+  double* occ;  /* O(n) = exp(alpha(n) + beta(n) - log P) */
+  double* cb;   /* c_blank(n): sum of the posteriors of the blank moves out of n */
+  double* cl;   /* c_label(n): sum of the posteriors of the label moves out of n */
+  double* cdur; /* [.][D] c_dur(n, i): sum of the posteriors of the moves of duration index i */
+} post_t;
+
 /*
- * Steps 7-8: posteriors of the moves out of n and the gradient of loss_b with respect
- * to h(n) and g(n):
- *   d loss / d h(n,v) = O(n) softmax(h(n))_v - [v = blank] c_blank(n) - [v = y_{u+1}] c_label(n)
- *   d loss / d g(n,i) = O(n) softmax(g(n))_i - c_dur(n,i)
- * The node posteriors are written to the per-node outputs; the gradient rows (scaled by
- * the reduction weight wb) are written when gtok / gdur are not NULL.
+ * Step 7: the posterior of a move e out of n is exp(alpha(n) + weight(e) + beta(dest) - log P)
+ * (beta of the terminal = 0); O(n), c_blank(n), c_label(n) and c_dur(n, i) are the sums
+ * named above.
  */
-static void node_posteriors_and_grads(const problem_t* p, int64_t b, const utt_t* w, double logP, double wb,
-                                      const node_out_t* no, double* gtok, double* gdur, const int64_t* rows,
-                                      int64_t nrows, double* rtok, double* rdur) {
-  const int64_t T = w->T, U = w->U, V = p->V, D = p->D;
+static post_t node_posteriors(const problem_t* p, const utt_t* w, double logP) {
+  const int64_t T = w->T, U = w->U, D = p->D;
   const int64_t nn = T * (U + 1);
-  double* cdur_all = (double*)calloc((size_t)(nn * D), sizeof(double));
-  double* cb_all = (double*)calloc((size_t)nn, sizeof(double));
-  double* cl_all = (double*)calloc((size_t)nn, sizeof(double));
-  double* occ_all = (double*)calloc((size_t)nn, sizeof(double));
+  post_t q;
+  q.cdur = (double*)calloc((size_t)(nn * D > 0 ? nn * D : 1), sizeof(double));
+  q.cb = (double*)calloc((size_t)(nn > 0 ? nn : 1), sizeof(double));
+  q.cl = (double*)calloc((size_t)(nn > 0 ? nn : 1), sizeof(double));
+  q.occ = (double*)calloc((size_t)(nn > 0 ? nn : 1), sizeof(double));
 #pragma omp parallel for schedule(static)
   for (int64_t idx = 0; idx < nn; ++idx) {
     int64_t t = idx / (U + 1), u = idx % (U + 1);
@@ -302,12 +306,61 @@ static void node_posteriors_and_grads(const problem_t* p, int64_t b, const utt_t
         cl += g;
         gi += g;
       }
-      cdur_all[idx * D + i] = gi;
+      q.cdur[idx * D + i] = gi;
     }
-    cb_all[idx] = cb;
-    cl_all[idx] = cl;
-    occ_all[idx] = exp(a + w->beta[idx] - logP);
+    q.cb[idx] = cb;
+    q.cl[idx] = cl;
+    q.occ[idx] = exp(a + w->beta[idx] - logP);
   }
+  return q;
+}
+
+static void free_posteriors(post_t* q) {
+  free(q->cdur);
+  free(q->cb);
+  free(q->cl);
+  free(q->occ);
+}
+
+/*
+ * Step 8 and the reduction weight, for one node (t, u) of utterance b:
+ *   orow_t[v] = wb * (O(n) softmax(h(n))_v - [v = blank] c_blank(n) - [v = y_{u+1}] c_label(n))
+ *   orow_d[i] = wb * (O(n) softmax(g(n))_i - c_dur(n, i))
+ * Either output may be NULL.
+ */
+static void gradient_row(const problem_t* p, int64_t b, const utt_t* w, const post_t* q, int64_t t, int64_t u,
+                         double wb, double* orow_t, double* orow_d) {
+  const int64_t U = w->U, V = p->V, D = p->D;
+  int64_t idx = t * (U + 1) + u;
+  double O = q->occ[idx];
+  const int64_t base = b * p->ts0 + t * p->ts1 + u * p->ts2;
+  if (orow_t) {
+    double lh = w->lse_h[idx];
+    for (int64_t v = 0; v < V; ++v) {
+      double hv = load_elem(p->dtype, p->tok, base + v);
+      orow_t[v] = O * exp(hv - lh);
+    }
+    orow_t[p->blank] -= q->cb[idx];
+    if (u < U) orow_t[p->labels[b * p->lab_stride + u]] -= q->cl[idx];
+    for (int64_t v = 0; v < V; ++v) orow_t[v] *= wb;
+  }
+  if (orow_d) {
+    for (int64_t i = 0; i < D; ++i) orow_d[i] = wb * (O * exp(w->lam[idx * D + i]) - q->cdur[idx * D + i]);
+  }
+}
+
+/*
+ * Steps 7-8 for utterance b: the node posteriors go to the per-node outputs; the gradient
+ * rows (scaled by the reduction weight wb) go to the full gradient when gtok / gdur are
+ * not NULL, and to rtok / rdur for the selected padded node indices `rows` of this
+ * utterance.
+ */
+static void node_posteriors_and_grads(const problem_t* p, int64_t b, const utt_t* w, double logP, double wb,
+                                      const node_out_t* no, double* gtok, double* gdur, const int64_t* rows,
+                                      int64_t nrows, double* rtok, double* rdur) {
+  const int64_t T = w->T, U = w->U, V = p->V, D = p->D;
+  const int64_t nn = T * (U + 1);
+  post_t q = node_posteriors(p, w, logP);
   if (no) {
     for (int64_t idx = 0; idx < nn; ++idx) {
       int64_t t = idx / (U + 1), u = idx % (U + 1);
@@ -316,61 +369,73 @@ static void node_posteriors_and_grads(const problem_t* p, int64_t b, const utt_t
       if (no->lse_g) no->lse_g[n] = w->lse_g[idx];
       if (no->alpha) no->alpha[n] = w->alpha[idx];
       if (no->beta) no->beta[n] = w->beta[idx];
-      if (no->occ) no->occ[n] = occ_all[idx];
-      if (no->cblank) no->cblank[n] = cb_all[idx];
-      if (no->clabel) no->clabel[n] = cl_all[idx];
+      if (no->occ) no->occ[n] = q.occ[idx];
+      if (no->cblank) no->cblank[n] = q.cb[idx];
+      if (no->clabel) no->clabel[n] = q.cl[idx];
       if (no->cdur)
-        for (int64_t i = 0; i < D; ++i) no->cdur[n * D + i] = cdur_all[idx * D + i];
+        for (int64_t i = 0; i < D; ++i) no->cdur[n * D + i] = q.cdur[idx * D + i];
     }
   }
   /* gradient rows: full tensor and/or a list of selected nodes of this utterance */
   const int64_t per_b = p->Tmax * p->U1max;
-  for (int pass = 0; pass < 2; ++pass) {
-    if (pass == 0 && !gtok && !gdur) continue;
-    if (pass == 1 && !rows) continue;
-    int64_t count = pass == 0 ? nn : nrows;
+  if (gtok || gdur) {
 #pragma omp parallel for schedule(dynamic, 16)
-    for (int64_t j = 0; j < count; ++j) {
-      int64_t t, u;
-      double *orow_t, *orow_d;
-      if (pass == 0) {
-        t = j / (U + 1);
-        u = j % (U + 1);
-        int64_t n = node_index(p, b, t, u);
-        orow_t = gtok ? gtok + n * V : NULL;
-        orow_d = gdur ? gdur + n * D : NULL;
-      } else {
-        int64_t n = rows[j];
-        if (n / per_b != b) continue;
-        t = (n / p->U1max) % p->Tmax;
-        u = n % p->U1max;
-        if (t >= T || u > U) continue; /* padding: the caller zero-filled it */
-        orow_t = rtok ? rtok + j * V : NULL;
-        orow_d = rdur ? rdur + j * D : NULL;
-      }
-      int64_t idx = t * (U + 1) + u;
-      double O = occ_all[idx];
-      const int64_t base = b * p->ts0 + t * p->ts1 + u * p->ts2;
-      if (orow_t) {
-        double lh = w->lse_h[idx];
-        for (int64_t v = 0; v < V; ++v) {
-          double hv = load_elem(p->dtype, p->tok, base + v);
-          orow_t[v] = O * exp(hv - lh);
-        }
-        orow_t[p->blank] -= cb_all[idx];
-        if (u < U) orow_t[p->labels[b * p->lab_stride + u]] -= cl_all[idx];
-        for (int64_t v = 0; v < V; ++v) orow_t[v] *= wb;
-      }
-      if (orow_d) {
-        for (int64_t i = 0; i < D; ++i)
-          orow_d[i] = wb * (O * exp(w->lam[idx * D + i]) - cdur_all[idx * D + i]);
-      }
+    for (int64_t j = 0; j < nn; ++j) {
+      int64_t t = j / (U + 1), u = j % (U + 1);
+      int64_t n = node_index(p, b, t, u);
+      gradient_row(p, b, w, &q, t, u, wb, gtok ? gtok + n * V : NULL, gdur ? gdur + n * D : NULL);
     }
   }
-  free(cdur_all);
-  free(cb_all);
-  free(cl_all);
-  free(occ_all);
+  if (rows) {
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t j = 0; j < nrows; ++j) {
+      int64_t n = rows[j];
+      if (n / per_b != b) continue;
+      int64_t t = (n / p->U1max) % p->Tmax;
+      int64_t u = n % p->U1max;
+      if (t >= T || u > U) continue; /* padding: the caller zero-filled it */
+      gradient_row(p, b, w, &q, t, u, wb, rtok ? rtok + j * V : NULL, rdur ? rdur + j * D : NULL);
+    }
+  }
+  free_posteriors(&q);
+}
+
+/* Step 9, reduction weights: none / sum -> 1, mean_batch -> 1/B,
+ * mean -> 1/(B max(U_b,1)), mean_volume -> 1/max(sum_b U_b, 1). */
+static void reduction_weights(int64_t B, const int64_t* Ulen, int reduction, double* wts) {
+  int64_t sumU = 0;
+  for (int64_t b = 0; b < B; ++b) sumU += Ulen[b];
+  for (int64_t b = 0; b < B; ++b) {
+    double wb = 1.0;
+    if (reduction == RED_MEAN_BATCH) wb = 1.0 / (double)B;
+    if (reduction == RED_MEAN) wb = 1.0 / ((double)B * (double)(Ulen[b] > 1 ? Ulen[b] : 1));
+    if (reduction == RED_MEAN_VOLUME) wb = 1.0 / (double)(sumU > 1 ? sumU : 1);
+    wts[b] = wb;
+  }
+}
+
+static void utt_alloc(utt_t* w, int64_t T, int64_t U, int64_t D) {
+  w->T = T;
+  w->U = U;
+  int64_t nn = T * (U + 1);
+  size_t sz = (size_t)(nn > 0 ? nn : 1);
+  w->lse_h = (double*)malloc(sizeof(double) * sz);
+  w->lse_g = (double*)malloc(sizeof(double) * sz);
+  w->lp_blank = (double*)malloc(sizeof(double) * sz);
+  w->lp_label = (double*)malloc(sizeof(double) * sz);
+  w->lam = (double*)malloc(sizeof(double) * sz * (size_t)D);
+  w->alpha = (double*)malloc(sizeof(double) * sz);
+  w->beta = (double*)malloc(sizeof(double) * sz);
+}
+
+static void utt_free(utt_t* w) {
+  free(w->lse_h);
+  free(w->lse_g);
+  free(w->lp_blank);
+  free(w->lp_label);
+  free(w->lam);
+  free(w->alpha);
+  free(w->beta);
 }
 
 /*
@@ -425,18 +490,7 @@ int tdt_oracle_run(int dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V,
   double* per = (double*)malloc(sizeof(double) * (size_t)(B > 0 ? B : 1));
   int* st = (int*)calloc((size_t)(B > 0 ? B : 1), sizeof(int));
   double* wts = (double*)malloc(sizeof(double) * (size_t)(B > 0 ? B : 1));
-
-  /* Step 9, reduction weights: none / sum -> 1, mean_batch -> 1/B,
-   * mean -> 1/(B max(U_b,1)), mean_volume -> 1/max(sum_b U_b, 1). */
-  int64_t sumU = 0;
-  for (int64_t b = 0; b < B; ++b) sumU += Ulen[b];
-  for (int64_t b = 0; b < B; ++b) {
-    double wb = 1.0;
-    if (reduction == RED_MEAN_BATCH) wb = 1.0 / (double)B;
-    if (reduction == RED_MEAN) wb = 1.0 / ((double)B * (double)(Ulen[b] > 1 ? Ulen[b] : 1));
-    if (reduction == RED_MEAN_VOLUME) wb = 1.0 / (double)(sumU > 1 ? sumU : 1);
-    wts[b] = wb;
-  }
+  reduction_weights(B, Ulen, reduction, wts);
 
   for (int64_t b = 0; b < B; ++b) {
     st[b] = utterance_status(&p, b);
@@ -447,17 +501,8 @@ int tdt_oracle_run(int dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V,
       continue;
     }
     utt_t w;
-    w.T = Tlen[b];
-    w.U = Ulen[b];
+    utt_alloc(&w, Tlen[b], Ulen[b], D);
     int64_t nn = w.T * (w.U + 1);
-    size_t sz = (size_t)(nn > 0 ? nn : 1);
-    w.lse_h = (double*)malloc(sizeof(double) * sz);
-    w.lse_g = (double*)malloc(sizeof(double) * sz);
-    w.lp_blank = (double*)malloc(sizeof(double) * sz);
-    w.lp_label = (double*)malloc(sizeof(double) * sz);
-    w.lam = (double*)malloc(sizeof(double) * sz * (size_t)D);
-    w.alpha = (double*)malloc(sizeof(double) * sz);
-    w.beta = (double*)malloc(sizeof(double) * sz);
     node_log_probs(&p, b, &w);
     forward_alpha(&p, &w);
     backward_beta(&p, &w);
@@ -482,13 +527,7 @@ int tdt_oracle_run(int dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V,
     } else {
       node_posteriors_and_grads(&p, b, &w, logP, wts[b], &no, gtok, gdur, rows, nrows, rtok, rdur);
     }
-    free(w.lse_h);
-    free(w.lse_g);
-    free(w.lp_blank);
-    free(w.lp_label);
-    free(w.lam);
-    free(w.alpha);
-    free(w.beta);
+    utt_free(&w);
   }
 
   double red = 0.0;
@@ -503,6 +542,121 @@ int tdt_oracle_run(int dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V,
   free(st);
   free(wts);
   return 0;
+}
+
+/*
+ * Session form of the same computation, for batches whose full float64 gradient does not
+ * fit in host memory: tdt_oracle_open runs steps 1-7 and 9 for every utterance and keeps
+ * their per-node results; tdt_oracle_rows then writes the gradient rows (step 8) of a
+ * range of padded node indices (b*Tmax + t)*U1max + u, zeros at padded nodes and for
+ * utterances with a data error or no alignment, exactly as tdt_oracle_run writes them.
+ * The logits, labels, lengths and durations passed to tdt_oracle_open must stay alive and
+ * unchanged until tdt_oracle_close.
+ */
+typedef struct {
+  problem_t p;
+  int64_t B;
+  int* st;
+  double* wts;
+  double* per;
+  utt_t* w;    /* [B]; only for utterances with st == 0 and a finite log P */
+  post_t* q;   /* [B] */
+  int* live;   /* [B]: 1 when w[b] and q[b] hold results */
+} session_t;
+
+void* tdt_oracle_open(int dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V, int64_t D, const void* tok,
+                      int64_t ts0, int64_t ts1, int64_t ts2, const void* dur, int64_t ds0, int64_t ds1, int64_t ds2,
+                      const int64_t* labels, int64_t lab_stride, const int64_t* Tlen, const int64_t* Ulen,
+                      const int32_t* durations, int32_t blank, double sigma, int reduction, double* loss_utt,
+                      double* loss_red, int32_t* status, int threads) {
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+  session_t* s = (session_t*)calloc(1, sizeof(session_t));
+  problem_t p = {dtype, B,   Tmax, U1max,      V,    D,    tok,        ts0,   ts1, ts2,
+                 dur,   ds0, ds1,  ds2,        labels, lab_stride, Tlen, Ulen, durations, blank, sigma};
+  s->p = p;
+  s->B = B;
+  size_t nb = (size_t)(B > 0 ? B : 1);
+  s->st = (int*)calloc(nb, sizeof(int));
+  s->wts = (double*)malloc(sizeof(double) * nb);
+  s->per = (double*)malloc(sizeof(double) * nb);
+  s->w = (utt_t*)calloc(nb, sizeof(utt_t));
+  s->q = (post_t*)calloc(nb, sizeof(post_t));
+  s->live = (int*)calloc(nb, sizeof(int));
+  reduction_weights(B, Ulen, reduction, s->wts);
+  for (int64_t b = 0; b < B; ++b) {
+    s->st[b] = utterance_status(&s->p, b);
+    if (s->st[b]) {
+      s->per[b] = NAN;
+      continue;
+    }
+    utt_t* w = &s->w[b];
+    utt_alloc(w, Tlen[b], Ulen[b], D);
+    node_log_probs(&s->p, b, w);
+    forward_alpha(&s->p, w);
+    backward_beta(&s->p, w);
+    double logP = w->logp_beta;
+    s->per[b] = -logP;
+    if (logP == -INFINITY) {
+      s->st[b] |= ST_INFEASIBLE;
+      utt_free(w);
+      continue;
+    }
+    s->q[b] = node_posteriors(&s->p, w, logP);
+    s->live[b] = 1;
+  }
+  double red = 0.0;
+  for (int64_t b = 0; b < B; ++b) red += (reduction == RED_NONE ? 1.0 : s->wts[b]) * s->per[b];
+  if (loss_red) loss_red[0] = red;
+  for (int64_t b = 0; b < B; ++b) {
+    if (loss_utt) loss_utt[b] = s->per[b];
+    if (status) status[b] = s->st[b];
+  }
+  return s;
+}
+
+/* Gradient rows of the padded node indices [first, first + count) into rtok [count][V]
+ * and rdur [count][D] (either may be NULL).  Returns 0, or -1 for a range outside the batch. */
+int tdt_oracle_rows(void* handle, int64_t first, int64_t count, double* rtok, double* rdur) {
+  session_t* s = (session_t*)handle;
+  const problem_t* p = &s->p;
+  const int64_t per_b = p->Tmax * p->U1max;
+  if (first < 0 || count < 0 || first + count > s->B * per_b) return -1;
+  if (rtok) memset(rtok, 0, sizeof(double) * (size_t)(count * p->V));
+  if (rdur) memset(rdur, 0, sizeof(double) * (size_t)(count * p->D));
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t j = 0; j < count; ++j) {
+    int64_t n = first + j;
+    int64_t b = n / per_b;
+    if (!s->live[b]) continue;
+    int64_t t = (n / p->U1max) % p->Tmax;
+    int64_t u = n % p->U1max;
+    if (t >= s->w[b].T || u > s->w[b].U) continue;
+    gradient_row(p, b, &s->w[b], &s->q[b], t, u, s->wts[b], rtok ? rtok + j * p->V : NULL,
+                 rdur ? rdur + j * p->D : NULL);
+  }
+  return 0;
+}
+
+void tdt_oracle_close(void* handle) {
+  session_t* s = (session_t*)handle;
+  if (!s) return;
+  for (int64_t b = 0; b < s->B; ++b) {
+    if (s->live[b]) {
+      utt_free(&s->w[b]);
+      free_posteriors(&s->q[b]);
+    }
+  }
+  free(s->st);
+  free(s->wts);
+  free(s->per);
+  free(s->w);
+  free(s->q);
+  free(s->live);
+  free(s);
 }
 
 /* Number of OpenMP threads a parallel region of this library uses. */
