@@ -8,10 +8,10 @@
  * alpha/beta passes over the lattice with no limit of 1024 labels, one fused gradient
  * pass for token and duration logits, fp32/fp16/bf16 logits read in place (slices of
  * the joint output such as logits[..., :V] are not copied), and the reductions
- * mean_volume, mean_batch, mean, sum and none.  Labels use -100 padding (page
- * "Add TDT loss kernel", huggingface/transformers PR #46048, commit summary "Use -100
- * label padding for training").  sigma is the logit under-normalisation of that page's
- * review thread ("Should we also test for sigma != 0?").
+ * mean_volume, mean_batch, mean, sum and none.  Labels are padded with -100 (page
+ * "Add TDT loss kernel", huggingface/transformers PR #46048, commit summary on label
+ * padding).  sigma is the logit under-normalisation discussed in that page's review
+ * thread on sigma.
  *
  * Definitions, for utterance b with T = logit_lengths[b] frames, U = label_lengths[b]
  * labels y_1..y_U and lattice nodes n = (t, u), 0 <= t < T, 0 <= u <= U:

@@ -113,15 +113,21 @@ __device__ __forceinline__ Ext ext_zero() { return Ext{0.0, kEZ}; }
 __device__ __forceinline__ Ext ext_one() { return Ext{0.5, 1}; }
 __device__ __forceinline__ Ext ext_mul(Ext a, Ext b) { return Ext{a.m * b.m, a.e + b.e}; }
 
-// Normalise a sum s * 2^E to a mantissa in [0.5, 1).
+// Normalise a sum s * 2^E to a mantissa in [0.5, 1).  Results below 2^-(2^27) are
+// zero (as in ext_exp), so exponent sums of a sweep stay far inside the int range.
 __device__ __forceinline__ Ext ext_norm(double s, int E) {
   if (s == 0.0) return ext_zero();
   int ex;
   double m = frexp(s, &ex);  // v_frexp_mant_f64 / v_frexp_exp_i32_f64
-  return Ext{m, E + ex};
+  return E + ex < -(1 << 27) ? ext_zero() : Ext{m, E + ex};
 }
 
-// exp(x) in extended range, accurate to a few ulp of float64.
+// exp(x) in extended range, accurate to a few ulp of float64.  The argument reduction
+// x = k ln2 + r splits ln2 into a high part with trailing zero bits and a low part
+// (Cody and Waite, "Software Manual for the Elementary Functions", 1980), so k ln2 is
+// exact for the k that occur.  Values below 2^-(2^27) (x below about -9.3e7, e.g. a
+// logit masked with -1e10) are taken as zero: their exponent would not fit the int
+// exponent arithmetic of the sweeps.
 __device__ __forceinline__ Ext ext_exp(double x) {
   if (!(x > -1.0e300)) {  // -inf (or a huge negative value): zero; NaN propagates below
     if (x != x) return Ext{x, 0};
@@ -129,6 +135,7 @@ __device__ __forceinline__ Ext ext_exp(double x) {
   }
   double kf = floor(x * kLog2eD);
   if (kf > 1.0e9) return Ext{__builtin_inf(), 0};
+  if (kf < -(double)(1 << 27)) return ext_zero();
   int k = (int)kf;
   double r = fma(-kf, kLn2Hi, x);
   r = fma(-kf, kLn2Lo, r);

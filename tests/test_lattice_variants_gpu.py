@@ -1,0 +1,48 @@
+"""GPU parity of every lattice kernel variant against the float64 oracle.
+
+The lattice launcher picks a kernel by the largest duration value (templates for
+durations up to 4, 8 and 16) and by the padded label count U1_max = U + 1 (labels per
+lane and work-group shape).  This matrix gives each (duration bound, label band) pair a
+small case whose loss and every gradient element are compared with the oracle, plus a
+case per band whose logits (standard deviation 400) put the move weights far below
+2^-300, which forces the extended-range sweep.  Frames are few (24-40) so that the oracle
+and the GPU run in well under a second per case; durations include 0 so that utterances
+with more labels than frames have alignments.
+"""
+import pytest
+
+from parity_util import check_grads, check_loss, gpu_run, oracle_run
+from tdt_inputs import make_case
+
+pytestmark = pytest.mark.gpu
+
+# duration sets by their largest value (the kernel template bound)
+DURATIONS = {4: [0, 1, 2, 3, 4], 8: [0, 1, 3, 8], 16: [0, 1, 2, 7, 16]}
+# one label count per band of the launcher: U1_max <= 64, 128, 256, 768, 1536, 3072, 8192
+LABELS = [50, 100, 220, 500, 1200, 2500, 5000]
+
+
+def _case(dm, U, dtype, scale=1.0, seed=0):
+    T = 24 + (U % 17)
+    return make_case(1, [T], [U], 13, DURATIONS[dm], dtype, scale=scale, sigma=0.05, reduction="sum",
+                     seed=seed, name=f"dm{dm}_U{U}_{dtype}_s{scale:g}")
+
+
+def _parity(case):
+    loss, gt, gd, st = gpu_run(case)
+    orc = oracle_run(case.to("cpu"))
+    check_loss(loss, orc, case.reduction, case.joint.dtype)
+    check_grads(gt, gd, orc, case.joint.dtype)
+    assert int(st.cpu()[0]) == int(orc["status"][0]) == 0
+
+
+@pytest.mark.parametrize("U", LABELS)
+@pytest.mark.parametrize("dm", sorted(DURATIONS))
+def test_lattice_variant(dm, U):
+    dtype = "f32" if (LABELS.index(U) + dm) % 2 == 0 else "bf16"
+    _parity(_case(dm, U, dtype, seed=100 + U + dm).to("cuda"))
+
+
+@pytest.mark.parametrize("U", LABELS)
+def test_lattice_variant_extended_range(U):
+    _parity(_case(4 if U % 2 == 0 else 8, U, "f32", scale=400.0, seed=200 + U).to("cuda"))

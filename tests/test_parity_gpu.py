@@ -31,34 +31,44 @@ def test_config_full_parity(cfg):
     _full_parity(case)
 
 
-def test_long_label_config_sampled():
-    """Workload 4 (B=2, T=1000, U=1500, V=1025, durations 0..8, bf16): full loss, and the
-    gradient rows of 1500 sampled nodes plus every corner node, against the oracle."""
+def test_long_label_config_full():
+    """Workload 4 (B=2, T=1000, U=1500, V=1025, durations 0..8, bf16, sum): the loss, and
+    every one of the 3,002,000 token and duration gradient rows against the oracle, read
+    from an oracle session one range of rows at a time (the full float64 gradient would
+    take about 25 GB of host memory)."""
+    import oracle
+
     case = config_case(4, device="cuda")
     loss, gt, gd, st = gpu_run(case)
     cpu = case.to("cpu")
-    B, Tm, U1 = case.joint.shape[:3]
-    rng = np.random.default_rng(4)
-    rows = set(int(x) for x in rng.integers(0, B * Tm * U1, 1500))
-    for b in range(B):
-        for t in (0, 1, Tm - 2, Tm - 1):
-            for u in (0, 1, U1 - 2, U1 - 1):
-                rows.add((b * Tm + t) * U1 + u)
-    rows = np.array(sorted(rows), dtype=np.int64)
-    say(f"    oracle on {len(rows)} sampled rows")
-    orc = oracle_run(cpu, grads=False, rows=rows)
-    check_loss(loss, orc, case.reduction, case.joint.dtype)
-    idx = torch.from_numpy(rows).to("cuda")
-    g_rows = gt.reshape(-1, case.V).index_select(0, idx).double().cpu().numpy()
-    gd_rows = gd.reshape(-1, case.D).index_select(0, idx).double().cpu().numpy()
     _, tg = TOL[case.joint.dtype]
-    e1 = float(np.abs(g_rows - orc["rows_tok"]).max())
-    e2 = float(np.abs(gd_rows - orc["rows_dur"]).max())
-    say(f"    sampled grad max-abs: token {e1:.3e} duration {e2:.3e}")
+    V, D = case.V, case.D
+    say("    oracle session (lattice and posteriors of both utterances)")
+    with oracle.Session(cpu.tok, cpu.dur, cpu.labels, cpu.logit_lengths, cpu.label_lengths, cpu.durations,
+                        cpu.blank, cpu.sigma, cpu.reduction) as s:
+        check_loss(loss, {"loss": s.loss, "loss_utt": s.loss_utt}, case.reduction, case.joint.dtype)
+        np.testing.assert_array_equal(st.cpu().numpy(), s.status)
+        gt2 = gt.reshape(-1, V)
+        gd2 = gd.reshape(-1, D)
+        e1 = e2 = zs = 0.0
+        chunk = 1 << 15
+        for first in range(0, s.nodes, chunk):
+            n = min(chunk, s.nodes - first)
+            rt, rd = s.rows(first, n)
+            g = gt2[first:first + n].cpu().double()
+            e1 = max(e1, float((g - torch.from_numpy(rt)).abs().max()))
+            e2 = max(e2, float((gd2[first:first + n].cpu().double() - torch.from_numpy(rd)).abs().max()))
+            # zero-sum rows: the exact row sums to 0; each stored element is the
+            # round-to-nearest-even bf16 value (8 significant bits: off by at most 2^-8 of
+            # its magnitude) of a float32 result whose own relative error is below 2^-20,
+            # so |sum_v g_v| <= (2^-8 + 2^-20) sum_v |g_v| (+ a subnormal allowance)
+            excess = (g.sum(-1).abs() - (2.0 ** -8 + 2.0 ** -20) * g.abs().sum(-1) - 1e-30).max()
+            zs = max(zs, float(excess))
+            if first % (chunk * 16) == 0:
+                say(f"    rows {first}..{first + n}: token {e1:.3e} duration {e2:.3e}")
+    say(f"    full grad max-abs: token {e1:.3e}  duration {e2:.3e}  (tol {tg:g}); zero-sum excess {zs:.3e}")
     assert e1 <= tg and e2 <= tg
-    # zero-sum rows hold at any size
-    zs = gt.reshape(-1, case.V).index_select(0, idx).double().sum(-1).abs().max().item()
-    assert zs <= 0.05
+    assert zs <= 0.0
 
 
 def _plain_sweep_underflow():
@@ -77,6 +87,27 @@ def _all_negative(dtype):
     # bf16 row maximum of every segment comes from the order-preserving key pass
     case = make_case(2, [9, 7], [3, 4], 3000, [0, 1, 2, 4], dtype, seed=58, scale=2.0, reduction="none")
     case.joint[..., :3000] -= 60.0
+    return case
+
+
+def _masked(dtype):
+    # logits masked with -1e10 (a common way to forbid a token or a duration): the blank
+    # logit of some nodes, a duration logit of others, and both at a few; the move weights
+    # there are exactly zero (log-weight far below the extended range) and the gradients
+    # must stay finite and match the oracle, which works in the log domain
+    case = make_case(2, [30, 22], [9, 6], 33, [0, 1, 2, 3, 4], dtype, seed=59, sigma=0.05, reduction="none")
+    V = case.V
+    g = torch.Generator().manual_seed(5)
+    for b in range(case.B):
+        T, U = int(case.logit_lengths[b]), int(case.label_lengths[b])
+        for _ in range(12):
+            t = int(torch.randint(1, T - 1, (1,), generator=g))
+            u = int(torch.randint(0, U + 1, (1,), generator=g))
+            what = int(torch.randint(0, 3, (1,), generator=g))
+            if what in (0, 2):
+                case.joint[b, t, u, case.blank] = -1e10
+            if what in (1, 2):
+                case.joint[b, t, u, V + int(torch.randint(0, case.D, (1,), generator=g))] = -1e10
     return case
 
 
@@ -115,6 +146,8 @@ EDGE = {
     "all_negative_logits_f16": lambda: _all_negative("f16"),
     "ragged_padded_f16": lambda: make_case(5, None, None, 129, [0, 1, 2, 3, 4], "f16", seed=52, Tmax=70, U1max=30,
                                            T_range=(1, 70), U_range=(0, 29), reduction="mean", extra_cols=3),
+    "masked_minus_1e10_f32": lambda: _masked("f32"),
+    "masked_minus_1e10_bf16": lambda: _masked("bf16"),
 }
 
 
@@ -151,10 +184,16 @@ def test_infeasible_and_data_errors():
         assert gt[b].abs().max().item() == 0 and gd[b].abs().max().item() == 0
 
 
-def test_forward_only_matches():
-    case = config_case(0, device="cuda")
-    loss_f, g, gd, _ = gpu_run(case, compute_grad=False)
+@pytest.mark.parametrize("cfg", [0, 3])
+def test_forward_only_matches(cfg):
+    """The forward-only call (no gradient pointers) gives the loss of the fused call bit
+    for bit, and the oracle's loss within the tolerance."""
+    case = config_case(cfg, device="cuda")
+    loss_f, g, gd, st = gpu_run(case, compute_grad=False)
     assert g is None and gd is None
+    orc = oracle_run(case.to("cpu"), grads=False)
+    check_loss(loss_f, orc, case.reduction, case.joint.dtype)
+    np.testing.assert_array_equal(st.cpu().numpy(), orc["status"])
     loss_b, _, _, _ = gpu_run(case)
     assert torch.equal(loss_f, loss_b)
 
