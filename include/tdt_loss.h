@@ -195,6 +195,29 @@ int tdt_loss_backward(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, i
                       const int64_t* grad_strides, void* grad_dur_logits, const int64_t* grad_dur_strides,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): tdt_loss_fwd_bwd without the
+ * workspace arguments.  The workspace is a library-owned device array of
+ * TDT_NOALLOC_SCRATCH_BYTES on each GPU the library runs on (held until the process
+ * ends); this call allocates nothing and frees nothing.  Arguments, launch sequence,
+ * results and return codes are those of tdt_loss_fwd_bwd (the same kernels), except that
+ * sizes whose tdt_loss_workspace_size() exceeds TDT_NOALLOC_SCRATCH_BYTES return
+ * TDT_ERR_WORKSPACE_TOO_SMALL before anything is launched, and a failure to obtain the
+ * array's device address returns TDT_ERR_HIP.  The array of a GPU is found from
+ * `stream`'s device (the current device for the NULL stream).  Every call on one GPU
+ * shares that GPU's array and overwrites its contents: calls that may overlap in time on
+ * one GPU (other streams, other threads) race and must not be issued.
+ */
+#define TDT_NOALLOC_SCRATCH_BYTES (64u << 20)
+int tdt_loss_fwd_bwd_noalloc(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,
+                             const void* logits, const int64_t* logits_strides, const void* dur_logits,
+                             const int64_t* dur_strides, int32_t num_durations, const int64_t* labels,
+                             int64_t labels_stride, const int64_t* logit_lengths, const int64_t* label_lengths,
+                             const int32_t* durations, int32_t blank, double sigma, int32_t reduction,
+                             float* loss_out, void* grad_logits, const int64_t* grad_strides, void* grad_dur_logits,
+                             const int64_t* grad_dur_strides, int32_t* utt_status, void* stream);
+
 /* Static string naming a return code. */
 const char* tdt_loss_status_string(int status);
 

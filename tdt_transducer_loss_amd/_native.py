@@ -20,6 +20,8 @@ UTT_BAD_LABEL_LENGTH = 2
 UTT_BAD_LABEL = 4
 UTT_INFEASIBLE = 8
 
+NOALLOC_SCRATCH_BYTES = 64 << 20  # TDT_NOALLOC_SCRATCH_BYTES of include/tdt_loss.h
+
 # Every function the header declares, with its ctypes signature.
 _i32, _i64, _vp, _f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
 _i64p = ctypes.POINTER(ctypes.c_int64)
@@ -49,6 +51,15 @@ SIGNATURES = {
         _vp,                                # grad_loss
         _vp, _i64p, _vp, _i64p,             # grad_logits, strides, grad_dur_logits, strides
         _vp, ctypes.c_size_t, _vp,          # workspace, workspace_bytes, stream
+    ]),
+    "tdt_loss_fwd_bwd_noalloc": (ctypes.c_int, [
+        _i32, _i64, _i64, _i64, _i64,       # dtype, B, T_max, U1_max, V
+        _vp, _i64p, _vp, _i64p, _i32,       # logits, strides, dur_logits, strides, num_durations
+        _vp, _i64, _vp, _vp,                # labels, labels_stride, logit_lengths, label_lengths
+        _i32p, _i32, _f64, _i32,            # durations (host), blank, sigma, reduction
+        _vp,                                # loss_out
+        _vp, _i64p, _vp, _i64p,             # grad_logits, strides, grad_dur_logits, strides
+        _vp, _vp,                           # utt_status, stream
     ]),
     "tdt_loss_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tdt_loss_abi_version": (ctypes.c_int, []),
@@ -133,4 +144,19 @@ def backward_raw(dtype, B, T_max, U1_max, V, logits, lstr, dur, dstr, D, labels,
         grad_loss,
         glog, i64_array(gstr) if gstr is not None else None, gdur, i64_array(gdstr) if gdstr is not None else None,
         ws, ctypes.c_size_t(int(ws_bytes)), stream,
+    )
+
+
+def fwd_bwd_noalloc_raw(dtype, B, T_max, U1_max, V, logits, lstr, dur, dstr, D, labels, lab_stride, tlen, ulen,
+                        durations, blank, sigma, reduction, loss, glog, gstr, gdur, gdstr, status, stream) -> int:
+    """Direct call of tdt_loss_fwd_bwd_noalloc (no workspace arguments) with raw integers
+    / pointers (None for NULL)."""
+    return lib().tdt_loss_fwd_bwd_noalloc(
+        int(dtype), int(B), int(T_max), int(U1_max), int(V),
+        logits, i64_array(lstr), dur, i64_array(dstr), int(D),
+        labels, int(lab_stride), tlen, ulen,
+        i32_array(durations), int(blank), float(sigma), int(reduction),
+        loss,
+        glog, i64_array(gstr) if gstr is not None else None, gdur, i64_array(gdstr) if gdstr is not None else None,
+        status, stream,
     )

@@ -6,6 +6,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "tdt_kernels.h"
 #include "tdt_loss.h"
@@ -402,4 +403,74 @@ extern "C" int tdt_loss_backward(int32_t dtype, int64_t B, int64_t T_max, int64_
   if (tdt::launch_lattice_side(p, 2, st) != hipSuccess) return TDT_ERR_HIP;
   if (launch_rows(p, aligned, st, 1) != hipSuccess) return TDT_ERR_HIP;
   return TDT_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// Allocation-free entry point.  The workspace lives in a file-scope device array (one
+// copy per GPU, held until the process ends).  In host code `scratch` names a host-side
+// stand-in, never a device address: the address of each GPU's copy is taken once per
+// device with hipGetSymbolAddress (with that device current) and only that address is
+// passed to the kernels.
+static_assert(TDT_NOALLOC_SCRATCH_BYTES % 256 == 0, "whole 256-byte blocks");
+static __device__ __align__(256) unsigned char scratch[TDT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this GPU's scratch copy for work on `stream` (the stream's
+// device; the current device for the null stream), or NULL on a HIP error.
+void* scratch_for(hipStream_t stream) {
+  int dev = -1;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int tdt_loss_fwd_bwd_noalloc(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,
+                                        const void* logits, const int64_t* logits_strides, const void* dur_logits,
+                                        const int64_t* dur_strides, int32_t num_durations, const int64_t* labels,
+                                        int64_t labels_stride, const int64_t* logit_lengths,
+                                        const int64_t* label_lengths, const int32_t* durations, int32_t blank,
+                                        double sigma, int32_t reduction, float* loss_out, void* grad_logits,
+                                        const int64_t* grad_strides, void* grad_dur_logits,
+                                        const int64_t* grad_dur_strides, int32_t* utt_status, void* stream) {
+  // every host check first (against a placeholder workspace address that is validated
+  // but never used), so that invalid arguments and oversized calls touch no HIP state
+  {
+    Params p;
+    bool grads = false, aligned = false;
+    void* const placeholder = (void*)(uintptr_t)256;
+    const int rc = prepare(dtype, B, T_max, U1_max, V, logits, logits_strides, dur_logits, dur_strides,
+                           num_durations, labels, labels_stride, logit_lengths, label_lengths, durations, blank,
+                           sigma, reduction, loss_out, true, false, grad_logits, grad_strides, grad_dur_logits,
+                           grad_dur_strides, utt_status, placeholder, (size_t)TDT_NOALLOC_SCRATCH_BYTES, &p, &grads,
+                           &aligned);
+    if (rc != TDT_OK) return rc;
+  }
+  void* ws = scratch_for((hipStream_t)stream);
+  if (!ws) return TDT_ERR_HIP;
+  return fwd_bwd_impl(dtype, B, T_max, U1_max, V, logits, logits_strides, dur_logits, dur_strides, num_durations,
+                      labels, labels_stride, logit_lengths, label_lengths, durations, blank, sigma, reduction,
+                      loss_out, grad_logits, grad_strides, grad_dur_logits, grad_dur_strides, utt_status, ws,
+                      (size_t)TDT_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0);
 }

@@ -26,7 +26,8 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert {"tdt_loss_fwd_bwd", "tdt_loss_workspace_size", "tdt_loss_status_string",
-            "tdt_loss_abi_version", "tdt_loss_fwd_bwd_timed", "tdt_loss_backward"} <= names
+            "tdt_loss_abi_version", "tdt_loss_fwd_bwd_timed", "tdt_loss_backward",
+            "tdt_loss_fwd_bwd_noalloc"} <= names
     lib = _native.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -156,3 +157,36 @@ def _bwd(**over):
 ])
 def test_backward_rejects_invalid_arguments(over, code):
     assert _bwd(**over) == code
+
+
+def _noalloc(**over):
+    args = dict(dtype=2, B=2, T_max=10, U1_max=5, V=9, logits=FAKE, lstr=[450, 45, 9], dur=FAKE + 4096,
+                dstr=[450, 45, 9], D=3, labels=FAKE, lab_stride=4, tlen=FAKE, ulen=FAKE, durations=[0, 1, 2],
+                blank=8, sigma=0.0, reduction=3, loss=FAKE, glog=None, gstr=None, gdur=None, gdstr=None,
+                status=None, stream=None)
+    args.update(over)
+    return _native.fwd_bwd_noalloc_raw(*args.values())
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(os.path.join(ROOT, "include", "tdt_loss.h")).read()
+    m = re.search(r"#define TDT_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == _native.NOALLOC_SCRATCH_BYTES
+
+
+# Every call below fails a host check before the library looks up its device array, so
+# nothing reaches the device (the pointers are fake).
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=3), _native.TDT_ERR_UNSUPPORTED_DTYPE),
+    (dict(reduction=9), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(logits=None), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(blank=9), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(durations=[0, 0, 1]), _native.TDT_ERR_INVALID_ARGUMENT),
+    (dict(lab_stride=2), _native.TDT_ERR_BAD_STRIDE),
+    (dict(glog=FAKE + 2, gstr=[450, 45, 9], gdur=FAKE + 12288, gdstr=[450, 45, 9]), _native.TDT_ERR_INVALID_ARGUMENT),
+    # a workspace beyond the library's array
+    (dict(B=64, T_max=1000, U1_max=500, lstr=[500 * 1000 * 12, 500 * 12, 12], dstr=[500 * 1000 * 12, 500 * 12, 12],
+          lab_stride=499), _native.TDT_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_noalloc_host_checks(over, code):
+    assert _noalloc(**over) == code
