@@ -70,13 +70,14 @@ typedef enum {
 #define TDT_UTT_INFEASIBLE 8       /* no alignment exists */
 
 /* Limits of this build: 1 <= num_durations <= 16, duration values in [0, 16] with at
- * least one > 0, U1_max <= 8192, and fewer than 2^31 (lattice position, row segment)
- * pairs per call, a row segment being up to 512 16-byte chunks of a logits row (beyond
- * these: TDT_ERR_UNSUPPORTED).  bf16 logits whose row maximum exceeds about 2.3e38 in
- * magnitude give their utterance a NaN loss. */
+ * least one > 0, T_max and U1_max below 2^24 with T_max * U1_max below 2^27, and fewer
+ * than 2^31 (node, row segment) pairs per call, a row segment being up to 512 16-byte
+ * chunks of a logits row (beyond these: TDT_ERR_UNSUPPORTED).  There is no other limit on
+ * the label count: long label sequences are swept as bands of tiles.  bf16 logits whose
+ * row maximum exceeds about 2.3e38 in magnitude give their utterance a NaN loss; a move
+ * whose log-weight is below about -9.3e7 (e.g. a logit masked with -1e10) is impossible. */
 #define TDT_MAX_DURATIONS 16
 #define TDT_MAX_DURATION_VALUE 16
-#define TDT_MAX_U1 8192
 
 /*
  * Workspace bytes needed by tdt_loss_fwd_bwd for these sizes.

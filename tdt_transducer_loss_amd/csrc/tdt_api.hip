@@ -17,11 +17,11 @@ namespace {
 using tdt::Params;
 
 struct Layout {
-  int KD, WP, DM, NW, NPR, RS, nseg, nch, gnseg, gnch;
-  int RW, UW, PR;
-  size_t off_pwin, off_pwout, pw_bytes;
-  size_t off_rstat, off_part, off_pr, off_wout, off_win, off_ar, off_br, off_rec;
-  size_t off_logp, off_logpa, off_wts, off_pm, off_pe, off_uok, off_xflag, off_lpx, off_lcnt;
+  int KD, A, Bb, DM, NW, NP, LG, RS, R, nT, nU, TT, nseg, nch, gnseg, gnch;
+  int64_t box;
+  size_t pw_bytes;
+  size_t off_part, off_stat, off_lg, off_pw, off_ar, off_br, off_lx;
+  size_t off_logp, off_wts, off_pm, off_pe, off_uok, off_xflag;
   size_t total;
 };
 
@@ -47,63 +47,71 @@ int check_durations(const int32_t* durations, int32_t D) {
   return any_pos ? maxd : TDT_ERR_INVALID_ARGUMENT;
 }
 
+// Workspace layout (every array 256-byte aligned), per node position of the padded box
+// [B, Tmax, U1max] in diagonal-major order (see Params): row-segment partials, row
+// statistics, log-domain move ingredients (overwritten by the gradient-pass record),
+// plain outgoing weights, alpha and beta; per utterance and tile column the label
+// contributions crossing a tile edge; per utterance a few words.
 int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V, int32_t D, int maxd, Layout* L) {
   if (dtype < 0 || dtype > 2) return TDT_ERR_UNSUPPORTED_DTYPE;
   if (B < 1 || Tmax < 1 || U1max < 1 || V < 1) return TDT_ERR_INVALID_ARGUMENT;
   if (V > ((int64_t)1 << 30) || B > ((int64_t)1 << 24)) return TDT_ERR_UNSUPPORTED;
-  if (U1max > TDT_MAX_U1) return TDT_ERR_UNSUPPORTED;
-  if (Tmax > (1 << 24)) return TDT_ERR_UNSUPPORTED;
+  if (Tmax > (1 << 24) || U1max > (1 << 24)) return TDT_ERR_UNSUPPORTED;
+  L->box = Tmax * U1max;
+  // alpha / beta / edge records of one utterance are addressed with 32-bit byte offsets
+  if (L->box * 16 >= ((int64_t)1 << 31)) return TDT_ERR_UNSUPPORTED;
   L->KD = (int)(Tmax + U1max - 1);
-  L->WP = (int)(Tmax < U1max ? Tmax : U1max);
+  L->A = (int)(Tmax < U1max ? Tmax : U1max);
+  L->Bb = (int)(Tmax < U1max ? U1max : Tmax);
   L->DM = pick_dm(maxd);
   L->NW = 2 * L->DM + 1;
-  L->NPR = L->DM + 3;
+  L->NP = L->DM + 1;
+  L->LG = 2 + D;
   L->RS = 5 + D;
+  // lattice tiles: one tile of 64 R labels (R = 2 only for durations up to 4) holding
+  // every frame, or bands of 64-label x 64-frame tiles for longer label sequences
+  if (U1max <= 64 || (L->DM == 4 && U1max <= 128)) {
+    L->R = U1max <= 64 ? 1 : 2;
+    L->TT = (int)Tmax;
+    L->nT = 1;
+    L->nU = 1;
+  } else {
+    L->R = 1;
+    L->TT = 64;
+    L->nT = (int)((Tmax + 63) / 64);
+    L->nU = (int)((U1max + 63) / 64);
+  }
   tdt::pick_segments(V, dtype == 0 ? 4 : 8, tdt::kRowWindows, &L->nch, &L->nseg);
   tdt::pick_segments(V, dtype == 0 ? 4 : 8, tdt::kGradWindows, &L->gnch, &L->gnseg);
-  const size_t NP = (size_t)B * (size_t)L->KD * (size_t)L->WP;
-  L->RW = tdt::rec_bytes(L->DM);
-  // the lattice addresses one utterance's weight records with 32-bit byte offsets
-  if ((size_t)L->KD * (size_t)L->WP * (size_t)L->RW > (size_t)0x7fffffff) return TDT_ERR_UNSUPPORTED;
-  if (NP > ((size_t)1 << 40)) return TDT_ERR_UNSUPPORTED;
-  // the row passes index (position, segment) pairs with 32-bit integers
-  if (NP * (size_t)L->nseg >= ((size_t)1 << 31)) return TDT_ERR_UNSUPPORTED;
+  const size_t NPOS = (size_t)B * (size_t)L->box;
+  // the row passes index (node, row segment) pairs with 32-bit integers
   const size_t segs = (size_t)(L->nseg > L->gnseg ? L->nseg : L->gnseg);
-  if ((size_t)B * (size_t)Tmax * (size_t)U1max * segs >= ((size_t)1 << 31)) return TDT_ERR_UNSUPPORTED;
+  if (NPOS * segs >= ((size_t)1 << 31)) return TDT_ERR_UNSUPPORTED;
+  const size_t nu64 = (size_t)((U1max + 63) / 64);
+  if (nu64 * (size_t)Tmax * 16 >= ((size_t)1 << 31)) return TDT_ERR_UNSUPPORTED;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
     o = align_up(o + bytes);
     return at;
   };
-  L->off_rstat = take(NP * 16);
-  L->off_part = take(NP * (size_t)L->nseg * 8);
-  L->off_pr = take(NP * (size_t)L->NPR * 8);
-  L->off_wout = take(NP * (size_t)L->RW);
-  L->off_win = take(NP * (size_t)L->RW);
-  L->off_ar = take(NP * 16);
-  L->off_br = take(NP * 16);
-  L->off_rec = take(NP * (size_t)L->RS * 4);
-  // slot-pair-major plain weights for the plain sweeps, addressed with 32-bit byte
-  // offsets per utterance (without them the extended-range sweep runs)
-  // labels per lane of the plain sweep that reads the copy (the lattice launcher's choice)
-  L->PR = U1max <= 256 ? (U1max <= 64 ? 1 : U1max <= 128 ? 2 : 4)
-                       : (U1max <= 768 ? 1 : U1max <= 1536 ? 2 : U1max <= 3072 ? 4 : 8);
-  const int64_t uq = L->PR > 4 ? L->PR : 4;  // rows hold whole bands of UW / PR columns
-  L->UW = (int)((U1max + uq - 1) / uq * uq);
-  const size_t pw_utt = (size_t)L->KD * (size_t)((L->NW + 1) / 2) * (size_t)L->UW * 16;
-  L->pw_bytes = pw_utt <= (size_t)0x7fffffff ? pw_utt * (size_t)B : 0;
-  L->off_pwin = take(L->pw_bytes);
-  L->off_pwout = take(L->pw_bytes);
+  L->off_part = take(NPOS * (size_t)L->nseg * 8);
+  L->off_stat = take(NPOS * 8);
+  L->off_lg = take(NPOS * (size_t)L->LG * 8);
+  // plain weights, addressed with 32-bit byte offsets per utterance (without them the
+  // extended-range sweeps run)
+  const size_t pw_utt = (size_t)tdt::pw_utt_entries(L->NP, L->box, L->KD) * 16;
+  L->pw_bytes = pw_utt < ((size_t)1 << 31) ? pw_utt * (size_t)B : 0;
+  L->off_pw = take(L->pw_bytes);
+  L->off_ar = take(NPOS * 16);
+  L->off_br = take(NPOS * 16);
+  L->off_lx = take((size_t)B * nu64 * (size_t)Tmax * 16);
   L->off_logp = take((size_t)B * 8);
-  L->off_logpa = take((size_t)B * 8);
   L->off_wts = take((size_t)B * 8);
   L->off_pm = take((size_t)B * 8);
   L->off_pe = take((size_t)B * 4);
   L->off_uok = take((size_t)B * 4);
   L->off_xflag = take((size_t)B * 4);
-  L->off_lpx = take((size_t)B * 16);
-  L->off_lcnt = take((size_t)B * 4);
   L->total = o;
   return TDT_OK;
 }
@@ -112,7 +120,7 @@ bool aligned_to(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 }  // namespace
 
-extern "C" int tdt_loss_abi_version(void) { return 2; }
+extern "C" int tdt_loss_abi_version(void) { return 3; }
 
 extern "C" const char* tdt_loss_status_string(int status) {
   switch (status) {
@@ -224,11 +232,19 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   p.red = reduction;
   p.dtype = dtype;
   p.KD = L.KD;
-  p.WP = L.WP;
+  p.A = L.A;
+  p.Bb = L.Bb;
+  p.box = L.box;
+  p.triA = (int64_t)L.A * (L.A + 1) / 2;
   p.DM = L.DM;
   p.NW = L.NW;
-  p.NPR = L.NPR;
+  p.NP = L.NP;
+  p.LG = L.LG;
   p.RS = L.RS;
+  p.R = L.R;
+  p.nT = L.nT;
+  p.nU = L.nU;
+  p.TT = L.TT;
   p.nseg = L.nseg;
   p.nch = L.nch;
   p.gnseg = L.gnseg;
@@ -255,8 +271,6 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   p.lab_stride = labels_stride;
   p.Tlen = logit_lengths;
   p.Ulen = label_lengths;
-  p.Btot = p.B;
-  p.Ulen_tot = label_lengths;
   p.loss = loss_out;
   p.ustatus = utt_status;
   if (grads) {
@@ -270,28 +284,19 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
     p.gds2 = grad_dur_strides[2];
   }
   char* ws = (char*)workspace;
-  p.rstat = (float4*)(ws + L.off_rstat);
   p.part = (float*)(ws + L.off_part);
-  p.pr = (double*)(ws + L.off_pr);
-  p.wout = ws + L.off_wout;
-  p.win = ws + L.off_win;
+  p.stat = (float2*)(ws + L.off_stat);
+  p.lg = (double*)(ws + L.off_lg);
+  p.pw = L.pw_bytes ? (double*)(ws + L.off_pw) : nullptr;
   p.ar = ws + L.off_ar;
   p.br = ws + L.off_br;
-  p.RW = L.RW;
-  p.rec = (float*)(ws + L.off_rec);
-  p.UW = L.UW;
-  p.PR = L.PR;
-  p.pwin = L.pw_bytes ? (double*)(ws + L.off_pwin) : nullptr;
-  p.pwout = L.pw_bytes ? (double*)(ws + L.off_pwout) : nullptr;
+  p.lx = ws + L.off_lx;
   p.logp = (double*)(ws + L.off_logp);
-  p.logpa = (double*)(ws + L.off_logpa);
   p.wts = (double*)(ws + L.off_wts);
   p.pm = (double*)(ws + L.off_pm);
   p.pe = (int*)(ws + L.off_pe);
   p.uok = (int*)(ws + L.off_uok);
   p.xflag = (int*)(ws + L.off_xflag);
-  p.lpx = (double*)(ws + L.off_lpx);
-  p.lcnt = (int*)(ws + L.off_lcnt);
 
   // Row and gradient chunks coincide when the logits and gradient rows share their
   // address modulo 16 bytes for every node.

@@ -40,15 +40,26 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umul
 
 // Everything the kernels of one call need, passed by value.
 //
-// Workspace layout.  Per utterance b the lattice nodes are stored by anti-diagonal:
-// position (b, k, i) with k = t + u in [0, KD) and i = u - ulo(k) in [0, WP), where
-// ulo(k) = max(0, k - T + 1).  pos = (b*KD + k)*WP + i.  Each position holds records
-// of row statistics, transition weights, alpha, beta and the gradient-pass coefficients.
+// Workspace layout.  Per utterance b the nodes (t, u) of the padded box
+// [0, Tmax) x [0, U1max) are stored diagonal-major: diagonal k = t + u in [0, KD), and
+// within it by u, so node (t, u) sits at
+//   pos = b * box + diag_off(k) + u - max(0, k - Tmax + 1),   box = Tmax * U1max,
+// where diag_off(k) counts the box nodes on diagonals below k (closed form below).  One
+// step of a lattice sweep (one anti-diagonal) thus reads and writes consecutive records,
+// and the workspace holds exactly the padded box (nodes outside an utterance are unused).
 struct Params {
   int B, Tmax, U1max, V, D, blank, red, dtype;
-  int KD, WP, DM, NW, NPR, RS;
-  int nseg, nch;    // row-statistics pass: segments per row, 64-chunk windows per segment
-  int gnseg, gnch;  // the same for the gradient pass
+  int KD;            // diagonals of the padded box: Tmax + U1max - 1
+  int A, Bb;         // min and max of Tmax, U1max
+  int64_t box;       // Tmax * U1max
+  int64_t triA;      // A (A + 1) / 2
+  int DM, NW, NP;    // duration bound of the kernels, move slots 2 DM + 1, slot pairs DM + 1
+  int LG;            // doubles per node in lg: 2 + D
+  int RS;            // floats of the gradient-pass record: 5 + D
+  int R;             // labels per lane of the lattice sweep (1 or 2)
+  int nT, nU, TT;    // lattice tiles: nT rows of TT frames, nU columns of 64 R labels
+  int nseg, nch;     // row-statistics pass: segments per row, 64-chunk windows per segment
+  int gnseg, gnch;   // the same for the gradient pass
   FastDiv fd_nseg, fd_gnseg, fd_u1, fd_tu1;  // by nseg, gnseg, U1max, Tmax*U1max
   double sigma;
   int dval[kMaxD];          // duration value of index i
@@ -62,11 +73,6 @@ struct Params {
   int64_t lab_stride;
   const int64_t* Tlen;
   const int64_t* Ulen;
-  // The kernels of one call may see a group of utterances (all pointers above and
-  // below offset to the group's first utterance, B = group size); the reduction
-  // weights use the whole batch: Btot utterances with label lengths Ulen_tot.
-  int Btot;
-  const int64_t* Ulen_tot;
   // outputs
   float* loss;     // NULL: the loss is not written (gradient-only call)
   int32_t* ustatus;
@@ -75,33 +81,57 @@ struct Params {
   int64_t gs0, gs1, gs2;
   void* gdur;
   int64_t gds0, gds1, gds2;
-  // workspace, per position
-  float4* rstat;  // {c, K, h_blank, h_label}: log-sum-exp of the row = lse(c, K), see row_lse
-  float* part;    // [2 * nseg] per row segment: its shift c and its sum 2^(x log2e - c), see k_row_partial
-  double* pr;     // [NPR]: softmax(h)_blank, softmax(h)_label, softmax(g) by duration value 0..DM
-  char* wout;     // [positions] weight records of the moves out of each node (RW bytes)
-  char* win;      // [positions] weight records of the moves into each node
-  char* ar;       // [positions] alpha, 16-byte records (float64 mantissa, int32 exponent)
-  char* br;       // [positions] beta, same records
-  int RW;         // bytes per weight record
-  float* rec;     // [RS] per-node record of the gradient pass
-  double* pwin;   // plain weights of the moves into / out of each node, by slot pair:
-  double* pwout;  //   [b][k][slot / 2][u][slot % 2] (NULL when too large)
-  int UW;         // labels per row of pwin / pwout (a multiple of 4 and of PR)
-  int PR;         // labels per lane of the plain sweep reading them: label u is stored at
-                  //   (u % PR) * (UW / PR) + u / PR, so that the lanes of one load read
-                  //   consecutive 16-byte pairs
+  // workspace, per node position
+  float* part;    // [nseg] float2 per row segment: its shift c and its sum 2^(x log2e - c), see k_row_partial
+  float2* stat;   // row pass: (h_blank, h_label); node weights then store (c, K), lse = row_lse(c, K)
+  double* lg;     // [LG]: l_blank - sigma, l_label - sigma, lambda[D] (log-softmax of the
+                  //   durations); the coefficient kernel overwrites it with the RS floats
+                  //   of the gradient-pass record
+  double* pw;     // plain outgoing move weights by slot pairs, see pw_entry
+  char* ar;       // alpha, 16-byte records (float64 mantissa, int32 exponent)
+  char* br;       // beta, same records
+  char* lx;       // [b][nU][Tmax] 16-byte records: label contributions crossing a tile column edge
   // workspace, per utterance
   double* logp;   // log P from beta(0,0)
-  double* logpa;  // log P from the alpha terminal (diagnostic)
   double* wts;    // reduction weight w_b
   double* pm;     // P as mantissa / exponent
   int* pe;
   int* uok;       // 1: gradients are written from the lattice, 0: zeros
   int* xflag;     // 1: some move weight lies outside [2^-300, 2^300] (extended-range sweep only)
-  double* lpx;    // [2]: log P of the plain single-wave sweep, alpha and beta
-  int* lcnt;      // plain single-wave sweeps finished (zeroed by the row-statistics pass)
 };
+
+// ---- padded-box diagonal layout ----
+// box nodes on diagonals 0 .. k-1
+__device__ __forceinline__ int64_t diag_off(const Params& p, int k) {
+  if (k <= p.A) return (int64_t)k * (k + 1) / 2;
+  if (k <= p.Bb) return p.triA + (int64_t)(k - p.A) * p.A;
+  const int64_t r = p.KD - k;
+  return p.box - r * (r + 1) / 2;
+}
+// smallest u on diagonal k, and the diagonal's node count
+__device__ __forceinline__ int diag_ulo(const Params& p, int k) { return max(0, k - p.Tmax + 1); }
+__device__ __forceinline__ int diag_len(const Params& p, int k) {
+  return min(k, p.U1max - 1) - diag_ulo(p, k) + 1;
+}
+// position of node (t, u) of utterance b
+__device__ __forceinline__ int64_t node_pos(const Params& p, int b, int t, int u) {
+  const int k = t + u;
+  return (int64_t)b * p.box + diag_off(p, k) + (u - diag_ulo(p, k));
+}
+// Plain outgoing weights: per utterance, diagonal k owns a block of NP x (len(k) + 3)
+// 16-byte entries at entry NP (diag_off(k) + 3k) (slot pairs major, one column per node
+// of the diagonal, up to 3 unused columns); entry (pair q, node index i) is at column
+// (i % R) * ceil(len / R) + i / R, so that the lanes of a sweep holding R labels each read
+// consecutive entries for each of their labels.  Slot d - 1 (d = 1..DM) is the blank move
+// of duration d, slot DM + d (d = 0..DM) the label move of duration d.
+__host__ __device__ constexpr int64_t pw_utt_entries(int64_t NP, int64_t box, int64_t KD) {
+  return NP * (box + 3 * KD);
+}
+__device__ __forceinline__ int64_t pw_block(const Params& p, int k) { return (int64_t)p.NP * (diag_off(p, k) + 3 * (int64_t)k); }
+__device__ __forceinline__ int pw_col(int i, int len, int R) {
+  const int half = (len + R - 1) / R;
+  return R == 1 ? i : (i % R) * half + i / R;
+}
 
 // ---- extended-range non-negative numbers: value = m * 2^e ----
 struct Ext {
@@ -172,17 +202,6 @@ __device__ __forceinline__ Ext ext_sum(const Ext (&t)[N]) {
 __device__ __forceinline__ double row_lse(bool base2, double c, double K) {
   return base2 ? (c + K) * kLn2 : c + K * kLn2;
 }
-
-// ---- lattice layout ----
-__device__ __forceinline__ int diag_ulo(int k, int T) { return max(0, k - T + 1); }
-
-__device__ __forceinline__ int64_t node_pos(const Params& p, int b, int k, int i) {
-  return ((int64_t)b * p.KD + k) * p.WP + i;
-}
-
-// Bytes of one node's weight record: 2*DM+1 float64 mantissas and as many int32
-// exponents, rounded up to 16 bytes.
-__host__ __device__ constexpr int rec_bytes(int DM) { return ((12 * (2 * DM + 1) + 15) / 16) * 16; }
 
 __device__ __forceinline__ bool utt_dims_ok(const Params& p, int64_t T, int64_t U) {
   return T >= 0 && T <= p.Tmax && U >= 0 && U <= p.U1max - 1;

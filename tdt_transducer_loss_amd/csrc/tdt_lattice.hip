@@ -1,136 +1,85 @@
 // Lattice side of the TDT loss on gfx950:
-//   node weights  — duration log-softmax and the extended-range weight of every move out
-//                   of a node (thread per node), stored per node as an outgoing record
-//                   and scattered into the incoming record of each destination;
-//   lattice       — float64 alpha and beta sweeps over the T x (U+1) lattice, one
-//                   work-group per (utterance, direction), anti-diagonal wavefront with
-//                   the label index across lanes (the alpha/beta passes of the page
-//                   "tdt-loss: add TDT loss kernel", comment "What's in it": float64,
-//                   no 1024-label limit);
+//   node weights  — duration log-softmax, the log-domain move ingredients and the plain
+//                   float64 weight of every move out of a node (one group of lanes per
+//                   node, lane d = duration value d);
+//   lattice tiles — float64 alpha and beta sweeps over the T x (U+1) lattice (the
+//                   alpha/beta passes of the page "tdt-loss: add TDT loss kernel", comment
+//                   "What's in it": float64, no 1024-label limit), as an anti-diagonal
+//                   wavefront with the label index across the lanes of one wave; label
+//                   sequences longer than one wave holds are cut into tiles of 64 labels x
+//                   64 frames swept band after band (one launch per band of tiles), so
+//                   there is no limit on the label count and no work-group waits for another;
 //   coefficients  — posteriors of the moves out of each node and the per-node record of
 //                   the gradient pass, plus the loss reduction.
 //
-// Probabilities are kept in the linear domain as extended-range float64 (mantissa and a
-// separate int exponent), so a lattice step is multiply-adds and exponent arithmetic
-// with no exp/log on the serial chain.
+// Probabilities are kept in the linear domain: plain float64 numbers relative to a
+// per-lane binary scale where every move weight lies in [2^-300, 2^300] (range-checked
+// step by step), extended-range float64 (mantissa and a separate int exponent) otherwise,
+// so a lattice step is multiply-adds and exponent arithmetic with no exp/log on the
+// serial chain of the plain sweep.
 #include "tdt_kernels.h"
 
 namespace tdt {
 
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x3v __attribute__((ext_vector_type(3)));
-// Pointer into LDS (address space 3): stores and loads through it are ds_* operations
-// and never wait on outstanding global loads.
-typedef __attribute__((address_space(3))) int lds_int;
+
+// A buffer offset beyond every buffer range used here (all below 2^31 bytes): loads at
+// it read zeros and stores to it are dropped.
+constexpr int kBadOff = (int)0x80000000u;
 
 // Reduction weight w_b of utterance b (d reduced loss / d loss_b).
 __device__ double reduction_weight(const Params& p, int b, int64_t sumU) {
   switch (p.red) {
-    case 3: return 1.0 / (double)p.Btot;  // mean_batch
-    case 2: {                             // mean
+    case 3: return 1.0 / (double)p.B;  // mean_batch
+    case 2: {                          // mean
       const int64_t U = p.Ulen[b];
-      return 1.0 / ((double)p.Btot * (double)(U > 1 ? U : 1));
+      return 1.0 / ((double)p.B * (double)(U > 1 ? U : 1));
     }
     case 4: return 1.0 / (double)(sumU > 1 ? sumU : 1);  // mean_volume
     default: return 1.0;                                 // none, sum
   }
 }
 
-// ---- records ----
-// Weight record of a node (RW bytes, 16-byte aligned): NW float64 mantissas, then NW
-// int32 exponents carrying +kWBias (all-zero bits = the zero weight).  Slot d-1
-// (d = 1..DM) is the blank move of duration d, slot DM+d (d = 0..DM) the label move of
-// duration d.  Alpha / beta records are 16 bytes: float64 mantissa, int32 exponent.
-__device__ __forceinline__ char* wrec(char* base, const Params& p, int64_t pos) { return base + pos * p.RW; }
-
-__device__ __forceinline__ void wrec_put(char* rec, int NW, int s, Ext w) {
-  ((double*)rec)[s] = w.m;
-  ((int*)(rec + 8 * NW))[s] = w.m == 0.0 ? 0 : w.e + kWBias;
+// A lattice position group of the padded box's diagonal bounding box [KD x A]: decode
+// utterance b, diagonal k and index i on the diagonal; false outside the box.
+__device__ __forceinline__ bool box_node(const Params& p, int64_t g, int& b, int& k, int& i) {
+  const int64_t per = (int64_t)p.KD * p.A;
+  b = (int)(g / per);
+  if (b >= p.B) return false;
+  const int64_t rem = g - (int64_t)b * per;
+  k = (int)(rem / p.A);
+  i = (int)(rem - (int64_t)k * p.A);
+  return i < diag_len(p, k);
 }
 
-// A move weight: values in [2^-1000, 2^1000] are stored as plain float64 numbers with a
-// zero exponent (exactly), others in extended form.  Returns true when the weight is
-// non-zero and outside [2^-300, 2^300], the range the plain-float64 sweep accepts.
-__device__ __forceinline__ bool wrec_put_weight(char* rec, int NW, int s, Ext w) {
-  if (w.m == 0.0) {
-    wrec_put(rec, NW, s, ext_zero());
-    return false;
-  }
-  const Ext n = ext_norm(w.m, w.e);  // value in [2^(e-1), 2^e)
-  if (n.e >= -999 && n.e <= 1000) {
-    ((double*)rec)[s] = ldexp(n.m, n.e);
-    ((int*)(rec + 8 * NW))[s] = kWBias;
-  } else {
-    wrec_put(rec, NW, s, n);
-  }
-  return n.e < -299 || n.e > 300;
-}
-
-// Slot-pair-major copy of the plain float64 weights for the plain sweeps (empty when one
-// utterance's copy would exceed 2 GB): [b][k][slot / 2][column][slot % 2], rows of UW
-// columns, label u in column (u % PR) * (UW / PR) + u / PR, so that one 16-byte load per
-// lane fetches two slots of one of its R = PR labels and the lanes of a wave read
-// consecutive bytes.
-__host__ __device__ constexpr int slot_pairs(int NW) { return (NW + 1) / 2; }
-
-__device__ __forceinline__ void pw_put(double* pw, const Params& p, int b, int k, int s, int u, Ext w) {
-  if (pw) {
-    const int col = (u % p.PR) * (p.UW / p.PR) + u / p.PR;  // label u of lane u / PR
-    pw[((((int64_t)b * p.KD + k) * slot_pairs(p.NW) + (s >> 1)) * p.UW + col) * 2 + (s & 1)] =
-        w.m == 0.0 ? 0.0 : ldexp(w.m, w.e);
-  }
-}
-
-__device__ __forceinline__ Ext wrec_get(const char* rec, int NW, int s) {
-  return Ext{((const double*)rec)[s], ((const int*)(rec + 8 * NW))[s] - kWBias};
-}
-
-__device__ __forceinline__ Ext xrec_get(const char* base, int64_t pos) {
-  const char* r = base + pos * 16;
-  return Ext{*(const double*)r, *(const int*)(r + 8)};
-}
+__host__ __device__ constexpr int group_lanes(int DM) { return DM < 8 ? 8 : (DM < 16 ? 16 : 32); }
 
 // ------------------------------------------------------------------------------------
-// Node weights: for node n = (t,u)
-//   l_blank = h_blank - lse, l_label = h_{y_{u+1}} - lse, lambda = log_softmax(g(n)),
-//   W_blank(d) = exp(l_blank - sigma + lambda_d)  (d > 0; t+d < T, or t+d = T at u = U),
-//   W_label(d) = exp(l_label - sigma + lambda_d)  (u < U, t+d < T),
-// plus softmax(h)_blank, softmax(h)_label and softmax(g) for the gradient.  A group of
-// NG = 8, 16 or 32 lanes (at least DM + 1) works on one lattice position: lane d of the
-// group handles duration value d, lanes 0..3 the per-node exponentials, so the float64
-// work of a node is spread over its group.  Every record of a node in the lattice is
-// written: moves that leave the lattice, absent durations and moves with no source hold
-// the zero weight, so the sweeps read the records of active nodes without predicates.
-// Slot s of the incoming record of n is written by the source of that move, or zeroed by
-// n itself when the source does not exist (exactly one writer per slot).
+// Node weights: for node n = (t,u) of utterance b
+//   lb = l_blank - sigma, ly = l_label - sigma (l = log-softmax of the token logits),
+//   lambda_i = log-softmax of the duration logits,
+//   W_blank(d) = exp(lb + lambda_d)  (d > 0; t+d < T, or t+d = T at u = U),
+//   W_label(d) = exp(ly + lambda_d)  (u < U, t+d < T),
+// stored as the log-domain ingredients (lb, ly, lambda) and as plain float64 weights by
+// slot pairs (zero for absent durations and for moves that leave the lattice).  A group
+// of NG lanes (at least DM + 1) works on one node: lane d handles duration value d, so
+// the float64 work of a node is spread over its group.  The group also combines the row
+// segments' log-sum-exp partials into the row statistics (c, K).
 template <int DM>
 __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
-  constexpr int NW = 2 * DM + 1;
-  constexpr int NG = DM < 8 ? 8 : (DM < 16 ? 16 : 32);
+  constexpr int NG = group_lanes(DM);
   const int64_t gt = (int64_t)xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
   const int j = threadIdx.x & (NG - 1);  // lane in the group: duration value j
-  const int64_t g = gt / NG;              // lattice position of the group
-  const int64_t per = (int64_t)p.KD * p.WP;
-  const int b = (int)(g / per);
-  if (b >= p.B) return;  // whole groups leave together
-  const int64_t rem = g - (int64_t)b * per;
-  const int k = (int)(rem / p.WP);
-  const int i = (int)(rem - (int64_t)k * p.WP);
-  const int64_t pos = (int64_t)b * per + rem;
-  char* orec = wrec(p.wout, p, pos);
-  char* irec = wrec(p.win, p, pos);
+  int b, k, i;
+  // whole groups leave together: every condition depends on the node only
+  if (!box_node(p, gt / NG, b, k, i)) return;
   const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
+  if (!utt_dims_ok(p, T64, U64)) return;
   const int T = (int)T64, U = (int)U64;
-  const bool dims = utt_dims_ok(p, T64, U64);
-  const int u = dims ? diag_ulo(k, T) + i : 0;
-  const bool valid = dims && k < T + U && u <= min(k, U);
+  const int u = diag_ulo(p, k) + i, t = k - u;
+  if (t >= T || u > U) return;
+  const int64_t pos = (int64_t)b * p.box + diag_off(p, k) + i;
   const int d = j;
-  // positions outside the utterance write nothing: every slot of a node in the lattice
-  // is written by the source of its move or zeroed by the node itself, and the sweeps
-  // discard whatever lanes outside the lattice compute
-  if (!valid) return;
-  const int t = k - u;
 
   // the duration logit of this lane, loaded first
   const int idx = d <= DM ? p.didx[d] : -1;
@@ -162,23 +111,11 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
   for (int o = NG / 2; o >= 1; o >>= 1) S += __shfl_xor(S, o, NG);
   const double K = log2(S);
   const double L = row_lse(base2, (double)mx, K);  // natural-log normaliser
-  const float4 rs = p.rstat[pos];
-  const double lb = (double)rs.z - L;
-  const double ly = (u < U && rs.w > -__builtin_inff()) ? (double)rs.w - L : -__builtin_inf();
+  const float2 hs = p.stat[pos];                   // blank and label logits (row pass)
+  const double lb = (double)hs.x - L - p.sigma;
+  const double ly = (u < U && hs.y > -__builtin_inff()) ? (double)hs.y - L - p.sigma : -__builtin_inf();
 
-  // lanes 0..3: exp(l_blank - sigma), exp(l_label - sigma) in extended range, and
-  // softmax(h)_blank, softmax(h)_label
-  const double xl = (j & 1) ? ly : lb;
-  Ext ex = ext_zero();
-  if (j < 2) ex = ext_exp(xl - p.sigma);
-  double* pr = p.pr + pos * p.NPR;
-  if (j >= 2 && j < 4) pr[j - 2] = exp(xl);
-  if (j == 0) ((float2*)(p.rstat + pos))[0] = make_float2(mx, (float)K);
-  const int base = threadIdx.x & ~(NG - 1);
-  const Ext eb = Ext{__shfl(ex.m, base, 64), __shfl(ex.e, base, 64)};
-  const Ext ey = Ext{__shfl(ex.m, base + 1, 64), __shfl(ex.e, base + 1, 64)};
-
-  // duration softmax: lambda_d = gl - gmax - log(sg)
+  // duration log-softmax: lambda = gl - gmax - log(sum exp(g - gmax))
   double gmax = gl;
 #pragma unroll
   for (int o = NG / 2; o >= 1; o >>= 1) gmax = fmax(gmax, __shfl_xor(gmax, o, NG));
@@ -186,314 +123,404 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
   double sg = eg;
 #pragma unroll
   for (int o = NG / 2; o >= 1; o >>= 1) sg += __shfl_xor(sg, o, NG);
-  const double pd = eg / sg;
-  // exp(lambda_d) in extended range: the quotient unless it left the normal range
-  const Ext ed = !has ? ext_zero() : (gl - gmax > -700.0 ? ext_norm(pd, 0) : ext_exp(gl - gmax - log(sg)));
+  const double lam = has ? gl - gmax - log(sg) : -__builtin_inf();
 
+  double* lg = p.lg + pos * p.LG;
+  if (j == 0) {
+    lg[0] = lb;
+    lg[1] = ly;
+    p.stat[pos] = make_float2(mx, (float)K);  // after every lane of the group read hs
+  }
+  if (has) lg[2 + idx] = lam;
+
+  // plain outgoing weights; a non-zero weight outside [2^-300, 2^300] sends the utterance
+  // to the extended-range sweeps
+  constexpr double kLo = -300.0 * 0.6931471805599453, kHi = 300.0 * 0.6931471805599453;
   bool wide = false;
   if (d <= DM) {
-    pr[2 + d] = has ? pd : 0.0;
-    const int64_t ub = (int64_t)b * per;
+    const int len = diag_len(p, k);
+    double* pw = p.pw ? p.pw + ((int64_t)b * pw_utt_entries(p.NP, p.box, p.KD) + pw_block(p, k) +
+                                pw_col(i, len, p.R)) * 2
+                      : nullptr;
+    const int64_t pstride = (int64_t)(len + 3) * 2;  // doubles between slot pairs
     if (d >= 1) {
-      const bool inside = t + d < T;
-      const bool ok = has && (inside || (t + d == T && u == U));
-      const Ext wb = ok ? ext_mul(eb, ed) : ext_zero();
-      wide |= wrec_put_weight(orec, NW, d - 1, wb);
-      pw_put(p.pwout, p, b, k, d - 1, u, wb);
-      if (inside) {  // incoming slot of (t+d, u)
-        const int k2 = k + d;
-        wrec_put_weight(wrec(p.win, p, ub + (int64_t)k2 * p.WP + (u - diag_ulo(k2, T))), NW, d - 1, wb);
-        pw_put(p.pwin, p, b, k2, d - 1, u, wb);
-      }
-      if (t - d < 0) {  // no source for this slot
-        wrec_put(irec, NW, d - 1, ext_zero());
-        pw_put(p.pwin, p, b, k, d - 1, u, ext_zero());
-      }
+      const bool ok = has && (t + d < T || (t + d == T && u == U));
+      const double x = ok ? lb + lam : -__builtin_inf();
+      wide |= x > -__builtin_inf() && (x < kLo || x > kHi);
+      const int s = d - 1;
+      if (pw) pw[(s >> 1) * pstride + (s & 1)] = exp(x);
     }
-    const bool inside = u < U && t + d < T;
-    const Ext wl = (has && inside) ? ext_mul(ey, ed) : ext_zero();
-    wide |= wrec_put_weight(orec, NW, DM + d, wl);
-    pw_put(p.pwout, p, b, k, DM + d, u, wl);
-    if (inside) {  // incoming slot of (t+d, u+1)
-      const int k2 = k + d + 1;
-      wrec_put_weight(wrec(p.win, p, ub + (int64_t)k2 * p.WP + (u + 1 - diag_ulo(k2, T))), NW, DM + d, wl);
-      pw_put(p.pwin, p, b, k2, DM + d, u + 1, wl);
-    }
-    if (u == 0 || t - d < 0) {
-      wrec_put(irec, NW, DM + d, ext_zero());
-      pw_put(p.pwin, p, b, k, DM + d, u, ext_zero());
-    }
+    const bool okl = has && u < U && t + d < T;
+    const double xl = okl ? ly + lam : -__builtin_inf();
+    wide |= xl > -__builtin_inf() && (xl < kLo || xl > kHi);
+    const int s = DM + d;
+    if (pw) pw[(s >> 1) * pstride + (s & 1)] = exp(xl);
   }
   if (wide) atomicOr(p.xflag + b, 1);
 }
 
 // ------------------------------------------------------------------------------------
-// Lattice sweeps.  Thread j owns labels u = j*R .. j*R + R - 1.  Step k of the alpha
-// sweep computes anti-diagonal k (t = k - u); every dependency lies on diagonals
-// k-1 .. k-1-DM, kept in a register ring of S >= DM+1 slots.  S is a multiple of 6 so
-// that, after unrolling S steps, the exchange parity (2) and the triple buffer of
-// weight records prefetched two steps ahead (3) sit in fixed registers.  The value of
-// the neighbouring label index owned by the next thread is exchanged once per step (DPP
-// wave shift for one wave, LDS + barrier otherwise).  The beta sweep runs the same
-// wavefront from the last diagonal back to (0,0).
-template <int DM>
-__host__ __device__ constexpr int ring_size() { return ((DM + 1 + 5) / 6) * 6; }
-
-template <bool SW>
-__device__ __forceinline__ Ext exchange(Ext v, bool from_left, int parity, double* xm, int* xe) {
-  if (SW) {
-    const long long bitsv = __double_as_longlong(v.m);
-    int lo = (int)(bitsv & 0xffffffffll), hi = (int)(bitsv >> 32);
-    int e = v.e;
-    if (from_left) {  // lane i receives lane i-1 (wave_shr:1); lane 0 receives zero
-      lo = __builtin_amdgcn_update_dpp(0, lo, 0x138, 0xf, 0xf, false);
-      hi = __builtin_amdgcn_update_dpp(0, hi, 0x138, 0xf, 0xf, false);
-      e = __builtin_amdgcn_update_dpp(kEZ, e, 0x138, 0xf, 0xf, false);
-    } else {          // lane i receives lane i+1 (wave_shl:1); lane 63 receives zero
-      lo = __builtin_amdgcn_update_dpp(0, lo, 0x130, 0xf, 0xf, false);
-      hi = __builtin_amdgcn_update_dpp(0, hi, 0x130, 0xf, 0xf, false);
-      e = __builtin_amdgcn_update_dpp(kEZ, e, 0x130, 0xf, 0xf, false);
-    }
-    const long long nb = ((long long)(unsigned)hi << 32) | (unsigned)lo;
-    return Ext{__longlong_as_double(nb), e};
-  } else {
-    const int tid = threadIdx.x, nt = blockDim.x;
-    xm[parity * 1024 + tid] = v.m;
-    xe[parity * 1024 + tid] = v.e;
-    __syncthreads();
-    const int src = from_left ? tid - 1 : tid + 1;
-    if (src < 0 || src >= nt) return ext_zero();
-    return Ext{xm[parity * 1024 + src], xe[parity * 1024 + src]};
-  }
-}
-
-// Pairwise (tree) reductions for the sum of extended values: shorter dependency chains
-// than a running sum, which is what bounds one lattice step.
-template <int N>
-__device__ __forceinline__ int tree_max_e(const Ext* t) {
-  if constexpr (N == 1) return t[0].e;
-  else return max(tree_max_e<N / 2>(t), tree_max_e<N - N / 2>(t + N / 2));
-}
-template <int N>
-__device__ __forceinline__ double tree_sum_m(const Ext* t, int E) {
-  if constexpr (N == 1) return ldexp(t[0].m, t[0].e - E);
-  else return tree_sum_m<N / 2>(t, E) + tree_sum_m<N - N / 2>(t + N / 2, E);
-}
-// Sum of terms whose exponents all carry +kWBias; returns the un-biased sum.
-template <int N>
-__device__ __forceinline__ Ext ext_sum_biased(const Ext (&t)[N]) {
-  const int E = tree_max_e<N>(t);
-  const double sm = tree_sum_m<N>(t, E);
-  return ext_norm(sm, E - kWBias);
-}
-
-// A weight record loaded as RW/16 16-byte words; decoded slot by slot.
-template <int DM>
-struct WRec {
-  static constexpr int NW = 2 * DM + 1;
-  static constexpr int NQ = rec_bytes(DM) / 16;
-  u32x4v q[NQ];
-  __device__ __forceinline__ uint32_t dw(int j) const { return q[j >> 2][j & 3]; }
-  __device__ __forceinline__ Ext get(int s) const {  // biased exponent kept
-    const uint64_t bits = ((uint64_t)dw(2 * s + 1) << 32) | dw(2 * s);
-    return Ext{__builtin_bit_cast(double, bits), (int)dw(2 * NW + s)};
-  }
+// Lattice tiles.
+//
+// A tile covers frames [t0, t1) and labels [u0, ulast] of one utterance; lane l of the
+// sweeping wave owns labels u0 + l R .. u0 + l R + R - 1.  Step by step the wave walks the
+// tile's anti-diagonals k = t + u.  Values of nodes outside the tile that the tile
+// needs come from memory: the alpha (beta) of up to DM frames below (above) the tile,
+// replayed as if computed, and, for alpha, the label moves entering the tile's first
+// label from the tile to its left (`lx`, written by that tile); for beta the last lane
+// reads the beta of the label right of the tile.  Those tiles belong to earlier bands.
+//
+// Alpha runs in push form: when node (t, u) is done, its value times each of its outgoing
+// weights is added to accumulator rings for the destinations (blank: (t+d, u) in the same
+// label; label: (t+d, u+1)), and the complete label contribution into (t, u+1) moves to
+// the next label (same lane, or the next lane by a DPP shift) for the next step.  Beta
+// runs in pull form from the beta of the destinations.  Both read only the node's own
+// outgoing weight record, which lies on the node's own diagonal: the records a step reads
+// are contiguous.
+struct Tile {
+  int b, T, U;
+  int t0, t1;       // frames of the tile: [t0, t1), t1 <= T
+  int u0, ulast;    // labels: [u0, ulast], ulast <= U
+  bool below, above, left, right;  // other tiles hold frames < t0, frames >= t1, labels < u0, labels > ulast
 };
 
-// P = beta(0,0) of utterance b: log P, P as mantissa / exponent, the gradient flag and
-// the infeasible status bit.
-__device__ void beta_final(const Params& p, int b, Ext P) {
-  const double lp = ext_log(P);
-  p.logp[b] = lp;
-  p.pm[b] = P.m;
-  p.pe[b] = P.e;
-  const bool feasible = P.m > 0.0 && lp == lp;
-  p.uok[b] = feasible ? 1 : 0;
-  if (p.ustatus) p.ustatus[b] = (P.m > 0.0 || lp != lp) ? 0 : 8;
+__device__ __forceinline__ bool make_tile(const Params& p, int b, int T, int U, int i, int j, int width,
+                                          Tile& tl) {
+  tl.b = b;
+  tl.T = T;
+  tl.U = U;
+  tl.t0 = i * p.TT;
+  tl.t1 = min(tl.t0 + p.TT, T);
+  tl.u0 = j * width;
+  tl.ulast = min(tl.u0 + width - 1, U);
+  tl.below = tl.t0 > 0;
+  tl.above = tl.t1 < T;
+  tl.left = tl.u0 > 0;
+  tl.right = tl.ulast < U;
+  return tl.t0 < T && tl.u0 <= U;
 }
 
-// log P from the alpha side (the thread that owns u = U, after its last alpha store):
-// the blanks that land on t = T from u = U.
+// Ring slots: S >= DM + 2 (the accumulators of DM + 1 future frames plus the contribution
+// in flight to the next label), a multiple of 6 so that unrolled loops hold whole rings
+// and whole rounds of the prefetch buffers.
 template <int DM>
-__device__ double alpha_terminal(const Params& p, int b, int T, int U) {
-  constexpr int NW = 2 * DM + 1;
-  __threadfence();
-  Ext terms[DM];
-#pragma unroll
-  for (int d = 1; d <= DM; ++d) {
-    terms[d - 1] = ext_zero();
-    const int t = T - d;
-    if (t >= 0) {
-      const int k = t + U;
-      const int64_t pos = node_pos(p, b, k, U - diag_ulo(k, T));
-      terms[d - 1] = ext_mul(xrec_get(p.ar, pos), wrec_get(wrec(p.wout, p, pos), NW, d - 1));
-    }
-  }
-  const double lp = ext_log(ext_sum(terms));
-  p.logpa[b] = lp;
-  return lp;
-}
+__host__ __device__ constexpr int ring_size() { return ((DM + 2 + 5) / 6) * 6; }
 
-// One direction of the lattice.  ALPHA: forward sweep with the incoming records;
-// otherwise backward sweep with the node's outgoing records, beta of the terminal
-// (t = T, u = U) seeded as 1 in the ring.  Moves that leave the lattice and moves with
-// no source have zero weight, and sources outside the lattice have zero alpha, so no
-// term needs a predicate; a node outside the lattice is forced to zero.  Out-of-range
-// record reads return zero (buffer range check).  `prog` (LDS) receives the step index
-// for the L2 warm-up waves.
-template <int DM, int R, bool SW, bool ALPHA>
-__device__ void sweep(const Params& p, int b, int T, int U, int tid, double* xm, int* xe, lds_int* prog) {
-  constexpr int NW = 2 * DM + 1;
-  constexpr int S = ring_size<DM>();
-  constexpr int RWB = rec_bytes(DM);
-  const int nsteps = T + U;
-  const int WP = p.WP;
-  const int64_t nrec = (int64_t)p.KD * WP;
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((ALPHA ? p.win : p.wout) + b * nrec * RWB), (short)0, (int)(nrec * RWB), 0x00020000);
-  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((ALPHA ? p.ar : p.br) + b * nrec * 16), (short)0, (int)(nrec * 16), 0x00020000);
-  Ext h[R][S];
-  Ext nb[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    nb[s] = ext_zero();
-#pragma unroll
-    for (int r = 0; r < R; ++r) h[r][s] = ext_zero();
-  }
-  if (!ALPHA) {
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (tid * R + r == U) h[r][S - 1] = ext_one();  // beta(T, U): the terminal
-  }
-  // NB record buffers, prefetched NB-1 steps ahead (NB divides the unroll length S)
-  constexpr int NB = (DM <= 4 && R == 1) ? S : 3;
-  WRec<DM> wb[NB][R];
-
-  auto load_w = [&](int ks, WRec<DM> (&w)[R]) {
-    const int k = ALPHA ? ks : nsteps - 1 - ks;
-    const int base = k * WP - diag_ulo(k, T);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      int off = (base + tid * R + r) * RWB;
-      asm volatile("" : "+v"(off));  // keep the per-chunk constants in the instruction offset
-      constexpr int NQ = WRec<DM>::NQ;
-#pragma unroll
-      for (int j = 0; j < NQ - 1; ++j) w[r].q[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + 16 * j, 0, 0);
-      // the record holds 12*NW bytes (NW odd): its last 16-byte word ends with 4 bytes of
-      // padding, which are not loaded
-      const u32x3v last = __builtin_amdgcn_raw_buffer_load_b96(wr, off + 16 * (NQ - 1), 0, 0);
-      w[r].q[NQ - 1] = u32x4v{last.x, last.y, last.z, 0u};
-    }
-  };
-
-#pragma unroll
-  for (int j = 0; j < NB - 1; ++j) load_w(j, wb[j]);
-  for (int k0 = 0; k0 < nsteps; k0 += S) {
-#pragma unroll
-    for (int ph = 0; ph < S; ++ph) {
-      const int ks = k0 + ph;
-      if (ks >= nsteps) break;
-      // unconditional: past the last step the offsets fall outside the records of this
-      // utterance and the buffer range check returns zeros (never consumed), and a
-      // conditional load would make the wait before the next use cover this load too
-      load_w(ks + NB - 1, wb[(ph + NB - 1) % NB]);
-      const int k = ALPHA ? ks : nsteps - 1 - ks;
-      const int base = k * WP - diag_ulo(k, T);
-      Ext nv[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int u = tid * R + r, t = k - u;
-        const bool act = (unsigned)t < (unsigned)T && u <= U;
-        const WRec<DM>& w = wb[ph % NB][r];
-        Ext terms[NW];
-#pragma unroll
-        for (int d = 1; d <= DM; ++d) terms[d - 1] = ext_mul(h[r][(ph - d + 4 * S) % S], w.get(d - 1));
-        if (ALPHA) {
-#pragma unroll
-          for (int d = 0; d <= DM; ++d) {
-            const Ext src = r > 0 ? h[r > 0 ? r - 1 : 0][(ph - 1 - d + 4 * S) % S] : nb[(ph - 1 - d + 4 * S) % S];
-            terms[DM + d] = ext_mul(src, w.get(DM + d));
-          }
-        } else {
-#pragma unroll
-          for (int d = 0; d <= DM; ++d) {
-            const Ext dst = r < R - 1 ? h[r < R - 1 ? r + 1 : 0][(ph - 1 - d + 4 * S) % S] : nb[(ph - 1 - d + 4 * S) % S];
-            terms[DM + d] = ext_mul(dst, w.get(DM + d));
-          }
-        }
-        Ext a = ext_sum_biased(terms);
-        if (ALPHA && ks == 0 && u == 0) a = ext_one();
-        if (!act) a = ext_zero();
-        nv[r] = a;
-        const int o = act ? (base + u) * 16 : -16;
-        const uint64_t mb = __builtin_bit_cast(uint64_t, a.m);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4v{(uint32_t)mb, (uint32_t)(mb >> 32), (uint32_t)a.e, 0u}, xr, o, 0,
-                                               0);
-        if (!ALPHA && ks == nsteps - 1 && u == 0) beta_final(p, b, a);  // beta(0,0) = P
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) h[r][ph] = nv[r];
-      nb[ph] = exchange<SW>(ALPHA ? nv[R - 1] : nv[0], ALPHA, ph & 1, xm, xe);
-      if (SW) __hip_atomic_store(prog, ks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-  }
-  if (ALPHA && tid * R <= U && U < tid * R + R) (void)alpha_terminal<DM>(p, b, T, U);
-}
-
-// ------------------------------------------------------------------------------------
-// Plain-float64 sweep (one wave, R label indices per lane).  Lane u keeps its values as
-// plain float64 numbers x relative to a lane scale: value = x * 2^sc.  Every S steps
-// each lane shifts its rings and sc so that its newest value is near 1; a neighbour's
-// value arrives with the neighbour's scale and is converted once, so values of different
-// labels on one anti-diagonal may lie any number of binary orders apart.  A step is then
-// DM + (DM + 1) fused multiply-adds per label on plain numbers.  Every move weight of the
-// utterance lies in [2^-300, 2^300] (checked by the node-weight kernel).  Mass lost to
-// underflow (or an overflow) cannot be seen step by step without cost; it is caught
-// afterwards by comparing log P from the two directions, each of which would lose a
-// different share of it, and the caller then redoes both with the extended-range sweep.
-// Alpha/beta records are written in extended form.
-// Record buffers of the plain sweep, from {6, 3, 2}: as many as fit about 240 VGPRs (R
-// labels of 2*DM+1 float64 per buffer) and keep the loads of NB-1 steps in flight within
-// the 6-bit memory counter (per step: one load per slot pair and label, and R stores); 0
-// when even 2 do not fit in 200 VGPRs (the extended-range sweep is used then).
+// Prefetch buffers of the plain sweeps: as many as fit about 200 VGPRs together with the
+// alpha rings (2 R S float64) and keep the loads of NB - 1 steps within the 6-bit memory
+// counter; NB divides the ring size.  0: no plain sweep (durations beyond 8 run the
+// extended-range sweeps only).
 template <int DM, int R>
-__host__ __device__ constexpr int fast_buffers() {
-  constexpr int NW = 2 * DM + 1;
-  constexpr int per = R * 2 * NW;                        // VGPRs of one buffer
-  constexpr int ops = slot_pairs(NW) * R + R;            // memory instructions per step
-  constexpr int steps = 60 / ops;                        // steps in flight
-  return (6 * per <= 240 && steps >= 5) ? 6
-         : (3 * per <= 240 && steps >= 2) ? 3
-         : (2 * per <= 200 && steps >= 1) ? 2 : 0;
+__host__ __device__ constexpr int plain_buffers() {
+  constexpr int NP = DM + 1, S = ring_size<DM>();
+  constexpr int budget = 200 - 4 * R * S;
+  constexpr int per = 4 * NP * R + 8;      // VGPRs of one buffer (weights and boundary records)
+  constexpr int mem = NP * R + 4;          // memory instructions per step
+  constexpr int steps = 56 / mem;          // steps in flight the counter allows
+  return (6 * per <= budget && steps >= 5) ? 6
+         : (S % 4 == 0 && 4 * per <= budget && steps >= 3) ? 4
+         : (3 * per <= budget && steps >= 2) ? 3
+         : (2 * per <= budget && steps >= 1) ? 2 : 0;
 }
 
-// The NW weights of R consecutive labels, loaded slot by slot from the slot-major copy.
+// Range check of the plain sweeps by binary exponents (frexp: x = m 2^e, m in [0.5, 1);
+// e = 0 for a zero): a value that left [2^-700, 2^700], or an input that would have
+// entered the lane's scale outside it, sends the tile to the extended-range sweep.
+struct RangeTrack {
+  int lo = 0, hi = 0;
+  __device__ __forceinline__ void add_exp(int e) {
+    lo = min(lo, e);
+    hi = max(hi, e);
+  }
+  __device__ __forceinline__ void add(double x) { add_exp(__builtin_amdgcn_frexp_exp(x)); }
+  __device__ __forceinline__ bool bad() const { return lo <= -700 || hi > 700; }
+};
+
+// An extended record (float64 value, int32 binary exponent) as the 16 bytes of a buffer
+// load, normalised (a zero gets the extended zero's exponent).
+__device__ __forceinline__ Ext rec_ext(u32x4v x) {
+  return ext_norm(__builtin_bit_cast(double, ((uint64_t)x.y << 32) | x.x), (int)x.z);
+}
+__device__ __forceinline__ u32x4v ext_rec(Ext v) {
+  const uint64_t mb = __builtin_bit_cast(uint64_t, v.m);
+  return u32x4v{(uint32_t)mb, (uint32_t)(mb >> 32), (uint32_t)v.e, 0u};
+}
+// a plain value x * 2^sc as a record (not normalised: every reader normalises)
+__device__ __forceinline__ u32x4v plain_rec(double x, int sc) {
+  const uint64_t mb = __builtin_bit_cast(uint64_t, x);
+  return u32x4v{(uint32_t)mb, (uint32_t)(mb >> 32), (uint32_t)sc, 0u};
+}
+
+// A plain value enters a lane: v = m 2^e in the lane's scale sc.  A lane that holds no
+// value yet (`started` = 0) takes the scale that puts v near 1; `started` becomes an
+// all-ones mask once the lane holds a value.  Bit operations only: no branch and no lane
+// mask logic on the chain.  The exponent v would have is recorded in `rt` (so an input
+// that would underflow to zero in the lane's scale is caught too).
+__device__ __forceinline__ double enter(double m, int e, int& sc, int& started, RangeTrack& rt) {
+  const uint32_t hi = (uint32_t)((uint64_t)__double_as_longlong(m) >> 32);
+  const int nz = -(int)min((hi >> 20) & 0x7ffu, 1u);  // all ones for a normal non-zero m
+  const int em = __builtin_amdgcn_frexp_exp(m);
+  const int keep = started | ~nz;  // keep the scale: the lane holds a value, or m is zero
+  sc = (keep & sc) | (~keep & (e + em));
+  started |= nz;
+  rt.add_exp((e + em - sc) & nz);
+  return ldexp(m, e - sc);
+}
+
+// Running geometry of one diagonal of the padded box: the position of its first node
+// (diag_off), its smallest u and its node count, stepped one diagonal at a time with a
+// few selects (the closed forms take 64-bit arithmetic and branches).
+struct DiagCursor {
+  int k, off, ulo, len;
+  __device__ __forceinline__ void init(const Params& p, int k0) {
+    k = k0;
+    off = (int)diag_off(p, k0);
+    ulo = diag_ulo(p, k0);
+    len = diag_len(p, k0);
+  }
+  __device__ __forceinline__ void next(const Params& p) {  // k -> k + 1
+    off += len;
+    ++k;
+    const int up = k < p.U1max ? 1 : 0, lo = k >= p.Tmax ? 1 : 0;  // gains a node at the top, loses one at t = Tmax
+    len += up - lo;
+    ulo += lo;
+  }
+  __device__ __forceinline__ void prev(const Params& p) {  // k -> k - 1
+    --k;
+    const int up = k + 1 < p.U1max ? 1 : 0, lo = k + 1 >= p.Tmax ? 1 : 0;
+    len -= up - lo;
+    ulo -= lo;
+    off -= len;
+  }
+  // first 16-byte entry of the diagonal's plain-weight block
+  __device__ __forceinline__ int pw_block(const Params& p) const { return p.NP * (off + 3 * k); }
+};
+
+// Buffer resource over `bytes` bytes at `base` (range-checked: out-of-range loads read 0,
+// out-of-range stores are dropped).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+// position of node (t, u) relative to its utterance
+__device__ __forceinline__ int64_t rel_pos(const Params& p, int t, int u) {
+  const int k = t + u;
+  return diag_off(p, k) + (u - diag_ulo(p, k));
+}
+
+// The NP slot pairs of R labels' plain weights (v[s][r] = weight slot s of label r), the
+// boundary records and the position base of one step's diagonal.
 template <int DM, int R>
 struct WPlain {
-  static constexpr int NW = 2 * DM + 1;
-  double v[NW][R];
+  static constexpr int NP = DM + 1;
+  double v[2 * NP][R];
+  u32x4v x0, x1;  // boundary records: own label's replayed value, and the neighbour's (see callers)
+  int dbase;      // position of node (k - u, u) of the diagonal relative to the utterance: dbase + u
 };
 
-template <int DM, int R, bool ALPHA>
-__device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, double* lp_out) {
-  constexpr int S = ring_size<DM>();
-  // weight buffers, prefetched NB-1 steps ahead
-  constexpr int NB = fast_buffers<DM, R>();
-  constexpr int UL = NB > S ? NB : S;  // steps unrolled per iteration
-  static_assert(NB >= 2 && UL % S == 0 && UL % NB == 0, "unroll must hold whole rings and buffer rounds");
-  const int nsteps = T + U;
-  const int WP = p.WP, UW = p.UW;
-  const int64_t nrec = (int64_t)p.KD * WP;
-  const int64_t npw = (int64_t)p.KD * slot_pairs(p.NW) * UW * 2;  // plain weights of one utterance
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((ALPHA ? p.pwin : p.pwout) + b * npw), (short)0, (int)(npw * 8), 0x00020000);
-  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((ALPHA ? p.ar : p.br) + b * nrec * 16), (short)0, (int)(nrec * 16), 0x00020000);
-  const int u0 = lane * R;  // labels u0 .. u0 + R - 1 of this lane
-  unsigned Tl[R];          // node (k - u, u) is in the lattice iff k - u < Tl
+// Plain weights of the labels u0 + lane R + r (r < R) on the cursor's diagonal, for the
+// labels whose node `need`s them (the others read zeros).  Node index i = u - ulo on the
+// diagonal; its entry is block + (i % R) ceil(len / R) + i / R: a lane-constant plus a
+// uniform part.
+template <int DM, int R>
+__device__ __forceinline__ void load_weights(const Params& p, __amdgpu_buffer_rsrc_t wr, const DiagCursor& c, int lane,
+                                             int u0, const bool (&need)[R], WPlain<DM, R>& w) {
+  constexpr int NP = DM + 1;
+  const int blk = c.pw_block(p);
+  const int cap = c.len + 3;
+  const int half = (c.len + R - 1) / R;
 #pragma unroll
-  for (int r = 0; r < R; ++r) Tl[r] = u0 + r <= U ? (unsigned)T : 0u;
+  for (int r = 0; r < R; ++r) {
+    const int ir = r + u0 - c.ulo;  // i = lane R + ir
+    const int col = R == 1 ? lane + ir : (ir & (R - 1)) * half + lane + (ir >> (R == 2 ? 1 : 2));
+    const int off = need[r] ? (blk + col) * 16 : kBadOff;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      // the slot pair's offset is uniform: it goes in the scalar offset
+      const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(wr, off, q * cap * 16, 0);
+      w.v[2 * q][r] = __builtin_bit_cast(double, ((uint64_t)x.y << 32) | x.x);
+      w.v[2 * q + 1][r] = __builtin_bit_cast(double, ((uint64_t)x.w << 32) | x.z);
+    }
+  }
+}
+
+__device__ __forceinline__ double dpp_shift_f64(double x, bool right) {
+  const long long bits = __double_as_longlong(x);
+  int lo = (int)(bits & 0xffffffffll), hi = (int)(bits >> 32);
+  // wave_shr:1 / wave_shl:1; the lane without a source reads 0 (bound_ctrl)
+  lo = right ? __builtin_amdgcn_mov_dpp(lo, 0x138, 0xf, 0xf, true) : __builtin_amdgcn_mov_dpp(lo, 0x130, 0xf, 0xf, true);
+  hi = right ? __builtin_amdgcn_mov_dpp(hi, 0x138, 0xf, 0xf, true) : __builtin_amdgcn_mov_dpp(hi, 0x130, 0xf, 0xf, true);
+  return __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ int dpp_shift_i32(int x, bool right) {
+  return right ? __builtin_amdgcn_mov_dpp(x, 0x138, 0xf, 0xf, true) : __builtin_amdgcn_mov_dpp(x, 0x130, 0xf, 0xf, true);
+}
+
+// Plain alpha sweep of a tile.  Returns true when some value left [2^-700, 2^700] (the
+// tile is then redone in extended range).
+template <int DM, int R, bool BOUND>
+__device__ bool alpha_plain(const Params& p, const Tile& tl, int lane) {
+  constexpr int S = ring_size<DM>();
+  constexpr int NB = plain_buffers<DM, R>();
+  static_assert(NB >= 2 && S % NB == 0, "prefetch buffers must divide the ring");
+  static_assert(S >= DM + 2, "ring slots: DM + 1 pending frames and one in flight");
+  static_assert(!BOUND || R == 1, "band tiles hold one label per lane");
+  const int b = tl.b;
+  const int trl = tl.below ? max(0, tl.t0 - DM) : tl.t0;  // first frame swept (replayed below t0)
+  const int kb = trl + tl.u0;
+  const int nsteps = tl.t1 - 1 + tl.ulast - kb + 1;
+  const int64_t pwe = pw_utt_entries(p.NP, p.box, p.KD);
+  const __amdgpu_buffer_rsrc_t wr = rsrc(p.pw + (int64_t)b * pwe * 2, pwe * 16);
+  const __amdgpu_buffer_rsrc_t ar = rsrc(p.ar + (int64_t)b * p.box * 16, p.box * 16);
+  const int nu64 = (p.U1max + 63) / 64;
+  const __amdgpu_buffer_rsrc_t xr = rsrc(p.lx + (int64_t)b * nu64 * p.Tmax * 16, (int64_t)nu64 * p.Tmax * 16);
+  const int ub = tl.u0 + lane * R;
+  // label r's node at step q is (kb + q - u, u): computed for q in [qa, qa + na), holding
+  // weights (computed or replayed) for q in [qn, qn + nn)
+  int qa[R], na[R], qn[R], nn[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int u = ub + r;
+    const bool in = u <= tl.ulast;
+    qa[r] = tl.t0 + u - kb;
+    na[r] = in ? tl.t1 - tl.t0 : 0;
+    qn[r] = trl + u - kb;
+    nn[r] = in ? tl.t1 - trl : 0;
+  }
+  const int nrep = nn[0] > 0 ? tl.t0 - trl : 0;  // replayed frames of label ub
+  double bacc[R][S], lacc[R][S];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int r = 0; r < R; ++r) bacc[r][s] = lacc[r][s] = 0.0;
+  int sc = 0, started = 0;
+  RangeTrack rt;
+  double lin = 0.0;  // label contribution into this lane's first label for the coming step
+  WPlain<DM, R> wb[NB];
+  DiagCursor cl;  // the diagonal being loaded, NB - 1 steps ahead
+  cl.init(p, kb);
+  int ql = 0;
+  const int xoff = ((ub / 64) * p.Tmax - ub) * 16;  // lx record of frame t = k - ub: xoff + 16 k
+  auto load = [&](WPlain<DM, R>& w) {
+    bool need[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) need[r] = (unsigned)(ql - qn[r]) < (unsigned)nn[r];
+    load_weights<DM, R>(p, wr, cl, lane, tl.u0, need, w);
+    w.dbase = cl.off - cl.ulo;
+    if (BOUND) {
+      // x0: the replayed alpha of a frame below the tile; x1 (lane 0): the label moves
+      // entering the tile's first label from the left tile
+      const bool rep = (unsigned)(ql - qn[0]) < (unsigned)nrep;
+      const bool edge = lane == 0 && tl.left && (unsigned)(ql - qa[0]) < (unsigned)na[0];
+      w.x0 = __builtin_amdgcn_raw_buffer_load_b128(ar, rep ? (w.dbase + ub) * 16 : kBadOff, 0, 0);
+      w.x1 = __builtin_amdgcn_raw_buffer_load_b128(xr, edge ? xoff + 16 * cl.k : kBadOff, 0, 0);
+    }
+    cl.next(p);
+    ++ql;
+  };
+#pragma unroll
+  for (int j = 0; j < NB - 1; ++j) load(wb[j]);
+  for (int q0 = 0; q0 < nsteps; q0 += S) {
+#pragma unroll
+    for (int ph = 0; ph < S; ++ph) {  // steps past the last diagonal touch no node
+      const int q = q0 + ph;
+      if (ph == 0) {  // keep the lane's pending values near 1 (a zero lane shifts by 0)
+        const double big = fmax(fmax(fabs(lin), fabs(bacc[0][0])), fmax(fabs(bacc[0][1]), fabs(lacc[R - 1][0])));
+        const int ex = __builtin_amdgcn_frexp_exp(big);
+        sc += ex;
+        lin = ldexp(lin, -ex);
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            bacc[r][s] = ldexp(bacc[r][s], -ex);
+            lacc[r][s] = ldexp(lacc[r][s], -ex);
+          }
+      }
+      load(wb[(ph + NB - 1) % NB]);
+      const WPlain<DM, R>& w = wb[ph % NB];
+      if (BOUND) {  // lane 0: the first label's input from the left tile (zero when not loaded)
+        const Ext x = rec_ext(w.x1);
+        const double e1 = enter(x.m, x.e, sc, started, rt);
+        lin = (lane == 0 && tl.left) ? e1 : lin;
+      }
+      double a[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const bool act = (unsigned)(q - qa[r]) < (unsigned)na[r];
+        const double in = r == 0 ? lin : lacc[r > 0 ? r - 1 : 0][(ph + S - 1) % S];
+        double v = act ? bacc[r][ph] + in : 0.0;
+        if (r == 0) {
+          const bool origin = act && kb + q == 0;  // alpha(0, 0) = 1
+          v = origin ? 1.0 : v;
+          sc = origin ? 0 : sc;
+          started = origin ? -1 : started;
+        }
+        if (BOUND && r == 0) {  // a replayed frame below the tile (zero when not loaded)
+          const Ext x = rec_ext(w.x0);
+          const double vr = enter(x.m, x.e, sc, started, rt);
+          v = (unsigned)(q - qn[0]) < (unsigned)nrep ? vr : v;
+        }
+        rt.add(v);
+        a[r] = v;
+        __builtin_amdgcn_raw_buffer_store_b128(plain_rec(v, sc), ar, act ? (w.dbase + ub + r) * 16 : kBadOff, 0, 0);
+      }
+      // push the new values along their outgoing moves; the first contribution to a
+      // ring slot (duration DM) replaces its consumed value
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int d = 1; d < DM; ++d) bacc[r][(ph + d) % S] = fma(a[r], w.v[d - 1][r], bacc[r][(ph + d) % S]);
+        bacc[r][(ph + DM) % S] = a[r] * w.v[DM - 1][r];
+#pragma unroll
+        for (int d = 0; d < DM; ++d) lacc[r][(ph + d) % S] = fma(a[r], w.v[DM + d][r], lacc[r][(ph + d) % S]);
+        lacc[r][(ph + DM) % S] = a[r] * w.v[2 * DM][r];
+      }
+      // the complete label contribution into (t, u + 1) of the last label goes to the next lane
+      const double out = lacc[R - 1][ph];
+      if (BOUND) {  // ... or, from lane 63, to the tile on the right
+        // record of column ub / 64 + 1 (lane 63: ub % 64 == 63) at frame t = k - ub
+        const bool edge = lane == 63 && tl.right && (unsigned)(q - qa[0]) < (unsigned)na[0];
+        __builtin_amdgcn_raw_buffer_store_b128(plain_rec(out, sc), xr, edge ? xoff + p.Tmax * 16 + 16 * (kb + q) : kBadOff,
+                                               0, 0);
+      }
+      lin = enter(dpp_shift_f64(out, true), dpp_shift_i32(sc, true), sc, started, rt);
+    }
+  }
+  return rt.bad();
+}
+
+// Plain beta sweep of a tile (pull form).  *P00 receives beta(0, 0) when the tile holds
+// node (0, 0) (lane 0).  Returns true when some value left [2^-700, 2^700].
+template <int DM, int R, bool BOUND>
+__device__ bool beta_plain(const Params& p, const Tile& tl, int lane, Ext* P00) {
+  constexpr int S = ring_size<DM>();
+  constexpr int NB = plain_buffers<DM, R>();
+  static_assert(NB >= 2 && S % NB == 0, "prefetch buffers must divide the ring");
+  const int b = tl.b, T = tl.T, U = tl.U;
+  const int rtop = min(tl.t1 + DM - 1, T);  // highest frame swept (replayed above t1, or the terminal)
+  const int kb = rtop + tl.ulast;
+  const int nsteps = kb - (tl.t0 + tl.u0) + 1;
+  const int64_t pwe = pw_utt_entries(p.NP, p.box, p.KD);
+  const __amdgpu_buffer_rsrc_t wr = rsrc(p.pw + (int64_t)b * pwe * 2, pwe * 16);
+  const __amdgpu_buffer_rsrc_t br = rsrc(p.br + (int64_t)b * p.box * 16, p.box * 16);
+  const int ub = tl.u0 + lane * R;
+  const int un = tl.u0 + 64 * R;  // the label right of the tile (read by lane 63)
+  // label r's node at step q is (kb - q - u, u): computed for q in [qa, qa + na)
+  int qa[R], na[R];
+  bool term[R];  // the terminal (T, U): beta = 1 at step 0 (its diagonal is the first)
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int u = ub + r;
+    const bool in = u <= tl.ulast;
+    qa[r] = kb - u - tl.t1 + 1;
+    na[r] = in ? tl.t1 - tl.t0 : 0;
+    term[r] = u == U && rtop == T;
+  }
+  // replayed frames above the tile of label ub: t in [t1, rr], at steps [qr, qr + nr)
+  const int rr = min(tl.t1 + DM - 1, T - 1);
+  const int qr = kb - ub - rr;
+  const int nr = (tl.above && ub <= tl.ulast) ? rr - tl.t1 + 1 : 0;
   double h[R][S], nb[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
@@ -501,458 +528,350 @@ __device__ void sweep_fast(const Params& p, int b, int T, int U, int lane, doubl
 #pragma unroll
     for (int r = 0; r < R; ++r) h[r][s] = 0.0;
   }
-  int sc = 0;             // the lane's scale: a value is x * 2^sc
-  bool started = false;   // the lane holds a non-zero value, so its scale is fixed
-  if (!ALPHA && u0 <= U && U < u0 + R) {  // beta(T, U): the terminal
+  int sc = 0, started = 0;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (u0 + r == U) h[r][S - 1] = 1.0;
-    started = true;
-  }
+  for (int r = 0; r < R; ++r) started = term[r] ? -1 : started;  // the terminal starts its lane at scale 0
+  RangeTrack rt;
   WPlain<DM, R> wb[NB];
-  auto load_w = [&](int ks, WPlain<DM, R>& w) {
-    const int k = ALPHA ? ks : nsteps - 1 - ks;
-    constexpr int NW = 2 * DM + 1, NP = slot_pairs(NW);
-    int off = (k * NP * UW + lane) * 16;  // label u0 + r in column r * (UW / R) + lane
-    asm volatile("" : "+v"(off));
+  // the diagonal being loaded, NB - 1 steps ahead (kb may be one past the box's last
+  // diagonal: the terminal of an utterance as long as the box; the closed forms hold there)
+  DiagCursor cl;
+  cl.init(p, kb);
+  int ql = 0;
+  auto load = [&](WPlain<DM, R>& w) {
+    bool need[R];
 #pragma unroll
-    for (int pr = 0; pr < NP; ++pr) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(wr, off + (pr * UW + r * (UW / R)) * 16, 0, 0);
-        w.v[2 * pr][r] = __builtin_bit_cast(double, ((uint64_t)x.y << 32) | x.x);
-        if (2 * pr + 1 < NW) w.v[2 * pr + 1][r] = __builtin_bit_cast(double, ((uint64_t)x.w << 32) | x.z);
-      }
+    for (int r = 0; r < R; ++r) need[r] = (unsigned)(ql - qa[r]) < (unsigned)na[r];
+    load_weights<DM, R>(p, wr, cl, lane, tl.u0, need, w);
+    w.dbase = cl.off - cl.ulo;
+    if (BOUND) {
+      // x0: the replayed beta of a frame above the tile; x1 (lane 63): the beta of the
+      // label right of the tile on this diagonal
+      const int tn = cl.k - un;
+      const bool rep = (unsigned)(ql - qr) < (unsigned)nr;
+      const bool edge = lane == 63 && tl.right && tn >= tl.t0 && tn < T;
+      w.x0 = __builtin_amdgcn_raw_buffer_load_b128(br, rep ? (w.dbase + ub) * 16 : kBadOff, 0, 0);
+      w.x1 = __builtin_amdgcn_raw_buffer_load_b128(br, edge ? (w.dbase + un) * 16 : kBadOff, 0, 0);
     }
+    cl.prev(p);
+    ++ql;
   };
-  // past the last step the loads fall outside this utterance's records (zeros) or hit
-  // records that are never consumed; loading unconditionally keeps the wait counts of
-  // the unrolled loop exact
 #pragma unroll
-  for (int j = 0; j < NB - 1; ++j) load_w(j, wb[j]);
-  // whole blocks of UL steps: steps past the last diagonal are inactive for every lane
-  for (int k0 = 0; k0 < nsteps; k0 += UL) {
+  for (int j = 0; j < NB - 1; ++j) load(wb[j]);
+  for (int q0 = 0; q0 < nsteps; q0 += S) {
 #pragma unroll
-    for (int q = 0; q < UL; ++q) {
-      const int ph = q % S;  // ring slot
-      if (ph == 0) {  // keep the lane's largest newest value near 1 (a zero lane shifts by 0)
-        double big = fabs(h[0][S - 1]);
-#pragma unroll
-        for (int r = 1; r < R; ++r) big = fmax(big, fabs(h[r][S - 1]));
-        int ex;
-        (void)frexp(big, &ex);
+    for (int ph = 0; ph < S; ++ph) {  // steps past the last diagonal touch no node
+      const int q = q0 + ph;
+      if (ph == 0) {  // keep the lane's newest values near 1
+        const double big = fmax(fabs(h[0][S - 1]), fabs(nb[S - 1]));
+        const int ex = __builtin_amdgcn_frexp_exp(big);
         sc += ex;
 #pragma unroll
-        for (int s2 = 0; s2 < S; ++s2) {
-          nb[s2] = ldexp(nb[s2], -ex);
+        for (int s = 0; s < S; ++s) {
+          nb[s] = ldexp(nb[s], -ex);
 #pragma unroll
-          for (int r = 0; r < R; ++r) h[r][s2] = ldexp(h[r][s2], -ex);
+          for (int r = 0; r < R; ++r) h[r][s] = ldexp(h[r][s], -ex);
         }
       }
-      const int ks = k0 + q;
-      load_w(ks + NB - 1, wb[(q + NB - 1) % NB]);
-      const int k = ALPHA ? ks : nsteps - 1 - ks;
-      const int base = k * WP - diag_ulo(k, T) + u0;
+      load(wb[(ph + NB - 1) % NB]);
+      const WPlain<DM, R>& w = wb[ph % NB];
       double a[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const WPlain<DM, R>& w = wb[q % NB];
-        // own moves (durations 1..DM), and the neighbour label's moves (durations 0..DM):
-        // label u-1 (alpha) or u+1 (beta), in this lane or from the next lane over
+        const bool act = (unsigned)(q - qa[r]) < (unsigned)na[r];
         double c0 = 0.0, c1 = 0.0, c2 = 0.0, c3 = 0.0;
 #pragma unroll
         for (int d = 1; d <= DM; ++d) {
-          const double x = h[r][(ph - d + 4 * S) % S] * w.v[d - 1][r];
-          if (d & 1) c0 += x; else c1 += x;
+          const double x = w.v[d - 1][r] * h[r][(ph - d + 4 * S) % S];
+          if (d & 1) c0 += x;
+          else c1 += x;
         }
 #pragma unroll
         for (int d = 0; d <= DM; ++d) {
           const int sl = (ph - 1 - d + 4 * S) % S;
-          const double src = ALPHA ? (r > 0 ? h[r > 0 ? r - 1 : 0][sl] : nb[sl])
-                                   : (r < R - 1 ? h[r < R - 1 ? r + 1 : 0][sl] : nb[sl]);
-          const double x = src * w.v[DM + d][r];
-          if (d & 1) c3 += x; else c2 += x;
+          const double dst = r < R - 1 ? h[r < R - 1 ? r + 1 : 0][sl] : nb[sl];
+          const double x = w.v[DM + d][r] * dst;
+          if (d & 1) c3 += x;
+          else c2 += x;
         }
-        a[r] = (c0 + c1) + (c2 + c3);
-        if (ALPHA && ks == 0 && u0 + r == 0) {  // alpha(0, 0)
-          a[r] = 1.0;
-          sc = 0;
-          started = true;
+        double v = act ? (c0 + c1) + (c2 + c3) : 0.0;
+        v = (term[r] && q == 0) ? ldexp(1.0, -sc) : v;
+        if (BOUND && r == 0) {  // a replayed frame above the tile (zero when not loaded)
+          const Ext x = rec_ext(w.x0);
+          const double vr = enter(x.m, x.e, sc, started, rt);
+          v = (unsigned)(q - qr) < (unsigned)nr ? vr : v;
         }
-        if (!((unsigned)(k - u0 - r) < Tl[r])) a[r] = 0.0;
+        rt.add(v);
+        a[r] = v;
+        __builtin_amdgcn_raw_buffer_store_b128(plain_rec(v, sc), br, act ? (w.dbase + ub + r) * 16 : kBadOff, 0, 0);
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        h[r][ph] = a[r];
-        int ea;
-        const double ma = frexp(a[r], &ea);  // (0, 0) for a zero
-        const int eo = a[r] != 0.0 ? ea + sc : kEZ;
-        const int o = (unsigned)(k - u0 - r) < Tl[r] ? (base + r) * 16 : -16;
-        const uint64_t mb = __builtin_bit_cast(uint64_t, ma);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4v{(uint32_t)mb, (uint32_t)(mb >> 32), (uint32_t)eo, 0u}, xr, o, 0,
-                                               0);
-        started = started || a[r] != 0.0;
+      for (int r = 0; r < R; ++r) h[r][ph] = a[r];
+      // the beta of the label after this lane's last one, on this diagonal: the next
+      // lane's first label (DPP wave shift), or the tile on the right for lane 63
+      double m = dpp_shift_f64(a[0], false);
+      int e = dpp_shift_i32(sc, false);
+      if (BOUND) {
+        const Ext x = rec_ext(w.x1);
+        m = lane == 63 ? x.m : m;
+        e = lane == 63 ? x.e : e;
       }
-      // lane exchange: alpha passes its last label's value to the next lane, beta its
-      // first label's value to the previous lane
-      const double out = ALPHA ? a[R - 1] : a[0];
-      const long long bits = __double_as_longlong(out);
-      int lo = (int)(bits & 0xffffffffll), hi = (int)(bits >> 32), e = sc;
-      constexpr int ctl = ALPHA ? 0x138 : 0x130;  // wave_shr:1 / wave_shl:1
-      lo = __builtin_amdgcn_update_dpp(0, lo, ctl, 0xf, 0xf, false);
-      hi = __builtin_amdgcn_update_dpp(0, hi, ctl, 0xf, 0xf, false);
-      e = __builtin_amdgcn_update_dpp(0, e, ctl, 0xf, 0xf, false);
-      const double m = __longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo);
-      {  // an empty lane takes a scale that puts its first input near 1 (the sender's
-         // own scale may be stale at the wavefront, far from the value it sends)
-        int em;
-        (void)frexp(m, &em);  // 0 for a zero
-        if (!started) sc = e + em;
-      }
-      started = started || m != 0.0;
-      nb[ph] = ldexp(m, e - sc);  // into this lane's scale
+      nb[ph] = enter(m, e, sc, started, rt);
     }
   }
-  if (ALPHA) {
-    if (u0 <= U && U < u0 + R) *lp_out = alpha_terminal<DM>(p, b, T, U);
-  } else if (lane == 0) {  // beta(0,0) = P: the value of the last step, still in the ring
+  if (lane == 0 && tl.t0 == 0 && tl.u0 == 0) {  // beta(0, 0): the last step's value of lane 0
     const int last = (nsteps - 1) % S;
-    double a = h[0][0];
+    double b00 = h[0][0];
 #pragma unroll
-    for (int s2 = 1; s2 < S; ++s2)
-      if (s2 == last) a = h[0][s2];
-    int ea;
-    const double ma = frexp(a, &ea);
-    const Ext P = a != 0.0 ? Ext{ma, ea + sc} : ext_zero();
-    beta_final(p, b, P);
-    *lp_out = ext_log(P);
+    for (int s = 1; s < S; ++s) b00 = s == last ? h[0][s] : b00;
+    int ex;
+    const double mm = frexp(b00, &ex);
+    *P00 = b00 != 0.0 ? Ext{mm, ex + sc} : ext_zero();
+  }
+  return rt.bad();
+}
+
+// ---- extended-range sweeps (one label per lane, no prefetch; the rare path) ----
+
+__device__ __forceinline__ Ext ext_add(Ext a, Ext b) {
+  const int E = max(a.e, b.e);
+  return ext_norm(ldexp(a.m, a.e - E) + ldexp(b.m, b.e - E), E);
+}
+
+// The 2 DM + 1 outgoing weights of node (t, u) in extended range, from its log-domain
+// ingredients (zero for absent durations and moves that leave the lattice).
+template <int DM>
+__device__ __forceinline__ void ext_weights(const Params& p, int b, int t, int u, int T, int U, Ext (&w)[2 * DM + 1]) {
+  const double* lg = p.lg + ((int64_t)b * p.box + rel_pos(p, t, u)) * p.LG;
+  const double lb = lg[0], ly = lg[1];
+#pragma unroll
+  for (int d = 0; d <= DM; ++d) {
+    const int idx = p.didx[d];
+    const double lam = idx >= 0 ? lg[2 + idx] : -__builtin_inf();
+    if (d >= 1) w[d - 1] = (t + d < T || (t + d == T && u == U)) ? ext_exp(lb + lam) : ext_zero();
+    w[DM + d] = (u < U && t + d < T) ? ext_exp(ly + lam) : ext_zero();
   }
 }
 
-// Plain-float64 sweep over several waves (U1max > 256): the lanes of all waves of the
-// work-group run across the labels, R per lane, with the lane scales, renormalisation and
-// per-step arithmetic of the single-wave sweep; the neighbour's value goes through LDS
-// with one barrier per step, and the records of the next step are loaded while that
-// exchange runs.  Alpha and beta run in different work-groups here, so the log P
-// comparison is not available: each lane checks instead that every value it creates,
-// converts or shifts stays within [2^-700, 2^700] (then, with every weight in
-// [2^-300, 2^300], no product or sum can underflow or overflow), and the work-group redoes
-// the direction with the extended-range sweep when any lane saw a value outside it.
-template <int DM, int R>
-__host__ __device__ constexpr bool fast_mw_ok() {
-  return R * 2 * (2 * DM + 1) + 2 * (R + 1) * ring_size<DM>() <= 150;  // VGPRs at 768 threads
+__device__ __forceinline__ Ext dpp_shift_ext(Ext v, bool right) {
+  const long long bits = __double_as_longlong(v.m);
+  int lo = (int)(bits & 0xffffffffll), hi = (int)(bits >> 32), e = v.e;
+  if (right) {  // lane i receives lane i - 1 (wave_shr:1); lane 0 receives the zero
+    lo = __builtin_amdgcn_update_dpp(0, lo, 0x138, 0xf, 0xf, false);
+    hi = __builtin_amdgcn_update_dpp(0, hi, 0x138, 0xf, 0xf, false);
+    e = __builtin_amdgcn_update_dpp(kEZ, e, 0x138, 0xf, 0xf, false);
+  } else {  // lane i receives lane i + 1 (wave_shl:1); lane 63 receives the zero
+    lo = __builtin_amdgcn_update_dpp(0, lo, 0x130, 0xf, 0xf, false);
+    hi = __builtin_amdgcn_update_dpp(0, hi, 0x130, 0xf, 0xf, false);
+    e = __builtin_amdgcn_update_dpp(kEZ, e, 0x130, 0xf, 0xf, false);
+  }
+  return Ext{__longlong_as_double(((long long)(unsigned)hi << 32) | (unsigned)lo), e};
 }
 
-__device__ __forceinline__ bool out_of_range(double x) {  // non-zero and outside [2^-700, 2^700]
-  const double a = fabs(x);
-  return a != 0.0 && (a < 0x1p-700 || a > 0x1p700);
+// Loads of records written earlier by this same wave go around the vector L1 (sc0).
+__device__ __forceinline__ Ext load_ext_rec(__amdgpu_buffer_rsrc_t r, int off) {
+  return rec_ext(__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 1));
 }
 
-template <int DM, int R, bool ALPHA>
-__device__ bool sweep_fast_mw(const Params& p, int b, int T, int U, int tid, double* xm, int* xe) {
-  constexpr int S = ring_size<DM>();
-  const int nt = blockDim.x;
-  const int nsteps = T + U;
-  const int WP = p.WP, UW = p.UW;
-  const int64_t nrec = (int64_t)p.KD * WP;
-  const int64_t npw = (int64_t)p.KD * slot_pairs(p.NW) * UW * 2;  // plain weights of one utterance
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((ALPHA ? p.pwin : p.pwout) + b * npw), (short)0, (int)(npw * 8), 0x00020000);
-  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((ALPHA ? p.ar : p.br) + b * nrec * 16), (short)0, (int)(nrec * 16), 0x00020000);
-  const int u0 = tid * R;
-  unsigned Tl[R];
+// Extended-range alpha sweep of a tile of at most 64 labels (push form, as alpha_plain).
+// The accumulators are kept aligned to the current step (index d: the frame d steps
+// ahead) and shifted after each step, so the loop needs no unrolling.
+template <int DM>
+__device__ void alpha_ext(const Params& p, const Tile& tl, int lane) {
+  constexpr int NW = 2 * DM + 1;
+  const int b = tl.b, T = tl.T, U = tl.U;
+  const int trl = tl.below ? max(0, tl.t0 - DM) : tl.t0;
+  const int kb = trl + tl.u0;
+  const int nsteps = tl.t1 - 1 + tl.ulast - kb + 1;
+  const __amdgpu_buffer_rsrc_t ar = rsrc(p.ar + (int64_t)b * p.box * 16, p.box * 16);
+  const int nu64 = (p.U1max + 63) / 64;
+  const __amdgpu_buffer_rsrc_t xr = rsrc(p.lx + (int64_t)b * nu64 * p.Tmax * 16, (int64_t)nu64 * p.Tmax * 16);
+  const int u = tl.u0 + lane;
+  Ext bacc[DM + 1], lacc[DM + 1];  // contributions to (t + d, u) and to (t + d, u + 1)
 #pragma unroll
-  for (int r = 0; r < R; ++r) Tl[r] = u0 + r <= U ? (unsigned)T : 0u;
-  double h[R][S], nb[S];
+  for (int d = 0; d <= DM; ++d) bacc[d] = lacc[d] = ext_zero();
+  Ext lin = ext_zero();
+  for (int q = 0; q < nsteps; ++q) {
+    const int k = kb + q, t = k - u;
+    const bool inl = u <= tl.ulast;
+    const bool act = inl && t >= tl.t0 && t < tl.t1;
+    const bool rep = inl && t >= trl && t < tl.t0;
+    if (lane == 0 && tl.left) lin = act ? load_ext_rec(xr, ((u / 64) * p.Tmax + t) * 16) : ext_zero();
+    Ext v = ext_zero();
+    if (act) v = k == 0 ? ext_one() : ext_add(bacc[0], lin);
+    if (rep) v = load_ext_rec(ar, (int)(rel_pos(p, t, u) * 16));
+    if (act) __builtin_amdgcn_raw_buffer_store_b128(ext_rec(v), ar, (int)(rel_pos(p, t, u) * 16), 0, 0);
+    Ext w[NW];
+    if (act || rep) {
+      ext_weights<DM>(p, b, t, u, T, U, w);
+    } else {
 #pragma unroll
-  for (int s2 = 0; s2 < S; ++s2) {
-    nb[s2] = 0.0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) h[r][s2] = 0.0;
-  }
-  int sc = 0;
-  bool started = false, trouble = false;
-  if (!ALPHA && u0 <= U && U < u0 + R) {
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (u0 + r == U) h[r][S - 1] = 1.0;
-    started = true;
-  }
-  WPlain<DM, R> w;  // the slot-pair-major plain weights of this lane's labels
-  auto load_w = [&](int ks) {
-    const int k = ALPHA ? ks : nsteps - 1 - ks;
-    constexpr int NW = 2 * DM + 1, NP = slot_pairs(NW);
-    const int off = (k * NP * UW + tid) * 16;  // label u0 + r in column r * (UW / R) + tid
-#pragma unroll
-    for (int pr = 0; pr < NP; ++pr) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(wr, off + (pr * UW + r * (UW / R)) * 16, 0, 0);
-        w.v[2 * pr][r] = __builtin_bit_cast(double, ((uint64_t)x.y << 32) | x.x);
-        if (2 * pr + 1 < NW) w.v[2 * pr + 1][r] = __builtin_bit_cast(double, ((uint64_t)x.w << 32) | x.z);
-      }
+      for (int s2 = 0; s2 < NW; ++s2) w[s2] = ext_zero();
     }
-  };
-  load_w(0);
-  for (int k0 = 0; k0 < nsteps; k0 += S) {
 #pragma unroll
-    for (int ph = 0; ph < S; ++ph) {
-      if (ph == 0) {  // keep the lane's largest newest value near 1
-        double big = fabs(h[0][S - 1]);
+    for (int d = 1; d <= DM; ++d) bacc[d] = ext_add(bacc[d], ext_mul(v, w[d - 1]));
 #pragma unroll
-        for (int r = 1; r < R; ++r) big = fmax(big, fabs(h[r][S - 1]));
-        int ex;
-        (void)frexp(big, &ex);
-        sc += ex;
+    for (int d = 0; d <= DM; ++d) lacc[d] = ext_add(lacc[d], ext_mul(v, w[DM + d]));
+    const Ext out = lacc[0];
 #pragma unroll
-        for (int s2 = 0; s2 < S; ++s2) {
-          nb[s2] = ldexp(nb[s2], -ex);
-          trouble |= out_of_range(nb[s2]);
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            h[r][s2] = ldexp(h[r][s2], -ex);
-            trouble |= out_of_range(h[r][s2]);
-          }
-        }
-      }
-      const int ks = k0 + ph;
-      const int k = ALPHA ? ks : nsteps - 1 - ks;
-      const int base = k * WP - diag_ulo(k, T) + u0;
-      double a[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        double c0 = 0.0, c1 = 0.0, c2 = 0.0, c3 = 0.0;
-#pragma unroll
-        for (int d = 1; d <= DM; ++d) {
-          const double x = h[r][(ph - d + 4 * S) % S] * w.v[d - 1][r];
-          if (d & 1) c0 += x; else c1 += x;
-        }
-#pragma unroll
-        for (int d = 0; d <= DM; ++d) {
-          const int sl = (ph - 1 - d + 4 * S) % S;
-          const double src = ALPHA ? (r > 0 ? h[r > 0 ? r - 1 : 0][sl] : nb[sl])
-                                   : (r < R - 1 ? h[r < R - 1 ? r + 1 : 0][sl] : nb[sl]);
-          const double x = src * w.v[DM + d][r];
-          if (d & 1) c3 += x; else c2 += x;
-        }
-        a[r] = (c0 + c1) + (c2 + c3);
-        if (ALPHA && ks == 0 && u0 + r == 0) {
-          a[r] = 1.0;
-          sc = 0;
-          started = true;
-        }
-        if (!((unsigned)(k - u0 - r) < Tl[r])) a[r] = 0.0;
-        trouble |= out_of_range(a[r]);
-      }
-      // the records of the next step, during the exchange (unconditional: past the last
-      // step the offsets fall outside this utterance's records and read zeros)
-      load_w(ks + 1);
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        h[r][ph] = a[r];
-        int ea;
-        const double ma = frexp(a[r], &ea);
-        const int eo = a[r] != 0.0 ? ea + sc : kEZ;
-        const int o = (unsigned)(k - u0 - r) < Tl[r] ? (base + r) * 16 : -16;
-        const uint64_t mb = __builtin_bit_cast(uint64_t, ma);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4v{(uint32_t)mb, (uint32_t)(mb >> 32), (uint32_t)eo, 0u}, xr, o, 0,
-                                               0);
-        started = started || a[r] != 0.0;
-      }
-      // neighbour exchange through LDS
-      const int par = (ks & 1) * 1024;
-      xm[par + tid] = ALPHA ? a[R - 1] : a[0];
-      xe[par + tid] = sc;
-      // barrier on the LDS exchange only: __syncthreads() would also wait for every
-      // outstanding global load, including the prefetches of later steps
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      const int src = ALPHA ? tid - 1 : tid + 1;
-      const bool has = src >= 0 && src < nt;
-      const double m = has ? xm[par + src] : 0.0;
-      const int e = has ? xe[par + src] : 0;
-      {  // an empty lane takes a scale that puts its first input near 1 (the sender's
-         // own scale may be stale at the wavefront, far from the value it sends)
-        int em;
-        (void)frexp(m, &em);  // 0 for a zero
-        if (!started) sc = e + em;
-      }
-      started = started || m != 0.0;
-      nb[ph] = ldexp(m, e - sc);
-      trouble |= m != 0.0 && out_of_range(nb[ph]);
+    for (int d = 0; d < DM; ++d) {
+      bacc[d] = bacc[d + 1];
+      lacc[d] = lacc[d + 1];
     }
+    bacc[DM] = lacc[DM] = ext_zero();
+    if (lane == 63 && tl.right && t >= tl.t0 && t < tl.t1)
+      __builtin_amdgcn_raw_buffer_store_b128(ext_rec(out), xr, (((u + 1) / 64) * p.Tmax + t) * 16, 0, 0);
+    lin = dpp_shift_ext(out, true);
   }
-  trouble = __syncthreads_or(trouble);
-  if (trouble) return true;
-  if (ALPHA) {
-    if (u0 <= U && U < u0 + R) (void)alpha_terminal<DM>(p, b, T, U);
-  } else if (tid == 0) {
-    const int last = (nsteps - 1) % S;
-    double a = h[0][0];
-#pragma unroll
-    for (int s2 = 1; s2 < S; ++s2)
-      if (s2 == last) a = h[0][s2];
-    int ea;
-    const double ma = frexp(a, &ea);
-    beta_final(p, b, a != 0.0 ? Ext{ma, ea + sc} : ext_zero());
-  }
-  return false;
 }
 
-// L2 warm-up for a single-wave sweep: a helper wave touches every 128-byte line of the
-// weight records of the diagonals its chain will reach next, at most kLead diagonals
-// ahead of it (the chain never waits for it).  Loads for kBatch diagonals are issued
-// before any is consumed, so the helper advances kBatch diagonals per memory round trip
-// rather than one.
-constexpr int kLead = 64;
-constexpr int kBatch = 16;
-
-__device__ void l2_warm(const Params& p, int b, int nsteps, bool alpha, int lane, lds_int* prog) {
-  const int64_t dbytes = (int64_t)p.WP * p.RW;  // one diagonal of records
-  const int lines = (int)((dbytes + 127) / 128);
-  const char* base = (alpha ? p.win : p.wout) + (int64_t)b * p.KD * dbytes;
-  uint32_t acc = 0;
-  for (int ks0 = 0; ks0 < nsteps; ks0 += kBatch) {
-    while (ks0 + kBatch - 1 > __hip_atomic_load(prog, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + kLead)
-      __builtin_amdgcn_s_sleep(2);
-    for (int l = lane; l < lines; l += kWave) {
-      uint32_t x[kBatch];
+// Extended-range beta sweep of a tile of at most 64 labels (pull form; the histories of
+// the own label and of the next one are kept aligned to the current step: index d holds
+// the frame d steps ahead).
+template <int DM>
+__device__ void beta_ext(const Params& p, const Tile& tl, int lane, Ext* P00) {
+  constexpr int NW = 2 * DM + 1;
+  const int b = tl.b, T = tl.T, U = tl.U;
+  const int rtop = min(tl.t1 + DM - 1, T);
+  const int kb = rtop + tl.ulast;
+  const int nsteps = kb - (tl.t0 + tl.u0) + 1;
+  const __amdgpu_buffer_rsrc_t br = rsrc(p.br + (int64_t)b * p.box * 16, p.box * 16);
+  const int u = tl.u0 + lane, un = tl.u0 + 64;
+  Ext h[DM + 1], nb[DM + 2];  // h[d] = beta(t + d, u), nb[d] = beta(t - 1 + d, u + 1)
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int ks = ks0 + j < nsteps ? ks0 + j : nsteps - 1;
-        const int k = alpha ? ks : nsteps - 1 - ks;
-        x[j] = *(const uint32_t*)(base + (int64_t)k * dbytes + (int64_t)l * 128);
-      }
+  for (int d = 0; d <= DM; ++d) h[d] = ext_zero();
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) acc += x[j];
+  for (int d = 0; d <= DM + 1; ++d) nb[d] = ext_zero();
+  Ext b00 = ext_zero();
+  for (int q = 0; q < nsteps; ++q) {
+    const int k = kb - q, t = k - u;
+    const bool inl = u <= tl.ulast;
+    const bool act = inl && t >= tl.t0 && t < tl.t1;
+    Ext v = ext_zero();
+    if (act) {
+      Ext w[NW];
+      ext_weights<DM>(p, b, t, u, T, U, w);
+      Ext terms[NW];
+#pragma unroll
+      for (int d = 1; d <= DM; ++d) terms[d - 1] = ext_mul(w[d - 1], h[d]);
+#pragma unroll
+      for (int d = 0; d <= DM; ++d) terms[DM + d] = ext_mul(w[DM + d], nb[d + 1]);
+      v = ext_sum(terms);
+      __builtin_amdgcn_raw_buffer_store_b128(ext_rec(v), br, (int)(rel_pos(p, t, u) * 16), 0, 0);
+      if (k == 0) b00 = v;
+    } else if (t == T && u == U) {
+      v = ext_one();
+    } else if (inl && tl.above && t >= tl.t1 && t < T) {
+      v = load_ext_rec(br, (int)(rel_pos(p, t, u) * 16));
     }
+    // the next label's value on this diagonal: beta(t - 1, u + 1)
+    Ext n = dpp_shift_ext(v, false);
+    if (lane == 63) {
+      const int tn = k - un;
+      n = ext_zero();
+      if (tn == T && un == U) n = ext_one();
+      if (tl.right && tn >= tl.t0 && tn < T) n = load_ext_rec(br, (int)(rel_pos(p, tn, un) * 16));
+    }
+    // step to the diagonal below: frame t - 1 of this label
+#pragma unroll
+    for (int d = DM; d >= 1; --d) h[d] = h[d - 1];
+    h[1] = v;
+#pragma unroll
+    for (int d = DM + 1; d >= 1; --d) nb[d] = nb[d - 1];
+    nb[1] = n;
   }
-  if (acc == 0x9e3779b9u && p.B < 0) p.uok[0] = (int)acc;  // keeps the touching loads alive
+  if (lane == 0 && tl.t0 == 0 && tl.u0 == 0) *P00 = b00;
 }
 
-// Lattice kernel, one work-group per (utterance, direction).  SW (U1max <= 256): 128
-// threads, wave 0 the chain; the plain-float64 sweep where its registers fit
-// (fast_buffers), checked by the agreement of log P from the two directions, and the
-// extended-range sweep (wave 1 keeping its records warm in L2) otherwise or when the
-// check fails.  Longer label sequences: up to 768 threads (1024 for R = 8) with the
-// range-checked multi-wave plain sweep where its registers fit (fast_mw_ok) and the
-// extended-range sweep after it or instead of it.
-template <int DM, int R, bool SW>
-__global__ __launch_bounds__(SW ? 128 : (R <= 4 ? 768 : 1024)) void k_lattice(const Params p) {
-  __shared__ double xm[SW ? 1 : 2 * 1024];
-  __shared__ int xe[SW ? 1 : 2 * 1024];
-  __shared__ unsigned long long s_sumU;
-  __shared__ int s_prog[2];
-  __shared__ double s_lp[2];
-  __shared__ int s_redo;
-  const int b = blockIdx.x >> 1;
-  const int dir = blockIdx.x & 1;  // 0: alpha, 1: beta
-  const bool alpha_side = dir == 0, beta_side = dir == 1;
-  const int tid = threadIdx.x, nt = blockDim.x;
+// Status, reduction weight, log P and the gradient flag of utterance b, by the tile that
+// holds node (0, 0) in the beta direction (after its sweep, P = beta(0, 0)).
+__device__ void finish_utterance(const Params& p, int b, Ext P, int lane) {
   const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
   int status = 0;
   if (T64 < 0 || T64 > p.Tmax) status |= 1;
   if (U64 < 0 || U64 > p.U1max - 1) status |= 2;
   bool bad = false;
-  if (!(status & 2)) {
-    for (int64_t u = tid; u < U64; u += nt) {
+  if (!(status & 2))
+    for (int64_t u = lane; u < U64; u += 64) {
       const int64_t y = p.labels[(int64_t)b * p.lab_stride + u];
       bad |= (y < 0 || y >= p.V);
     }
+  if (__any(bad)) status |= 4;
+  int64_t sumU = 0;
+  if (p.red == 4) {
+    for (int bb = lane; bb < p.B; bb += 64) sumU += p.Ulen[bb];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sumU += __shfl_xor(sumU, o, 64);
   }
-  if (tid == 0) {
-    s_sumU = 0;
-    s_prog[0] = s_prog[1] = -1;
-  }
-  if (__syncthreads_or(bad)) status |= 4;
-  if (beta_side && p.red == 4) {
-    unsigned long long part = 0;
-    for (int bb = tid; bb < p.Btot; bb += nt) part += (unsigned long long)p.Ulen_tot[bb];
-    if (part) atomicAdd(&s_sumU, part);
-  }
-  __syncthreads();
-  if (beta_side && tid == 0) p.wts[b] = reduction_weight(p, b, (int64_t)s_sumU);
-  const int T = (int)T64, U = (int)U64;
-  if (status != 0 || T == 0) {
-    if (tid == 0) {
-      if (beta_side) {
-        p.logp[b] = status ? __builtin_nan("") : -__builtin_inf();
-        p.pm[b] = 0.0;
-        p.pe[b] = kEZ;
-        p.uok[b] = 0;
-        if (p.ustatus) p.ustatus[b] = status ? status : 8;
-      }
-      if (alpha_side) p.logpa[b] = status ? __builtin_nan("") : -__builtin_inf();
-    }
+  if (lane != 0) return;
+  p.wts[b] = reduction_weight(p, b, sumU);
+  if (status != 0 || T64 == 0) {
+    p.logp[b] = status ? __builtin_nan("") : -__builtin_inf();
+    p.pm[b] = 0.0;
+    p.pe[b] = kEZ;
+    p.uok[b] = 0;
+    if (p.ustatus) p.ustatus[b] = status ? status : 8;
     return;
   }
-  if constexpr (SW) {
-    // one direction per work-group: wave 0 runs the chain, wave 1 keeps the records of
-    // the extended-range sweep warm in L2
-    const int wv = tid >> 6, lane = tid & (kWave - 1);
-    lds_int* prog = (lds_int*)&s_prog[0];
-    if constexpr (fast_buffers<DM, R>() > 0) {
-      if (!p.xflag[b] && p.pwin) {
-        if (wv == 0) {
-          if (alpha_side) sweep_fast<DM, R, true>(p, b, T, U, lane, &s_lp[0]);
-          else sweep_fast<DM, R, false>(p, b, T, U, lane, &s_lp[0]);
-        }
-        __syncthreads();
-        // The direction that finishes second compares the two log P values (both sum
-        // the same probability mass; rounding alone stays below 1e-12) and, unless both
-        // are finite and differ by at most 1e-9, redoes both directions with the
-        // extended-range sweep: mass lost to underflow differs between the directions, and
-        // when it is all of it both read -inf, which only the extended sweep can tell
-        // from an utterance without alignments.  The counter was zeroed by the
-        // row-statistics pass of this call.
-        if (tid == 0) {
-          __hip_atomic_store(p.lpx + 2 * b + dir, s_lp[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const int old = __hip_atomic_fetch_add(p.lcnt + b, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-          int redo = 0;
-          if (old == 1) {
-            const double other =
-                __hip_atomic_load(p.lpx + 2 * b + (dir ^ 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const double mine = s_lp[0];
-            redo = (isfinite(mine) && isfinite(other) && fabs(mine - other) <= 1e-9) ? 0 : 1;
-          }
-          s_redo = redo;
-        }
-        __syncthreads();
-        if (!s_redo) return;
-        for (int pass = 0; pass < 2; ++pass) {
-          if (tid == 0) s_prog[0] = -1;
-          __syncthreads();
-          if (wv == 0) {
-            if (pass == 0) sweep<DM, R, true, true>(p, b, T, U, lane, xm, xe, prog);
-            else sweep<DM, R, true, false>(p, b, T, U, lane, xm, xe, prog);
-          } else {
-            l2_warm(p, b, T + U, pass == 0, lane, prog);
-          }
-          __syncthreads();
-        }
-        return;
-      }
-    }
-    if (wv == 0) {
-      if (alpha_side) sweep<DM, R, true, true>(p, b, T, U, lane, xm, xe, prog);
-      else sweep<DM, R, true, false>(p, b, T, U, lane, xm, xe, prog);
-    } else {
-      l2_warm(p, b, T + U, alpha_side, lane, prog);
-    }
-  } else {
-    if constexpr (fast_mw_ok<DM, R>()) {
-      if (!p.xflag[b] && p.pwin) {
-        const bool trouble = dir == 0 ? sweep_fast_mw<DM, R, true>(p, b, T, U, tid, xm, xe)
-                                      : sweep_fast_mw<DM, R, false>(p, b, T, U, tid, xm, xe);
-        if (!trouble) return;
-        __syncthreads();  // the exchange arrays are reused below
-      }
-    }
-    if (dir == 0)
-      sweep<DM, R, false, true>(p, b, T, U, tid, xm, xe, (lds_int*)&s_prog[0]);
-    else
-      sweep<DM, R, false, false>(p, b, T, U, tid, xm, xe, (lds_int*)&s_prog[0]);
+  const double lp = ext_log(P);
+  p.logp[b] = lp;
+  p.pm[b] = P.m;
+  p.pe[b] = P.e;
+  p.uok[b] = (P.m > 0.0 && lp == lp) ? 1 : 0;
+  if (p.ustatus) p.ustatus[b] = (P.m > 0.0 || lp != lp) ? 0 : 8;
+}
+
+// Tiles of band `band` (i + j = band for alpha, counted from the far corner for beta):
+// one 64-lane work-group per (tile, utterance, direction).  R labels per lane (R = 2 only
+// for a single tile); BOUND: tiles with neighbours (band tiles of 64 labels).  The plain
+// sweep runs unless the utterance has move weights outside [2^-300, 2^300] or the plain
+// weights are not stored; a tile whose plain sweep went out of range is redone in
+// extended range, one 64-label strip after another.
+template <int DM, int R, bool BOUND>
+__global__ __launch_bounds__(64) void k_tiles(const Params p, int band) {
+  const int lane = threadIdx.x;
+  const int ilo = max(0, band - (p.nU - 1)), ihi = min(band, p.nT - 1);
+  const int ntile = ihi - ilo + 1;
+  const int m = blockIdx.x % ntile, rest = blockIdx.x / ntile;
+  const int dir = rest & 1, b = rest >> 1;
+  int i = ilo + m, j = band - i;
+  if (dir == 1) {
+    i = p.nT - 1 - i;
+    j = p.nU - 1 - j;
   }
+  const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
+  Ext P = ext_zero();
+  if (utt_dims_ok(p, T64, U64)) {
+    const int T = (int)T64, U = (int)U64;
+    Tile tl;
+    if (make_tile(p, b, T, U, i, j, 64 * R, tl)) {
+      bool redo = true;
+      if constexpr (plain_buffers<DM, R>() >= 2) {
+        if (p.pw && !p.xflag[b]) redo = dir == 0 ? alpha_plain<DM, R, BOUND>(p, tl, lane)
+                                                 : beta_plain<DM, R, BOUND>(p, tl, lane, &P);
+      }
+      // the sweeps run as one wavefront across the lanes: the whole wave redoes the tile
+      // when any lane saw a value out of range
+      if (__any(redo)) {
+        // extended range, 64-label strips in dependency order (the strips of one tile
+        // exchange through lx / br within this wave: stores complete before the next
+        // strip's loads, which bypass the vector L1)
+        for (int s = 0; s < R; ++s) {
+          const int sj = dir == 0 ? s : R - 1 - s;
+          Tile st = tl;
+          st.u0 = tl.u0 + 64 * sj;
+          if (st.u0 > U) continue;
+          st.ulast = min(st.u0 + 63, U);
+          st.left = st.u0 > 0;
+          st.right = st.ulast < U;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+          if (dir == 0) alpha_ext<DM>(p, st, lane);
+          else beta_ext<DM>(p, st, lane, &P);
+        }
+      }
+    }
+  }
+  if (dir == 1 && i == 0 && j == 0) finish_utterance(p, b, P, lane);
 }
 
 // ------------------------------------------------------------------------------------
@@ -973,58 +892,59 @@ __device__ void reduce_loss(const Params& p) {
   if (p.red != 0) p.loss[0] = (float)s;
 }
 
+// alpha / beta record of a node, normalised (the plain sweeps store unnormalised values)
+__device__ __forceinline__ Ext xrec_get(const char* base, int64_t pos) {
+  const char* r = base + pos * 16;
+  return ext_norm(*(const double*)r, *(const int*)(r + 8));
+}
+
 // A group of NG lanes works on one node (as in the node weights): lane d handles the
 // blank and the label move of duration value d; the group sums give O, c_blank, c_label.
 // The first work-group also reduces the loss (the lattice has finished every log P) unless
-// the call writes no loss.  An upstream gradient (chain rule) scales w_b.
+// the call writes no loss.  An upstream gradient (chain rule) scales w_b.  The record of
+// the gradient pass overwrites the node's log-domain ingredients.
 template <int DM>
 __global__ __launch_bounds__(256) void k_coef(const Params p) {
-  constexpr int NW = 2 * DM + 1;
-  constexpr int NG = DM < 8 ? 8 : (DM < 16 ? 16 : 32);
+  constexpr int NG = group_lanes(DM);
   if (p.loss && blockIdx.x == 0 && threadIdx.x == 0) reduce_loss(p);
   const int64_t gt = (int64_t)xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
   const int j = threadIdx.x & (NG - 1);
-  const int64_t g = gt / NG;
-  const int64_t per = (int64_t)p.KD * p.WP;
-  const int b = (int)(g / per);
-  // whole groups leave together below: every condition depends on the position only
-  if (b >= p.B) return;
+  int b, k, i;
+  // whole groups leave together below: every condition depends on the node only
+  if (!box_node(p, gt / NG, b, k, i)) return;
   // the three per-utterance words in one round trip (an ok utterance has valid lengths)
   const int ok = p.uok[b];
   const int T = (int)p.Tlen[b], U = (int)p.Ulen[b];
   if (!ok) return;
-  const int64_t rem = g - (int64_t)b * per;
-  const int k = (int)(rem / p.WP);
-  const int i = (int)(rem - (int64_t)k * p.WP);
-  if (k >= T + U) return;
-  const int u = diag_ulo(k, T) + i;
-  if (u > min(k, U)) return;
-  const int t = k - u;
-  const int64_t pos = node_pos(p, b, k, i);
+  const int u = diag_ulo(p, k) + i, t = k - u;
+  if (t >= T || u > U) return;
+  const int64_t pos = (int64_t)b * p.box + diag_off(p, k) + i;
 
   const Ext a = xrec_get(p.ar, pos);
-  const char* wr = wrec(p.wout, p, pos);
+  double* lgp = p.lg + pos * p.LG;
+  const double lb = lgp[0], ly = lgp[1];
+  const int d = j;
+  const int idx = d <= DM ? p.didx[d] : -1;
+  const double lam = idx >= 0 ? lgp[2 + idx] : -__builtin_inf();
   const double Pm = p.pm[b];
   const int Pe = p.pe[b];
-  const int d = j;
   double gb = 0.0, gy = 0.0;  // posteriors of the blank / label move of duration d
-  if (d <= DM) {
+  if (idx >= 0) {
     if (d >= 1) {
       Ext bt = ext_zero();
-      if (t + d < T) {
-        const int k2 = k + d;
-        bt = xrec_get(p.br, node_pos(p, b, k2, u - diag_ulo(k2, T)));
-      } else if (t + d == T && u == U) {
-        bt = ext_one();
+      if (t + d < T) bt = xrec_get(p.br, node_pos(p, b, t + d, u));
+      else if (t + d == T && u == U) bt = ext_one();
+      if (bt.m != 0.0) {
+        const Ext gm = ext_mul(ext_mul(a, ext_exp(lb + lam)), bt);
+        gb = ext_to_double(Ext{gm.m / Pm, gm.e - Pe});
       }
-      const Ext gm = ext_mul(ext_mul(a, wrec_get(wr, NW, d - 1)), bt);
-      gb = ext_to_double(Ext{gm.m / Pm, gm.e - Pe});
     }
     if (u < U && t + d < T) {
-      const int k2 = k + d + 1;
-      const Ext bt = xrec_get(p.br, node_pos(p, b, k2, u + 1 - diag_ulo(k2, T)));
-      const Ext gm = ext_mul(ext_mul(a, wrec_get(wr, NW, DM + d)), bt);
-      gy = ext_to_double(Ext{gm.m / Pm, gm.e - Pe});
+      const Ext bt = xrec_get(p.br, node_pos(p, b, t + d, u + 1));
+      if (bt.m != 0.0) {
+        const Ext gm = ext_mul(ext_mul(a, ext_exp(ly + lam)), bt);
+        gy = ext_to_double(Ext{gm.m / Pm, gm.e - Pe});
+      }
     }
   }
   double cb = gb, cl = gy;
@@ -1035,14 +955,15 @@ __global__ __launch_bounds__(256) void k_coef(const Params p) {
   }
   const double O = cb + cl;
   const double wgt = p.gscale ? p.wts[b] * (double)p.gscale[p.red == 0 ? b : 0] : p.wts[b];
-  const double* pr = p.pr + pos * p.NPR;
-  float* rec = p.rec + pos * p.RS;
+  // softmax(h)_blank, softmax(h)_label (sigma added back) and softmax(g)_d
+  const double sb = exp(lb + p.sigma), sy = exp(ly + p.sigma), sgd = exp(lam);
+  float* rec = (float*)lgp;  // every lane of the group has read the ingredients above
   if (j == 0) {
-    const float4 rs = p.rstat[pos];
+    const float2 rs = p.stat[pos];
     int y = -1;
     if (u < U) y = (int)p.labels[(int64_t)b * p.lab_stride + u];
-    double Gb = wgt * (O * pr[0] - cb);
-    const double Gy = wgt * (O * pr[1] - cl);
+    double Gb = wgt * (O * sb - cb);
+    const double Gy = wgt * (O * sy - cl);
     if (y == p.blank) {  // both corrections land on the blank column
       Gb -= wgt * cl;
       y = -1;
@@ -1059,10 +980,7 @@ __global__ __launch_bounds__(256) void k_coef(const Params p) {
     rec[3] = (float)Gy;
     rec[4] = __int_as_float(y);
   }
-  if (d <= DM) {
-    const int idx = p.didx[d];
-    if (idx >= 0) rec[5 + idx] = (float)(wgt * (O * pr[2 + d] - (gb + gy)));
-  }
+  if (idx >= 0) rec[5 + idx] = (float)(wgt * (O * sgd - (gb + gy)));
 }
 
 __global__ void k_reduce(const Params p) {
@@ -1072,53 +990,41 @@ __global__ void k_reduce(const Params p) {
 // ------------------------------------------------------------------------------------
 // Launchers
 template <int DM>
-static hipError_t launch_lattice_dm(const Params& p, hipStream_t st) {
-  const int u1 = p.U1max;
-  const dim3 grid(2 * p.B);  // one work-group per (utterance, direction)
-  if (u1 <= 64) {
-    hipLaunchKernelGGL((k_lattice<DM, 1, true>), grid, dim3(128), 0, st, p);
-  } else if (u1 <= 128) {
-    hipLaunchKernelGGL((k_lattice<DM, 2, true>), grid, dim3(128), 0, st, p);
-  } else if (u1 <= 256) {
-    hipLaunchKernelGGL((k_lattice<DM, 4, true>), grid, dim3(128), 0, st, p);
-  } else {
-    // at most 768 threads for R <= 4 (about 170 VGPRs per lane), 1024 for R = 8
-    int R = u1 <= 768 ? 1 : u1 <= 1536 ? 2 : u1 <= 3072 ? 4 : 8;
-    const int nt = ((u1 + R - 1) / R + 63) / 64 * 64;
-    switch (R) {
-      case 1: hipLaunchKernelGGL((k_lattice<DM, 1, false>), grid, dim3(nt), 0, st, p); break;
-      case 2: hipLaunchKernelGGL((k_lattice<DM, 2, false>), grid, dim3(nt), 0, st, p); break;
-      case 4: hipLaunchKernelGGL((k_lattice<DM, 4, false>), grid, dim3(nt), 0, st, p); break;
-      default: hipLaunchKernelGGL((k_lattice<DM, 8, false>), grid, dim3(nt), 0, st, p); break;
-    }
+static hipError_t launch_bands(const Params& p, hipStream_t st) {
+  const bool banded = p.nT > 1 || p.nU > 1;
+  for (int band = 0; band < p.nT + p.nU - 1; ++band) {
+    const int ilo = band - (p.nU - 1) > 0 ? band - (p.nU - 1) : 0;
+    const int ihi = band < p.nT - 1 ? band : p.nT - 1;
+    const dim3 grid((unsigned)((ihi - ilo + 1) * 2 * p.B));
+    if (banded) hipLaunchKernelGGL((k_tiles<DM, 1, true>), grid, dim3(64), 0, st, p, band);
+    else if (DM == 4 && p.R == 2) hipLaunchKernelGGL((k_tiles<4, 2, false>), grid, dim3(64), 0, st, p, band);
+    else hipLaunchKernelGGL((k_tiles<DM, 1, false>), grid, dim3(64), 0, st, p, band);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_lattice_side(const Params& p, int which, hipStream_t st) {
-  const int64_t n = (int64_t)p.B * p.KD * p.WP;
-  const dim3 grid((unsigned)((n + 255) / 256));
+  // node groups over the diagonal bounding box of the padded box
+  const int64_t n = (int64_t)p.B * p.KD * p.A;
+  const int ng = group_lanes(p.DM);
+  const dim3 gridg((unsigned)((n * ng + 255) / 256));
   switch (which) {
-    case 0: {  // node weights: NG lanes per position
-      const int ng = p.DM < 8 ? 8 : (p.DM < 16 ? 16 : 32);
-      const dim3 gridw((unsigned)((n * ng + 255) / 256));
-      if (p.DM == 4) hipLaunchKernelGGL((k_node_weights<4>), gridw, dim3(256), 0, st, p);
-      else if (p.DM == 8) hipLaunchKernelGGL((k_node_weights<8>), gridw, dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((k_node_weights<16>), gridw, dim3(256), 0, st, p);
+    case 0:  // node weights
+      if (p.DM == 4) hipLaunchKernelGGL((k_node_weights<4>), gridg, dim3(256), 0, st, p);
+      else if (p.DM == 8) hipLaunchKernelGGL((k_node_weights<8>), gridg, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((k_node_weights<16>), gridg, dim3(256), 0, st, p);
       return hipGetLastError();
-    }
-    case 1:  // lattice
-      if (p.DM == 4) return launch_lattice_dm<4>(p, st);
-      if (p.DM == 8) return launch_lattice_dm<8>(p, st);
-      return launch_lattice_dm<16>(p, st);
-    case 2: {  // coefficients (and the loss reduction): NG lanes per position
-      const int ng = p.DM < 8 ? 8 : (p.DM < 16 ? 16 : 32);
-      const dim3 gridc((unsigned)((n * ng + 255) / 256));
-      if (p.DM == 4) hipLaunchKernelGGL((k_coef<4>), gridc, dim3(256), 0, st, p);
-      else if (p.DM == 8) hipLaunchKernelGGL((k_coef<8>), gridc, dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((k_coef<16>), gridc, dim3(256), 0, st, p);
+    case 1:  // lattice: the bands of tiles
+      if (p.DM == 4) return launch_bands<4>(p, st);
+      if (p.DM == 8) return launch_bands<8>(p, st);
+      return launch_bands<16>(p, st);
+    case 2:  // coefficients (and the loss reduction)
+      if (p.DM == 4) hipLaunchKernelGGL((k_coef<4>), gridg, dim3(256), 0, st, p);
+      else if (p.DM == 8) hipLaunchKernelGGL((k_coef<8>), gridg, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((k_coef<16>), gridg, dim3(256), 0, st, p);
       return hipGetLastError();
-    }
     default:  // loss reduction over the whole batch
       hipLaunchKernelGGL(k_reduce, dim3(1), dim3(64), 0, st, p);
       return hipGetLastError();

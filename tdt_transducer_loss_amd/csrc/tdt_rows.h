@@ -118,7 +118,7 @@ __device__ __forceinline__ float expo(float x, float c) {
 
 // Partial log-sum-exp of one row segment.  Writes, per (node, segment):
 //   part[2*seg] = c, part[2*seg + 1] = sum 2^expo(h, c)
-// (floats, in a [positions][2*nseg] array), and the blank / label logits into rstat.
+// (floats, in a [positions][2*nseg] array), and the blank / label logits into stat.
 // A segment is NCH windows of 64 16-byte chunks, one chunk per lane per window; windows
 // that hold no chunk of the row are skipped.  The first and the last chunk of the row
 // (which may hold elements of other rows) are left out of the chunk windows and read
@@ -129,18 +129,14 @@ __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
   using ET = typename TI::T;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (blockIdx.x == 0)  // flags the node-weight kernel and the lattice of this call set
-    for (int i = threadIdx.x; i < p.B; i += blockDim.x) {
-      p.xflag[i] = 0;
-      p.lcnt[i] = 0;
-    }
+  if (blockIdx.x == 0)  // the flags the node-weight kernel of this call sets
+    for (int i = threadIdx.x; i < p.B; i += blockDim.x) p.xflag[i] = 0;
   // persistent: a fixed grid of waves walks the (node, segment) space of the padded
   // [B, Tmax, U1max] rows in memory order, skipping nodes outside their utterance in a
   // few instructions (ragged batches leave most of the padded space empty); the host
   // keeps this space below 2^31
   const uint32_t nseg = (uint32_t)p.nseg;
   const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
-  const int64_t dper = (int64_t)p.KD * p.WP;  // lattice positions per utterance
   const uint32_t total = (uint32_t)p.B * per * nseg;
   const uint32_t stride = gridDim.x * kWavesPerBlock;
   for (uint32_t g = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv; g < total; g += stride) {
@@ -154,9 +150,8 @@ __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
     if (!utt_dims_ok(p, T64, U64)) continue;
     const int T = (int)T64, U = (int)U64;
     if (t >= T || u > U) continue;
-    const int k = t + u;
-    // its lattice position (b, k, i): the anti-diagonal layout of the workspace
-    const uint32_t rem = (uint32_t)k * (uint32_t)p.WP + (uint32_t)(u - diag_ulo(k, T));
+    // its position in the diagonal-major workspace layout
+    const int64_t pos = node_pos(p, (int)b, t, u);
 
     const int V = p.V;
     const ET* row = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
@@ -186,16 +181,16 @@ __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
     else if (lane - eh < et) xe = TI::load(row, V - et + (lane - eh));
     // the blank and label logits, by the segment that holds their chunk
     const int seg_span = 64 * NCH;
-    float4* rs = p.rstat + rem + (int64_t)b * dper;
+    float* rs = (float*)(p.stat + pos);
     if (lane == 0) {
-      if ((rc.head + p.blank) / EPC / seg_span == seg) ((float*)rs)[2] = TI::load(row, p.blank);
+      if ((rc.head + p.blank) / EPC / seg_span == seg) rs[0] = TI::load(row, p.blank);
       int y = -1;
       if (u < U) {
         const int64_t yy = p.labels[(int64_t)b * p.lab_stride + u];
         if (yy >= 0 && yy < V) y = (int)yy;
       }
       if (y >= 0 ? (rc.head + y) / EPC / seg_span == seg : seg == 0)
-        ((float*)rs)[3] = y >= 0 ? TI::load(row, y) : -__builtin_inff();
+        rs[1] = y >= 0 ? TI::load(row, y) : -__builtin_inff();
     }
     // chunk 0, chunk nch-1 and chunks past the row hold no element for the windows
 #pragma unroll
@@ -255,7 +250,7 @@ __global__ __launch_bounds__(256) void k_row_partial(const Params p) {
     // 16-bit logits beyond about 2.3e38 in magnitude leave no float shift: NaN partial
     if (!empty && !(__builtin_fabsf(c) < __builtin_inff())) S = __builtin_nan("");
     if (lane == 0) {
-      float* part = p.part + ((int64_t)rem + (int64_t)b * dper) * 2 * nseg + 2 * seg;
+      float* part = p.part + (pos * nseg + seg) * 2;
       part[0] = empty ? -__builtin_inff() : c;
       part[1] = (float)S;
     }
@@ -272,7 +267,7 @@ template <typename TI, int NCH>
 struct RowTask {
   bool ok;  // a node of its utterance's lattice (wave-uniform)
   int seg, c0, nwin, nch;
-  uint32_t b, rem;  // utterance and lattice position (anti-diagonal workspace layout)
+  int64_t pos;      // workspace position of the node
   uint4 v[NCH];
   float xe;
 };
@@ -296,11 +291,9 @@ __device__ __forceinline__ void row_task_load(const Params& p, uint32_t g, uint3
   if (!utt_dims_ok(p, T64, U64)) return;
   const int T = (int)T64, U = (int)U64;
   if (t >= T || u > U) return;
-  const int k = t + u;
   tk.ok = true;
   tk.seg = seg;
-  tk.b = b;
-  tk.rem = (uint32_t)k * (uint32_t)p.WP + (uint32_t)(u - diag_ulo(k, T));
+  tk.pos = node_pos(p, (int)b, t, u);
   const int V = p.V;
   const ET* row = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
   const RowCover rc = row_cover<TI>(row, V);
@@ -326,16 +319,16 @@ __device__ __forceinline__ void row_task_load(const Params& p, uint32_t g, uint3
   if (lane < eh) tk.xe = TI::load(row, lane);
   else if (lane - eh < et) tk.xe = TI::load(row, V - et + (lane - eh));
   const int seg_span = 64 * NCH;
-  float4* rs = p.rstat + tk.rem + (int64_t)b * p.KD * p.WP;
+  float* rs = (float*)(p.stat + tk.pos);
   if (lane == 0) {
-    if ((rc.head + p.blank) / EPC / seg_span == seg) ((float*)rs)[2] = TI::load(row, p.blank);
+    if ((rc.head + p.blank) / EPC / seg_span == seg) rs[0] = TI::load(row, p.blank);
     int y = -1;
     if (u < U) {
       const int64_t yy = p.labels[(int64_t)b * p.lab_stride + u];
       if (yy >= 0 && yy < V) y = (int)yy;
     }
     if (y >= 0 ? (rc.head + y) / EPC / seg_span == seg : seg == 0)
-      ((float*)rs)[3] = y >= 0 ? TI::load(row, y) : -__builtin_inff();
+      rs[1] = y >= 0 ? TI::load(row, y) : -__builtin_inff();
   }
 }
 
@@ -400,7 +393,7 @@ __device__ __forceinline__ void row_task_finish(const Params& p, int lane, RowTa
   double S = wave_sum_dpp((double)acc);
   if (!empty && !(__builtin_fabsf(c) < __builtin_inff())) S = __builtin_nan("");
   if (lane == 0) {
-    float* part = p.part + ((int64_t)tk.rem + (int64_t)tk.b * p.KD * p.WP) * 2 * p.nseg + 2 * tk.seg;
+    float* part = p.part + (tk.pos * p.nseg + tk.seg) * 2;
     part[0] = empty ? -__builtin_inff() : c;
     part[1] = (float)S;
   }
@@ -410,11 +403,8 @@ template <typename TI, int NCH>
 __global__ __launch_bounds__(256) void k_row_partial2(const Params p) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (blockIdx.x == 0)  // flags the node-weight kernel and the lattice of this call set
-    for (int i = threadIdx.x; i < p.B; i += blockDim.x) {
-      p.xflag[i] = 0;
-      p.lcnt[i] = 0;
-    }
+  if (blockIdx.x == 0)  // the flags the node-weight kernel of this call sets
+    for (int i = threadIdx.x; i < p.B; i += blockDim.x) p.xflag[i] = 0;
   const uint32_t total = (uint32_t)p.B * (uint32_t)p.Tmax * (uint32_t)p.U1max * (uint32_t)p.nseg;
   const uint32_t stride = gridDim.x * kWavesPerBlock;
   for (uint32_t g = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv; g < total; g += 2 * stride) {
@@ -476,8 +466,7 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
   if (ok) {
     if (t < T && u <= U) {
       valid = true;
-      const int k = t + u;
-      rec = p.rec + node_pos(p, b, k, u - diag_ulo(k, T)) * p.RS;
+      rec = (const float*)(p.lg + node_pos(p, (int)b, t, u) * p.LG);
       A = rec[0];
       m = rec[1];
       Gb = rec[2];

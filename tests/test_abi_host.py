@@ -38,7 +38,7 @@ def test_status_strings():
     for code in range(0, -7, -1):
         assert _native.status_string(code) != "unknown status"
     assert _native.status_string(-99) == "unknown status"
-    assert _native.lib().tdt_loss_abi_version() == 2
+    assert _native.lib().tdt_loss_abi_version() == 3
 
 
 def test_workspace_size():
@@ -49,8 +49,10 @@ def test_workspace_size():
     for bad in ([], [0], [1, 1], [-1, 1], [0, 17]):
         with pytest.raises(ValueError):
             _native.workspace_size(0, 1, 10, 5, 17, bad)
-    with pytest.raises(ValueError):
-        _native.workspace_size(0, 1, 10, 8193, 17, [0, 1])
+    # no label-count limit: a long label sequence only needs its workspace
+    assert _native.workspace_size(0, 1, 10, 20000, 17, [0, 1]) > 0
+    with pytest.raises(ValueError):  # one utterance's box beyond 2^27 nodes
+        _native.workspace_size(0, 1, 20000, 20000, 17, [0, 1])
     with pytest.raises(ValueError):
         _native.workspace_size(0, 0, 10, 5, 17, [0, 1])
     with pytest.raises(ValueError):
@@ -84,7 +86,7 @@ def _call(**over):
     (dict(durations=[0, 0, 1]), _native.TDT_ERR_INVALID_ARGUMENT),
     (dict(durations=[0], D=1), _native.TDT_ERR_INVALID_ARGUMENT),
     (dict(durations=[0, 1, 99]), _native.TDT_ERR_UNSUPPORTED),
-    (dict(U1_max=9000, lab_stride=9000), _native.TDT_ERR_UNSUPPORTED),
+    (dict(T_max=20000, U1_max=9000, lab_stride=9000), _native.TDT_ERR_UNSUPPORTED),
     (dict(lab_stride=2), _native.TDT_ERR_BAD_STRIDE),
     (dict(glog=FAKE), _native.TDT_ERR_INVALID_ARGUMENT),  # one gradient pointer without the other
     (dict(), _native.TDT_ERR_WORKSPACE_TOO_SMALL),          # ws_bytes = 0
@@ -190,3 +192,21 @@ def test_noalloc_scratch_size_matches_header():
 ])
 def test_noalloc_host_checks(over, code):
     assert _noalloc(**over) == code
+
+
+def test_workspace_is_small_next_to_the_logits():
+    """The workspace holds per-node records of the padded box only (no per-diagonal
+    bounding box, one plain weight record per node): at most 10% of the logits on the
+    ragged fp16 batch and 20% on the long-label bf16 batch."""
+    import sys
+    sys.path.insert(0, ROOT)
+    from tdt_inputs import CONFIGS
+
+    for cid, limit in ((3, 0.10), (4, 0.20)):
+        c = CONFIGS[cid]
+        T = c.get("Tmax", max(c.get("T", [0])))
+        U1 = c.get("U1max", max(c.get("U", [0])) + 1)
+        dt = {"f32": 0, "f16": 1, "bf16": 2}[c["dtype"]]
+        ws = _native.workspace_size(dt, c["B"], T, U1, c["V"], c["durations"])
+        logits = c["B"] * T * U1 * (c["V"] + len(c["durations"])) * (4 if dt == 0 else 2)
+        assert ws <= limit * logits, (c["name"], ws, logits)

@@ -45,4 +45,10 @@ def test_lattice_variant(dm, U):
 
 @pytest.mark.parametrize("U", LABELS)
 def test_lattice_variant_extended_range(U):
-    _parity(_case(4 if U % 2 == 0 else 8, U, "f32", scale=400.0, seed=200 + U).to("cuda"))
+    _parity(_case(4 if LABELS.index(U) % 2 == 0 else 8, U, "f32", scale=400.0, seed=200 + U).to("cuda"))
+
+
+def test_more_than_8192_labels():
+    """9000 labels in 12 frames (label moves of duration 0): 141 bands of 64-label tiles."""
+    case = make_case(2, [12, 9], [9000, 8100], 9, [0, 1, 2], "f32", seed=300, sigma=0.02, reduction="mean")
+    _parity(case.to("cuda"))
