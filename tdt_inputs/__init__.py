@@ -8,11 +8,12 @@ columns are duration logits (the layout of the joint output of a Parakeet-TDT mo
 read in place as two slices, as the page "tdt-loss: add TDT loss kernel" describes
 for ``logits[..., :V]``).
 
-Draw order per case: lengths (ragged cases only), then labels, then logits.  Logits
-are float32 ``standard_normal * scale`` rounded to the storage dtype by torch's
-round-to-nearest-even cast; padded nodes hold random values too.  The same tensor
-(copied to the host when needed) feeds the GPU path and the oracle, so both sides see
-identical bits.
+Draw order per case: lengths (ragged cases only) and labels from a seeded CPU generator
+(so they, and the byte count of a ragged batch, are the same on every machine), then
+logits from a generator on the target device seeded with seed + 1 (float32
+``standard_normal * scale`` rounded to the storage dtype by torch's round-to-nearest-even
+cast; padded nodes hold random values too).  The same tensor (copied to the host when
+needed) feeds the GPU path and the oracle, so both sides see identical bits.
 """
 from __future__ import annotations
 
@@ -94,26 +95,29 @@ def make_case(B, T, U, V, durations, dtype="f32", *, scale=1.0, sigma=0.0, reduc
     V - 1; labels are uniform in [0, label_high) with label_high defaulting to the blank id
     when the blank is the last class.  ``extra_cols`` appends unused columns after the
     duration logits (a wider joint row)."""
-    gen = torch.Generator(device=device)
-    gen.manual_seed(int(seed))
+    cgen = torch.Generator(device="cpu")
+    cgen.manual_seed(int(seed))
     blank = V - 1 if blank is None else blank
     D = len(durations)
     if T is None:
         lo, hi = T_range
-        T_t = torch.randint(lo, hi + 1, (B,), generator=gen, device=device, dtype=torch.int64)
+        T_t = torch.randint(lo, hi + 1, (B,), generator=cgen, dtype=torch.int64)
         ulo, uhi = U_range
-        U_t = torch.randint(ulo, uhi + 1, (B,), generator=gen, device=device, dtype=torch.int64)
+        U_t = torch.randint(ulo, uhi + 1, (B,), generator=cgen, dtype=torch.int64)
         U_t = torch.minimum(U_t, 2 * T_t)
     else:
-        T_t = torch.tensor(list(T), dtype=torch.int64, device=device)
-        U_t = torch.tensor(list(U), dtype=torch.int64, device=device)
+        T_t = torch.tensor(list(T), dtype=torch.int64)
+        U_t = torch.tensor(list(U), dtype=torch.int64)
     Tmax = int(T_t.max().item()) if Tmax is None else Tmax
     U1max = int(U_t.max().item()) + 1 if U1max is None else U1max
     Lmax = max(U1max - 1, 1)
     high = (blank if blank == V - 1 else V) if label_high is None else label_high
-    labels = torch.randint(0, high, (B, Lmax), generator=gen, device=device, dtype=torch.int64)
-    pos = torch.arange(Lmax, device=device)[None, :]
+    labels = torch.randint(0, high, (B, Lmax), generator=cgen, dtype=torch.int64)
+    pos = torch.arange(Lmax)[None, :]
     labels = torch.where(pos < U_t[:, None], labels, torch.full_like(labels, -100))
+    T_t, U_t, labels = T_t.to(device), U_t.to(device), labels.to(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) + 1)
     C = V + D + extra_cols
     joint = torch.empty((B, Tmax, U1max, C), dtype=_DT[dtype], device=device)
     for b in range(B):

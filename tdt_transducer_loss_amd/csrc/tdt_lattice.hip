@@ -278,18 +278,21 @@ struct DiagCursor {
     ulo = diag_ulo(p, k0);
     len = diag_len(p, k0);
   }
+  // sign bit of x as 0 / 1
+  static __device__ __forceinline__ int neg(int x) { return (int)((unsigned)x >> 31); }
   __device__ __forceinline__ void next(const Params& p) {  // k -> k + 1
     off += len;
     ++k;
-    const int up = k < p.U1max ? 1 : 0, lo = k >= p.Tmax ? 1 : 0;  // gains a node at the top, loses one at t = Tmax
-    len += up - lo;
+    // the diagonal gains a node at the top while k < U1max, loses one at t = Tmax once k >= Tmax
+    const int lo = 1 - neg(k - p.Tmax);
+    len += neg(k - p.U1max) - lo;
     ulo += lo;
   }
   __device__ __forceinline__ void prev(const Params& p) {  // k -> k - 1
-    --k;
-    const int up = k + 1 < p.U1max ? 1 : 0, lo = k + 1 >= p.Tmax ? 1 : 0;
-    len -= up - lo;
+    const int lo = 1 - neg(k - p.Tmax);
+    len -= neg(k - p.U1max) - lo;
     ulo -= lo;
+    --k;
     off -= len;
   }
   // first 16-byte entry of the diagonal's plain-weight block
@@ -394,6 +397,10 @@ __device__ bool alpha_plain(const Params& p, const Tile& tl, int lane) {
 #pragma unroll
     for (int r = 0; r < R; ++r) bacc[r][s] = lacc[r][s] = 0.0;
   int sc = 0, started = 0;
+  if (kb == 0 && lane == 0) {  // alpha(0, 0) = 1: the first step's accumulator of label 0
+    bacc[0][0] = 1.0;
+    started = -1;
+  }
   RangeTrack rt;
   double lin = 0.0;  // label contribution into this lane's first label for the coming step
   WPlain<DM, R> wb[NB];
@@ -450,12 +457,6 @@ __device__ bool alpha_plain(const Params& p, const Tile& tl, int lane) {
         const bool act = (unsigned)(q - qa[r]) < (unsigned)na[r];
         const double in = r == 0 ? lin : lacc[r > 0 ? r - 1 : 0][(ph + S - 1) % S];
         double v = act ? bacc[r][ph] + in : 0.0;
-        if (r == 0) {
-          const bool origin = act && kb + q == 0;  // alpha(0, 0) = 1
-          v = origin ? 1.0 : v;
-          sc = origin ? 0 : sc;
-          started = origin ? -1 : started;
-        }
         if (BOUND && r == 0) {  // a replayed frame below the tile (zero when not loaded)
           const Ext x = rec_ext(w.x0);
           const double vr = enter(x.m, x.e, sc, started, rt);
