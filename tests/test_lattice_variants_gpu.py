@@ -1,11 +1,13 @@
 """GPU parity of every lattice kernel variant against the float64 oracle.
 
 The lattice launcher picks a kernel by the largest duration value (templates for
-durations up to 4, 8 and 16) and by the padded label count U1_max = U + 1 (labels per
-lane and work-group shape).  This matrix gives each (duration bound, label band) pair a
-small case whose loss and every gradient element are compared with the oracle, plus a
-case per band whose logits (standard deviation 400) put the move weights far below
-2^-300, which forces the extended-range sweep.  Frames are few (24-40) so that the oracle
+durations up to 4, 8 and 16; durations beyond 8 run the extended-range sweep only) and by
+the padded label count U1_max = U + 1: one tile holding every frame with one label per
+lane (U1_max <= 64), one tile with two labels per lane (durations up to 4, U1_max <= 128),
+or bands of 64-label x 64-frame tiles (everything longer).  This matrix gives each
+(duration bound, label count) pair a small case whose loss and every gradient element are
+compared with the oracle, plus a case per label count whose logits (standard deviation
+400) put the move weights far below 2^-300, which forces the extended-range sweep.  Frames are few (24-40) so that the oracle
 and the GPU run in well under a second per case; durations include 0 so that utterances
 with more labels than frames have alignments.
 """
@@ -18,7 +20,8 @@ pytestmark = pytest.mark.gpu
 
 # duration sets by their largest value (the kernel template bound)
 DURATIONS = {4: [0, 1, 2, 3, 4], 8: [0, 1, 3, 8], 16: [0, 1, 2, 7, 16]}
-# one label count per band of the launcher: U1_max <= 64, 128, 256, 768, 1536, 3072, 8192
+# label counts: one tile (51), one tile of two labels per lane or two bands (101), then
+# 4 to 79 bands of tiles
 LABELS = [50, 100, 220, 500, 1200, 2500, 5000]
 
 

@@ -73,10 +73,10 @@ def test_long_label_config_full():
 
 def _plain_sweep_underflow():
     # blank logits 200 above the rest: every move weight stays above 2^-300, so the plain
-    # single-wave sweep runs (151 labels, four per lane sharing one scale), but each label
-    # costs about 2^-290 and the four values of a lane drift beyond the float64 range:
-    # mass is lost to underflow, the two directions' log P disagree and the extended-range
-    # sweep redoes both (with the redo switched off the gradients are off by 2e-3)
+    # sweep runs (151 labels: three bands of 64-label tiles), but each label costs about
+    # 2^-290, so the values along one anti-diagonal lie tens of thousands of binary orders
+    # apart; the per-lane scales and the range check (a value leaving [2^-700, 2^700] sends
+    # the tile to the extended-range sweep) must keep every node's value exact
     case = make_case(2, [40, 30], [150, 20], 5, [0, 1, 2], "f32", seed=57, reduction="none")
     case.joint[..., 4] += 200.0
     return case
@@ -124,9 +124,9 @@ EDGE = {
                                                  reduction="mean_volume"),
     "max_duration_16": lambda: make_case(2, [40, 33], [7, 5], 10, [0, 1, 5, 16, 9], "f32", seed=47,
                                          reduction="sum", sigma=0.05),
-    "duration_8_multiwave": lambda: make_case(1, [30], [300], 21, list(range(9)), "bf16", seed=48,
+    "duration_8_banded": lambda: make_case(1, [30], [300], 21, list(range(9)), "bf16", seed=48,
                                               reduction="sum"),
-    "lattice_r2_multiwave": lambda: make_case(1, [12], [1100], 7, [0, 1, 2], "f32", seed=49, reduction="sum"),
+    "long_labels_banded": lambda: make_case(1, [12], [1100], 7, [0, 1, 2], "f32", seed=49, reduction="sum"),
     "wide_vocab_multipass": lambda: make_case(1, [5], [2], 40000, [0, 1, 2, 3, 4], "bf16", seed=50,
                                               reduction="none"),
     "tiny_vocab": lambda: make_case(2, [8, 6], [3, 2], 2, [0, 1, 2], "f32", seed=51, reduction="none",
@@ -138,8 +138,8 @@ EDGE = {
     # standard deviation 400: weights far below 2^-300 (extended-range lattice path)
     "huge_logits_extended_range": lambda: make_case(2, [40, 31], [12, 9], 17, [0, 1, 2], "f32", seed=54,
                                                     scale=400.0, reduction="none"),
-    # more than 256 labels with weights far below 2^-300: the multi-wave extended-range sweep
-    "huge_logits_multiwave": lambda: make_case(1, [24], [300], 9, [0, 1, 2], "f32", seed=55, scale=400.0,
+    # 300 labels with weights far below 2^-300: banded tiles in the extended-range sweep
+    "huge_logits_banded": lambda: make_case(1, [24], [300], 9, [0, 1, 2], "f32", seed=55, scale=400.0,
                                                reduction="sum"),
     "plain_sweep_underflow_redo": _plain_sweep_underflow,
     "all_negative_logits_bf16": lambda: _all_negative("bf16"),
