@@ -254,6 +254,7 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   p.fd_gnseg = tdt::make_fastdiv((uint32_t)L.gnseg);
   p.fd_u1 = tdt::make_fastdiv((uint32_t)U1_max);
   p.fd_tu1 = tdt::make_fastdiv((uint32_t)T_max * (uint32_t)U1_max);
+  p.fd_a = tdt::make_fastdiv((uint32_t)L.A);
   for (int d = 0; d <= tdt::kMaxDval; ++d) p.didx[d] = -1;
   for (int i = 0; i < num_durations; ++i) {
     p.dval[i] = durations[i];

@@ -60,7 +60,7 @@ struct Params {
   int nT, nU, TT;    // lattice tiles: nT rows of TT frames, nU columns of 64 R labels
   int nseg, nch;     // row-statistics pass: segments per row, 64-chunk windows per segment
   int gnseg, gnch;   // the same for the gradient pass
-  FastDiv fd_nseg, fd_gnseg, fd_u1, fd_tu1;  // by nseg, gnseg, U1max, Tmax*U1max
+  FastDiv fd_nseg, fd_gnseg, fd_u1, fd_tu1, fd_a;  // by nseg, gnseg, U1max, Tmax*U1max, A
   double sigma;
   int dval[kMaxD];          // duration value of index i
   int didx[kMaxDval + 1];   // index of duration value d, -1 when absent
@@ -112,6 +112,35 @@ __device__ __forceinline__ int64_t diag_off(const Params& p, int k) {
 __device__ __forceinline__ int diag_ulo(const Params& p, int k) { return max(0, k - p.Tmax + 1); }
 __device__ __forceinline__ int diag_len(const Params& p, int k) {
   return min(k, p.U1max - 1) - diag_ulo(p, k) + 1;
+}
+// largest k with k (k + 1) / 2 <= n, for 0 <= n < 2^27 (the float square root is off by
+// less than one, so one correction step suffices)
+__device__ __forceinline__ int tri_root(int n) {
+  int k = (int)((sqrtf(8.f * (float)n + 1.f) - 1.f) * 0.5f);
+  if ((k + 1) * (k + 2) / 2 <= n) ++k;
+  else if (k * (k + 1) / 2 > n) --k;
+  return k;
+}
+// Diagonal k and index i on it of position q in [0, box) of an utterance's padded box
+// (the inverse of diag_off): diagonals 1 .. A long up to triA, then a band of A-long
+// diagonals, then diagonals A - 1 .. 1 long.
+__device__ __forceinline__ void box_pos(const Params& p, int q, int& k, int& i) {
+  const int tri = (int)p.triA;
+  const int tail0 = (int)(p.box - p.triA + p.A);
+  if (q < tri) {
+    k = tri_root(q);
+    i = q - k * (k + 1) / 2;
+  } else if (q < tail0) {
+    const int r = q - tri;
+    const int m = (int)fdiv((uint32_t)r, p.fd_a);
+    k = p.A + m;
+    i = r - m * p.A;
+  } else {
+    const int s = (int)(p.box - 1) - q;  // position counted from the box's last node
+    const int kk = tri_root(s);
+    k = p.KD - 1 - kk;
+    i = kk - (s - kk * (kk + 1) / 2);
+  }
 }
 // position of node (t, u) of utterance b
 __device__ __forceinline__ int64_t node_pos(const Params& p, int b, int t, int u) {

@@ -40,20 +40,6 @@ __device__ double reduction_weight(const Params& p, int b, int64_t sumU) {
   }
 }
 
-// A lattice position group of the padded box's diagonal bounding box [KD x A]: decode
-// utterance b, diagonal k and index i on the diagonal; false outside the box.
-__device__ __forceinline__ bool box_node(const Params& p, int64_t g, int& b, int& k, int& i) {
-  const int64_t per = (int64_t)p.KD * p.A;
-  b = (int)(g / per);
-  if (b >= p.B) return false;
-  const int64_t rem = g - (int64_t)b * per;
-  k = (int)(rem / p.A);
-  i = (int)(rem - (int64_t)k * p.A);
-  return i < diag_len(p, k);
-}
-
-__host__ __device__ constexpr int group_lanes(int DM) { return DM < 8 ? 8 : (DM < 16 ? 16 : 32); }
-
 // ------------------------------------------------------------------------------------
 // Node weights: for node n = (t,u) of utterance b
 //   lb = l_blank - sigma, ly = l_label - sigma (l = log-softmax of the token logits),
@@ -61,102 +47,105 @@ __host__ __device__ constexpr int group_lanes(int DM) { return DM < 8 ? 8 : (DM 
 //   W_blank(d) = exp(lb + lambda_d)  (d > 0; t+d < T, or t+d = T at u = U),
 //   W_label(d) = exp(ly + lambda_d)  (u < U, t+d < T),
 // stored as the log-domain ingredients (lb, ly, lambda) and as plain float64 weights by
-// slot pairs (zero for absent durations and for moves that leave the lattice).  A group
-// of NG lanes (at least DM + 1) works on one node: lane d handles duration value d, so
-// the float64 work of a node is spread over its group.  The group also combines the row
+// slot pairs (zero for absent durations and for moves that leave the lattice).  One lane
+// per position of the padded box, the grid [box / 256, utterances] (blockIdx.y, strided
+// by gridDim.y, picks the utterance), so a wave writes 64 consecutive records.  A plain
+// weight is computed as exp(lb) softmax(g)_d, the same number as exp(lb + lambda_d) up to
+// rounding, so a node takes D + 2 exponentials.  The lane also combines the row
 // segments' log-sum-exp partials into the row statistics (c, K).
 template <int DM>
 __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
-  constexpr int NG = group_lanes(DM);
-  const int64_t gt = (int64_t)xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
-  const int j = threadIdx.x & (NG - 1);  // lane in the group: duration value j
-  int b, k, i;
-  // whole groups leave together: every condition depends on the node only
-  if (!box_node(p, gt / NG, b, k, i)) return;
-  const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
-  if (!utt_dims_ok(p, T64, U64)) return;
-  const int T = (int)T64, U = (int)U64;
+  const int q = (int)(blockIdx.x * 256 + threadIdx.x);
+  if (q >= p.box) return;
+  int k, i;
+  box_pos(p, q, k, i);
   const int u = diag_ulo(p, k) + i, t = k - u;
-  if (t >= T || u > U) return;
-  const int64_t pos = (int64_t)b * p.box + diag_off(p, k) + i;
-  const int d = j;
-
-  // the duration logit of this lane, loaded first
-  const int idx = d <= DM ? p.didx[d] : -1;
-  const bool has = idx >= 0;
-  const int64_t dbase = (int64_t)b * p.ds0 + (int64_t)t * p.ds1 + (int64_t)u * p.ds2;
-  const double gl = has ? (double)load_dur(p, dbase + idx) : -__builtin_inf();
-
-  // log-sum-exp of the token logits from the row-segment partials (lane s: segment s);
-  // 16-bit logits keep their shifts in base-2 units (see k_row_partial).  A NaN partial
-  // (logits beyond the float range of the shift) propagates.
   const bool base2 = p.dtype != 0;
   const float F = base2 ? 1.f : kLog2e;
-  const float* part = p.part + pos * 2 * p.nseg;
-  float ms = -__builtin_inff();
-  float ps = 0.f;
-  for (int s2 = j; s2 < p.nseg; s2 += NG) {
-    const float m2 = part[2 * s2], p2 = part[2 * s2 + 1];
-    if (!(p2 <= 0.f)) {
-      const float mn = fmaxf(ms, m2);
-      ps = (ps != 0.f ? ps * __builtin_amdgcn_exp2f((ms - mn) * F) : 0.f) + p2 * __builtin_amdgcn_exp2f((m2 - mn) * F);
-      ms = mn;
+  constexpr double kLo = -300.0 * 0.6931471805599453, kHi = 300.0 * 0.6931471805599453;
+  for (int b = blockIdx.y; b < p.B; b += gridDim.y) {
+    const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
+    if (!utt_dims_ok(p, T64, U64)) continue;
+    const int T = (int)T64, U = (int)U64;
+    if (t >= T || u > U) continue;
+    const int64_t pos = (int64_t)b * p.box + q;
+
+    // duration logits by duration value (absent values: -inf), loaded first
+    const int64_t dbase = (int64_t)b * p.ds0 + (int64_t)t * p.ds1 + (int64_t)u * p.ds2;
+    double gv[DM + 1];
+    double gmax = -__builtin_inf();
+#pragma unroll
+    for (int d = 0; d <= DM; ++d) {
+      const int idx = p.didx[d];
+      gv[d] = idx >= 0 ? (double)load_dur(p, dbase + idx) : -__builtin_inf();
+      gmax = fmax(gmax, gv[d]);
     }
-  }
-  float mx = ms;
-#pragma unroll
-  for (int o = NG / 2; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, NG));
-  double S = ps != 0.f ? (double)ps * exp2(((double)ms - (double)mx) * (base2 ? 1.0 : kLog2eD)) : 0.0;
-#pragma unroll
-  for (int o = NG / 2; o >= 1; o >>= 1) S += __shfl_xor(S, o, NG);
-  const double K = log2(S);
-  const double L = row_lse(base2, (double)mx, K);  // natural-log normaliser
-  const float2 hs = p.stat[pos];                   // blank and label logits (row pass)
-  const double lb = (double)hs.x - L - p.sigma;
-  const double ly = (u < U && hs.y > -__builtin_inff()) ? (double)hs.y - L - p.sigma : -__builtin_inf();
 
-  // duration log-softmax: lambda = gl - gmax - log(sum exp(g - gmax))
-  double gmax = gl;
-#pragma unroll
-  for (int o = NG / 2; o >= 1; o >>= 1) gmax = fmax(gmax, __shfl_xor(gmax, o, NG));
-  const double eg = has ? exp(gl - gmax) : 0.0;
-  double sg = eg;
-#pragma unroll
-  for (int o = NG / 2; o >= 1; o >>= 1) sg += __shfl_xor(sg, o, NG);
-  const double lam = has ? gl - gmax - log(sg) : -__builtin_inf();
+    // log-sum-exp of the token logits from the row-segment partials; 16-bit logits keep
+    // their shifts in base-2 units (see k_row_partial).  Each float32 partial sum is
+    // rescaled to the common shift in float32 and summed in float64.  A NaN partial
+    // (logits beyond the float range of the shift) propagates.
+    const float* part = p.part + pos * 2 * p.nseg;
+    float mx = -__builtin_inff();
+    for (int s2 = 0; s2 < p.nseg; ++s2)
+      if (!(part[2 * s2 + 1] <= 0.f)) mx = fmaxf(mx, part[2 * s2]);
+    double S = 0.0;
+    for (int s2 = 0; s2 < p.nseg; ++s2) {
+      const float m2 = part[2 * s2], p2 = part[2 * s2 + 1];
+      if (!(p2 <= 0.f)) S += (double)(p2 * __builtin_amdgcn_exp2f((m2 - mx) * F));
+    }
+    const double K = log2(S);
+    const double L = row_lse(base2, (double)mx, K);  // natural-log normaliser
+    const float2 hs = p.stat[pos];                   // blank and label logits (row pass)
+    const double lb = (double)hs.x - L - p.sigma;
+    const double ly = (u < U && hs.y > -__builtin_inff()) ? (double)hs.y - L - p.sigma : -__builtin_inf();
+    p.stat[pos] = make_float2(mx, (float)K);
 
-  double* lg = p.lg + pos * p.LG;
-  if (j == 0) {
+    // duration log-softmax: lambda_d = g_d - gmax - log(sum exp(g - gmax))
+    double e[DM + 1];
+    double sg = 0.0;
+#pragma unroll
+    for (int d = 0; d <= DM; ++d) {
+      e[d] = p.didx[d] >= 0 ? exp(gv[d] - gmax) : 0.0;
+      sg += e[d];
+    }
+    const double lsg = log(sg), rsg = 1.0 / sg;
+    const double eb = exp(lb), ey = exp(ly);
+
+    double* lg = p.lg + pos * p.LG;
     lg[0] = lb;
     lg[1] = ly;
-    p.stat[pos] = make_float2(mx, (float)K);  // after every lane of the group read hs
-  }
-  if (has) lg[2 + idx] = lam;
-
-  // plain outgoing weights; a non-zero weight outside [2^-300, 2^300] sends the utterance
-  // to the extended-range sweeps
-  constexpr double kLo = -300.0 * 0.6931471805599453, kHi = 300.0 * 0.6931471805599453;
-  bool wide = false;
-  if (d <= DM) {
+    // plain outgoing weights; a non-zero weight outside [2^-300, 2^300] (or an exp(lb),
+    // exp(ly) above 2^300, whose product form could overflow) sends the utterance to the
+    // extended-range sweeps
+    bool wide = lb > kHi || ly > kHi;
     const int len = diag_len(p, k);
-    double* pw = p.pw ? p.pw + ((int64_t)b * pw_utt_entries(p.NP, p.box, p.KD) + pw_block(p, k) +
-                                pw_col(i, len, p.R)) * 2
+    double* pw = p.pw ? p.pw + ((int64_t)b * pw_utt_entries(p.NP, p.box, p.KD) +
+                                (int64_t)p.NP * (q - i + 3 * (int64_t)k) + pw_col(i, len, p.R)) * 2
                       : nullptr;
     const int64_t pstride = (int64_t)(len + 3) * 2;  // doubles between slot pairs
-    if (d >= 1) {
-      const bool ok = has && (t + d < T || (t + d == T && u == U));
-      const double x = ok ? lb + lam : -__builtin_inf();
-      wide |= x > -__builtin_inf() && (x < kLo || x > kHi);
-      const int s = d - 1;
-      if (pw) pw[(s >> 1) * pstride + (s & 1)] = exp(x);
+#pragma unroll
+    for (int d = 0; d <= DM; ++d) {
+      const int idx = p.didx[d];
+      const bool has = idx >= 0;
+      const double lam = gv[d] - gmax - lsg;
+      if (has) lg[2 + idx] = lam;
+      const double sm = e[d] * rsg;  // softmax(g)_d
+      if (d >= 1) {
+        const bool ok = has && (t + d < T || (t + d == T && u == U));
+        const double x = ok ? lb + lam : -__builtin_inf();
+        wide |= x > -__builtin_inf() && (x < kLo || x > kHi);
+        const int s = d - 1;
+        if (pw) pw[(s >> 1) * pstride + (s & 1)] = ok ? eb * sm : 0.0;
+      }
+      const bool okl = has && u < U && t + d < T;
+      const double xl = okl ? ly + lam : -__builtin_inf();
+      wide |= xl > -__builtin_inf() && (xl < kLo || xl > kHi);
+      const int s = DM + d;
+      if (pw) pw[(s >> 1) * pstride + (s & 1)] = okl ? ey * sm : 0.0;
     }
-    const bool okl = has && u < U && t + d < T;
-    const double xl = okl ? ly + lam : -__builtin_inf();
-    wide |= xl > -__builtin_inf() && (xl < kLo || xl > kHi);
-    const int s = DM + d;
-    if (pw) pw[(s >> 1) * pstride + (s & 1)] = exp(xl);
+    if (wide) atomicOr(p.xflag + b, 1);
   }
-  if (wide) atomicOr(p.xflag + b, 1);
 }
 
 // ------------------------------------------------------------------------------------
@@ -899,67 +888,76 @@ __device__ __forceinline__ Ext xrec_get(const char* base, int64_t pos) {
   return ext_norm(*(const double*)r, *(const int*)(r + 8));
 }
 
-// A group of NG lanes works on one node (as in the node weights): lane d handles the
-// blank and the label move of duration value d; the group sums give O, c_blank, c_label.
-// The first work-group also reduces the loss (the lattice has finished every log P) unless
-// the call writes no loss.  An upstream gradient (chain rule) scales w_b.  The record of
-// the gradient pass overwrites the node's log-domain ingredients.
+// One lane per position of the padded box (as in the node weights).  Utterances whose
+// move weights all lie in [2^-300, 2^300] read the plain weights the lattice read; the
+// others rebuild each weight in extended range from its ingredients.  The first
+// work-group also reduces the loss (the lattice has finished every log P) unless the call
+// writes no loss.  An upstream gradient (chain rule) scales w_b.  The record of the
+// gradient pass overwrites the node's log-domain ingredients.
 template <int DM>
 __global__ __launch_bounds__(256) void k_coef(const Params p) {
-  constexpr int NG = group_lanes(DM);
-  if (p.loss && blockIdx.x == 0 && threadIdx.x == 0) reduce_loss(p);
-  const int64_t gt = (int64_t)xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
-  const int j = threadIdx.x & (NG - 1);
-  int b, k, i;
-  // whole groups leave together below: every condition depends on the node only
-  if (!box_node(p, gt / NG, b, k, i)) return;
-  // the three per-utterance words in one round trip (an ok utterance has valid lengths)
-  const int ok = p.uok[b];
-  const int T = (int)p.Tlen[b], U = (int)p.Ulen[b];
-  if (!ok) return;
+  if (p.loss && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) reduce_loss(p);
+  const int q = (int)(blockIdx.x * 256 + threadIdx.x);
+  if (q >= p.box) return;
+  int k, i;
+  box_pos(p, q, k, i);
   const int u = diag_ulo(p, k) + i, t = k - u;
-  if (t >= T || u > U) return;
-  const int64_t pos = (int64_t)b * p.box + diag_off(p, k) + i;
+  const int len = diag_len(p, k);
+  for (int b = blockIdx.y; b < p.B; b += gridDim.y) {
+    // the per-utterance words (an ok utterance has valid lengths)
+    const int ok = p.uok[b];
+    const int T = (int)p.Tlen[b], U = (int)p.Ulen[b];
+    if (!ok) continue;
+    if (t >= T || u > U) continue;
+    const int64_t pos = (int64_t)b * p.box + q;
+    const bool plain = p.pw != nullptr && p.xflag[b] == 0;
 
-  const Ext a = xrec_get(p.ar, pos);
-  double* lgp = p.lg + pos * p.LG;
-  const double lb = lgp[0], ly = lgp[1];
-  const int d = j;
-  const int idx = d <= DM ? p.didx[d] : -1;
-  const double lam = idx >= 0 ? lgp[2 + idx] : -__builtin_inf();
-  const double Pm = p.pm[b];
-  const int Pe = p.pe[b];
-  double gb = 0.0, gy = 0.0;  // posteriors of the blank / label move of duration d
-  if (idx >= 0) {
-    if (d >= 1) {
-      Ext bt = ext_zero();
-      if (t + d < T) bt = xrec_get(p.br, node_pos(p, b, t + d, u));
-      else if (t + d == T && u == U) bt = ext_one();
-      if (bt.m != 0.0) {
-        const Ext gm = ext_mul(ext_mul(a, ext_exp(lb + lam)), bt);
-        gb = ext_to_double(Ext{gm.m / Pm, gm.e - Pe});
-      }
-    }
-    if (u < U && t + d < T) {
-      const Ext bt = xrec_get(p.br, node_pos(p, b, t + d, u + 1));
-      if (bt.m != 0.0) {
-        const Ext gm = ext_mul(ext_mul(a, ext_exp(ly + lam)), bt);
-        gy = ext_to_double(Ext{gm.m / Pm, gm.e - Pe});
-      }
-    }
-  }
-  double cb = gb, cl = gy;
+    const Ext a = xrec_get(p.ar, pos);
+    double* lgp = p.lg + pos * p.LG;
+    const double lb = lgp[0], ly = lgp[1];
+    double lam[DM + 1];
 #pragma unroll
-  for (int o = NG / 2; o >= 1; o >>= 1) {
-    cb += __shfl_xor(cb, o, NG);
-    cl += __shfl_xor(cl, o, NG);
-  }
-  const double O = cb + cl;
-  const double wgt = p.gscale ? p.wts[b] * (double)p.gscale[p.red == 0 ? b : 0] : p.wts[b];
-  // softmax(h)_blank, softmax(h)_label (sigma added back) and softmax(g)_d
-  const double sb = exp(lb + p.sigma), sy = exp(ly + p.sigma), sgd = exp(lam);
-  float* rec = (float*)lgp;  // every lane of the group has read the ingredients above
-  if (j == 0) {
+    for (int d = 0; d <= DM; ++d) lam[d] = p.didx[d] >= 0 ? lgp[2 + p.didx[d]] : -__builtin_inf();
+    const double rP = 1.0 / p.pm[b];
+    const int Pe = p.pe[b];
+    const double* pw = plain ? p.pw + ((int64_t)b * pw_utt_entries(p.NP, p.box, p.KD) +
+                                       (int64_t)p.NP * (q - i + 3 * (int64_t)k) + pw_col(i, len, p.R)) * 2
+                             : nullptr;
+    const int64_t pstride = (int64_t)(len + 3) * 2;  // doubles between slot pairs
+    // posteriors of the blank / label move of each duration
+    double cd[DM + 1];
+    double cb = 0.0, cl = 0.0;
+#pragma unroll
+    for (int d = 0; d <= DM; ++d) {
+      double gb = 0.0, gy = 0.0;
+      if (p.didx[d] >= 0) {
+        if (d >= 1) {
+          Ext bt = ext_zero();
+          if (t + d < T) bt = xrec_get(p.br, node_pos(p, b, t + d, u));
+          else if (t + d == T && u == U) bt = ext_one();
+          if (bt.m != 0.0) {
+            const int sl = d - 1;
+            const Ext w = plain ? Ext{pw[(sl >> 1) * pstride + (sl & 1)], 0} : ext_exp(lb + lam[d]);
+            gb = ext_to_double(Ext{a.m * w.m * bt.m * rP, a.e + w.e + bt.e - Pe});
+          }
+        }
+        if (u < U && t + d < T) {
+          const Ext bt = xrec_get(p.br, node_pos(p, b, t + d, u + 1));
+          if (bt.m != 0.0) {
+            const int sl = DM + d;
+            const Ext w = plain ? Ext{pw[(sl >> 1) * pstride + (sl & 1)], 0} : ext_exp(ly + lam[d]);
+            gy = ext_to_double(Ext{a.m * w.m * bt.m * rP, a.e + w.e + bt.e - Pe});
+          }
+        }
+      }
+      cd[d] = gb + gy;
+      cb += gb;
+      cl += gy;
+    }
+    const double O = cb + cl;
+    const double wgt = p.gscale ? p.wts[b] * (double)p.gscale[p.red == 0 ? b : 0] : p.wts[b];
+    // softmax(h)_blank, softmax(h)_label (sigma added back)
+    const double sb = exp(lb + p.sigma), sy = exp(ly + p.sigma);
     const float2 rs = p.stat[pos];
     int y = -1;
     if (u < U) y = (int)p.labels[(int64_t)b * p.lab_stride + u];
@@ -970,6 +968,7 @@ __global__ __launch_bounds__(256) void k_coef(const Params p) {
       y = -1;
     }
     const double wO = wgt * O;
+    float* rec = (float*)lgp;  // the ingredients have all been read above
     if (p.dtype == 0) {  // A = w O 2^-K and the row maximum
       rec[0] = (float)(wO * exp2(-(double)rs.y));
       rec[1] = rs.x;
@@ -980,8 +979,11 @@ __global__ __launch_bounds__(256) void k_coef(const Params p) {
     rec[2] = (float)Gb;
     rec[3] = (float)Gy;
     rec[4] = __int_as_float(y);
+    // softmax(g)_d and the duration gradients
+#pragma unroll
+    for (int d = 0; d <= DM; ++d)
+      if (p.didx[d] >= 0) rec[5 + p.didx[d]] = (float)(wgt * (O * exp(lam[d]) - cd[d]));
   }
-  if (idx >= 0) rec[5 + idx] = (float)(wgt * (O * sgd - (gb + gy)));
 }
 
 __global__ void k_reduce(const Params p) {
@@ -1007,10 +1009,8 @@ static hipError_t launch_bands(const Params& p, hipStream_t st) {
 }
 
 hipError_t launch_lattice_side(const Params& p, int which, hipStream_t st) {
-  // node groups over the diagonal bounding box of the padded box
-  const int64_t n = (int64_t)p.B * p.KD * p.A;
-  const int ng = group_lanes(p.DM);
-  const dim3 gridg((unsigned)((n * ng + 255) / 256));
+  // one lane per node: [positions of the padded box, utterances]
+  const dim3 gridg((unsigned)((p.box + 255) / 256), (unsigned)(p.B < 65535 ? p.B : 65535));
   switch (which) {
     case 0:  // node weights
       if (p.DM == 4) hipLaunchKernelGGL((k_node_weights<4>), gridg, dim3(256), 0, st, p);
