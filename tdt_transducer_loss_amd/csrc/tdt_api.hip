@@ -81,8 +81,10 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
     L->nT = (int)((Tmax + 63) / 64);
     L->nU = (int)((U1max + 63) / 64);
   }
-  tdt::pick_segments(V, dtype == 0 ? 4 : 8, tdt::kRowWindows, &L->nch, &L->nseg);
-  tdt::pick_segments(V, dtype == 0 ? 4 : 8, tdt::kGradWindows, &L->gnch, &L->gnseg);
+  // a row's chunks: from its own 16-byte chunk (row statistics, one more chunk than V
+  // fills) or from its 128-byte line (gradient pass, up to 8 more)
+  tdt::pick_segments(V, dtype == 0 ? 4 : 8, tdt::kRowWindows, 1, &L->nch, &L->nseg);
+  tdt::pick_segments(V, dtype == 0 ? 4 : 8, tdt::kGradWindows, 8, &L->gnch, &L->gnseg);
   const size_t NPOS = (size_t)B * (size_t)L->box;
   // the row passes index (node, row segment) pairs with 32-bit integers
   const size_t segs = (size_t)(L->nseg > L->gnseg ? L->nseg : L->gnseg);

@@ -83,7 +83,7 @@ struct Params {
   int64_t gds0, gds1, gds2;
   // workspace, per node position
   float* part;    // [nseg] float2 per row segment: its shift c and its sum 2^(x log2e - c), see k_row_partial
-  float2* stat;   // row pass: (h_blank, h_label); node weights then store (c, K), lse = row_lse(c, K)
+  float2* stat;   // row statistics (c, K) written by the node weights, lse = row_lse(c, K)
   double* lg;     // [LG]: l_blank - sigma, l_label - sigma, lambda[D] (log-softmax of the
                   //   durations); the coefficient kernel overwrites it with the RS floats
                   //   of the gradient-pass record
@@ -244,13 +244,19 @@ __device__ __forceinline__ uint32_t xcd_block(uint32_t g, uint32_t G) {
   return x < r ? x * (q + 1) + idx : r * (q + 1) + (x - r) * q + idx;
 }
 
+// Global-memory (address space 1) pointers: accesses through them compile to global_*
+// instructions.  Through generic pointers they are flat_* ones, which count on both
+// memory counters, so that waiting for one of them waits for every access in flight.
+#define TDT_GLOBAL __attribute__((address_space(1)))
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // ---- element types ----
 struct F32 {
   using T = float;
   static constexpr int kEpc = 4;  // elements per 16-byte chunk
   static constexpr uint32_t kNegInf = 0xff800000u;
-  __device__ static __forceinline__ float load(const void* p, int64_t i) { return ((const float*)p)[i]; }
-  __device__ static __forceinline__ void store(void* p, int64_t i, float v) { ((float*)p)[i] = v; }
+  __device__ static __forceinline__ float load(const void* p, int64_t i) { return ((const TDT_GLOBAL float*)p)[i]; }
+  __device__ static __forceinline__ void store(void* p, int64_t i, float v) { ((TDT_GLOBAL float*)p)[i] = v; }
   __device__ static __forceinline__ float get(const uint4& c, int s) {
     uint32_t w = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
     return __uint_as_float(w);
@@ -271,12 +277,12 @@ struct BF16 {
   static constexpr int kEpc = 8;
   static constexpr uint32_t kNegInf = 0xff80u;
   __device__ static __forceinline__ float load(const void* p, int64_t i) {
-    return __uint_as_float(((uint32_t)((const uint16_t*)p)[i]) << 16);
+    return __uint_as_float(((uint32_t)((const TDT_GLOBAL uint16_t*)p)[i]) << 16);
   }
   __device__ static __forceinline__ uint32_t bits(float v) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);  // round to nearest even
   }
-  __device__ static __forceinline__ void store(void* p, int64_t i, float v) { ((uint16_t*)p)[i] = (uint16_t)bits(v); }
+  __device__ static __forceinline__ void store(void* p, int64_t i, float v) { ((TDT_GLOBAL uint16_t*)p)[i] = (uint16_t)bits(v); }
   __device__ static __forceinline__ float get(const uint4& c, int s) {
     uint32_t w = (s >> 1) == 0 ? c.x : (s >> 1) == 1 ? c.y : (s >> 1) == 2 ? c.z : c.w;
     return __uint_as_float((s & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -303,11 +309,11 @@ struct F16 {
   static constexpr int kEpc = 8;
   static constexpr uint32_t kNegInf = 0xfc00u;
   __device__ static __forceinline__ float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
-  __device__ static __forceinline__ float load(const void* p, int64_t i) { return h2f(((const uint16_t*)p)[i]); }
+  __device__ static __forceinline__ float load(const void* p, int64_t i) { return h2f(((const TDT_GLOBAL uint16_t*)p)[i]); }
   __device__ static __forceinline__ uint32_t bits(float v) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);  // round to nearest even
   }
-  __device__ static __forceinline__ void store(void* p, int64_t i, float v) { ((uint16_t*)p)[i] = (uint16_t)bits(v); }
+  __device__ static __forceinline__ void store(void* p, int64_t i, float v) { ((TDT_GLOBAL uint16_t*)p)[i] = (uint16_t)bits(v); }
   __device__ static __forceinline__ float get(const uint4& c, int s) {
     uint32_t w = (s >> 1) == 0 ? c.x : (s >> 1) == 1 ? c.y : (s >> 1) == 2 ? c.z : c.w;
     return h2f((s & 1) ? (w >> 16) : (w & 0xffffu));

@@ -12,6 +12,13 @@ __device__ __forceinline__ float load_dur(const Params& p, int64_t off) {
   return BF16::load(p.dur, off);
 }
 
+// Token logit at element offset `off` of the token view, widened exactly to float.
+__device__ __forceinline__ float load_tok(const Params& p, int64_t off) {
+  if (p.dtype == 0) return F32::load(p.tok, off);
+  if (p.dtype == 1) return F16::load(p.tok, off);
+  return BF16::load(p.tok, off);
+}
+
 // which: 0 row statistics, 1 gradient pass
 hipError_t launch_rows_f32(const Params& p, bool aligned, hipStream_t st, int which);
 hipError_t launch_rows_f16(const Params& p, bool aligned, hipStream_t st, int which);

@@ -52,7 +52,8 @@ __device__ double reduction_weight(const Params& p, int b, int64_t sumU) {
 // by gridDim.y, picks the utterance), so a wave writes 64 consecutive records.  A plain
 // weight is computed as exp(lb) softmax(g)_d, the same number as exp(lb + lambda_d) up to
 // rounding, so a node takes D + 2 exponentials.  The lane also combines the row
-// segments' log-sum-exp partials into the row statistics (c, K).
+// segments' log-sum-exp partials into the row statistics (c, K), and reads the node's
+// blank and label logits from the token view.
 template <int DM>
 __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
   const int q = (int)(blockIdx.x * 256 + threadIdx.x);
@@ -70,7 +71,11 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
     if (t >= T || u > U) continue;
     const int64_t pos = (int64_t)b * p.box + q;
 
-    // duration logits by duration value (absent values: -inf), loaded first
+    // the blank and label logits of the node (the label read first: its column is data)
+    const int64_t tbase = (int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2;
+    const int64_t yy = u < U ? p.labels[(int64_t)b * p.lab_stride + u] : -1;
+    const float hb = load_tok(p, tbase + p.blank);
+    // duration logits by duration value (absent values: -inf)
     const int64_t dbase = (int64_t)b * p.ds0 + (int64_t)t * p.ds1 + (int64_t)u * p.ds2;
     double gv[DM + 1];
     double gmax = -__builtin_inf();
@@ -96,9 +101,10 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
     }
     const double K = log2(S);
     const double L = row_lse(base2, (double)mx, K);  // natural-log normaliser
-    const float2 hs = p.stat[pos];                   // blank and label logits (row pass)
-    const double lb = (double)hs.x - L - p.sigma;
-    const double ly = (u < U && hs.y > -__builtin_inff()) ? (double)hs.y - L - p.sigma : -__builtin_inf();
+    // a label outside [0, V) is a data error the lattice reports; its move is impossible
+    const float hy = (yy >= 0 && yy < p.V) ? load_tok(p, tbase + yy) : -__builtin_inff();
+    const double lb = (double)hb - L - p.sigma;
+    const double ly = hy > -__builtin_inff() ? (double)hy - L - p.sigma : -__builtin_inf();
     p.stat[pos] = make_float2(mx, (float)K);
 
     // duration log-softmax: lambda_d = g_d - gmax - log(sum exp(g - gmax))

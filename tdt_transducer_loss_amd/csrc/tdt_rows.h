@@ -41,7 +41,6 @@ __device__ __forceinline__ uint4 neg_inf_chunk() {
 //   like their bit patterns); a segment with no non-negative value takes an exact second
 //   pass over order-preserving keys (negative values get their magnitude bits flipped).
 typedef short s16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 
 template <typename TI>
@@ -116,168 +115,50 @@ __device__ __forceinline__ float expo(float x, float c) {
   else return __builtin_fmaf(x, kLog2e, -c);
 }
 
-// Partial log-sum-exp of one row segment.  Writes, per (node, segment):
-//   part[2*seg] = c, part[2*seg + 1] = sum 2^expo(h, c)
-// (floats, in a [positions][2*nseg] array), and the blank / label logits into stat.
-// A segment is NCH windows of 64 16-byte chunks, one chunk per lane per window; windows
-// that hold no chunk of the row are skipped.  The first and the last chunk of the row
-// (which may hold elements of other rows) are left out of the chunk windows and read
-// element by element, one element per lane, so the windows need no per-element masks.
-template <typename TI, int NCH>
-__global__ __launch_bounds__(256) void k_row_partial(const Params p) {
-  constexpr int EPC = TI::kEpc;
-  using ET = typename TI::T;
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (blockIdx.x == 0)  // the flags the node-weight kernel of this call sets
-    for (int i = threadIdx.x; i < p.B; i += blockDim.x) p.xflag[i] = 0;
-  // persistent: a fixed grid of waves walks the (node, segment) space of the padded
-  // [B, Tmax, U1max] rows in memory order, skipping nodes outside their utterance in a
-  // few instructions (ragged batches leave most of the padded space empty); the host
-  // keeps this space below 2^31
-  const uint32_t nseg = (uint32_t)p.nseg;
-  const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
-  const uint32_t total = (uint32_t)p.B * per * nseg;
-  const uint32_t stride = gridDim.x * kWavesPerBlock;
-  for (uint32_t g = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv; g < total; g += stride) {
-    const uint32_t node = fdiv(g, p.fd_nseg);
-    const int seg = (int)(g - node * nseg);
-    const uint32_t b = fdiv(node, p.fd_tu1);
-    const uint32_t nrem = node - b * per;
-    const int t = (int)fdiv(nrem, p.fd_u1);
-    const int u = (int)(nrem - (uint32_t)t * (uint32_t)p.U1max);
-    const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
-    if (!utt_dims_ok(p, T64, U64)) continue;
-    const int T = (int)T64, U = (int)U64;
-    if (t >= T || u > U) continue;
-    // its position in the diagonal-major workspace layout
-    const int64_t pos = node_pos(p, (int)b, t, u);
-
-    const int V = p.V;
-    const ET* row = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
-    const RowCover rc = row_cover<TI>(row, V);
-    const int nch = rc.nch;
-    const int c0 = seg * 64 * NCH;
-    const int nwin = (nch - c0 + 63) >> 6;  // windows of this segment holding chunks (may exceed NCH)
-    // range-checked loads: chunks at or past the end of the row read as zero bits (and
-    // are masked below)
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)rc.base, (short)0, nch * 16, 0x00020000);
-    uint4 v[NCH];
+// Keep slots [lo, hi) of a chunk and replace the others by -inf.
+template <typename TI>
+__device__ __forceinline__ uint4 mask_slots(uint4 c, int lo, int hi) {
+  uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      if (j < nwin) {
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (c0 + lane + 64 * j) * 16, 0, 0);
-        v[j] = make_uint4(x.x, x.y, x.z, x.w);
-      }
-    }
-    // the first and the last chunk of the row, element by element: elements [0, eh) in
-    // the segment holding chunk 0, elements [V - et, V) in the segment holding chunk nch-1
-    const int eh = c0 == 0 ? min(V, EPC - rc.head) : 0;
-    const bool tail_here = nch > 1 && nch - 1 >= c0 && nch - 1 < c0 + 64 * NCH;
-    const int et = tail_here ? V - ((nch - 1) * EPC - rc.head) : 0;
-    float xe = -__builtin_inff();
-    if (lane < eh) xe = TI::load(row, lane);
-    else if (lane - eh < et) xe = TI::load(row, V - et + (lane - eh));
-    // the blank and label logits, by the segment that holds their chunk
-    const int seg_span = 64 * NCH;
-    float* rs = (float*)(p.stat + pos);
-    if (lane == 0) {
-      if ((rc.head + p.blank) / EPC / seg_span == seg) rs[0] = TI::load(row, p.blank);
-      int y = -1;
-      if (u < U) {
-        const int64_t yy = p.labels[(int64_t)b * p.lab_stride + u];
-        if (yy >= 0 && yy < V) y = (int)yy;
-      }
-      if (y >= 0 ? (rc.head + y) / EPC / seg_span == seg : seg == 0)
-        rs[1] = y >= 0 ? TI::load(row, y) : -__builtin_inff();
-    }
-    // chunk 0, chunk nch-1 and chunks past the row hold no element for the windows
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int cw = c0 + 64 * j;
-      if (j < nwin && (cw == 0 || cw + 63 >= nch - 1)) {
-        const int c = cw + lane;
-        if (c == 0 || c >= nch - 1) v[j] = neg_inf_chunk<TI>();
-      }
-    }
-    MaxAcc<TI> mx;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      if (j < nwin) {
-        mx.add(v[j].x);
-        mx.add(v[j].y);
-        mx.add(v[j].z);
-        mx.add(v[j].w);
-      }
-    }
-    float mw = wave_max_dpp(fmaxf(mx.value(), xe));
-    if constexpr (__is_same(TI, BF16)) {
-      if (!(mw >= 0.f)) {  // no non-negative value in the segment: exact maximum from keys
-        KeyMaxBF16 km;
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-          if (j < nwin) {
-            km.add(v[j].x);
-            km.add(v[j].y);
-            km.add(v[j].z);
-            km.add(v[j].w);
-          }
-        }
-        mw = wave_max_dpp(fmaxf(km.value(), xe));
-      }
-    }
-    // the shift: the maximum itself (fp32) or maximum * log2e rounded to float (16-bit)
-    const float c = EPC == 4 ? mw : mw * kLog2e;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      if (j < nwin) {
-#pragma unroll
-        for (int s = 0; s < EPC; ++s) {
-          const float e2 = __builtin_amdgcn_exp2f(expo<TI>(TI::get(v[j], s), c));
-          if ((s & 3) == 0) a0 += e2;
-          else if ((s & 3) == 1) a1 += e2;
-          else if ((s & 3) == 2) a2 += e2;
-          else a3 += e2;
-        }
-      }
-    }
-    float acc = ((a0 + a1) + (a2 + a3)) + __builtin_amdgcn_exp2f(expo<TI>(xe, c));
-    const bool empty = !(mw > -__builtin_inff());  // every slot masked: an empty segment
-    if (empty) acc = 0.f;
-    double S = wave_sum_dpp((double)acc);
-    // 16-bit logits beyond about 2.3e38 in magnitude leave no float shift: NaN partial
-    if (!empty && !(__builtin_fabsf(c) < __builtin_inff())) S = __builtin_nan("");
-    if (lane == 0) {
-      float* part = p.part + (pos * nseg + seg) * 2;
-      part[0] = empty ? -__builtin_inff() : c;
-      part[1] = (float)S;
+  for (int q = 0; q < 4; ++q) {
+    if constexpr (TI::kEpc == 4) {
+      w[q] = (q >= lo && q < hi) ? w[q] : TI::kNegInf;
+    } else {
+      const bool k0 = 2 * q >= lo && 2 * q < hi, k1 = 2 * q + 1 >= lo && 2 * q + 1 < hi;
+      w[q] = (k0 ? (w[q] & 0xffffu) : TI::kNegInf) | (k1 ? (w[q] & 0xffff0000u) : (TI::kNegInf << 16));
     }
   }
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Row statistics for short segments (at most 4 windows): the same task as
-// k_row_partial, split into its loads (row_task_load) and its reductions
-// (row_task_finish), so that a wave issues the loads of both of its tasks before reducing
-// either.  With longer segments the second task's registers cost more occupancy than the
-// overlap gains (B4 T200 U40 V8193 bf16, 6-window segments: 107 vs 104 us; the ragged fp16
-// batch, 3-window segments: 200 vs 210 us; B2 T1000 U1500 V1025 bf16: 2.17 vs 2.38 ms).
+// Partial log-sum-exp of one row segment.  Writes, per (node, segment):
+//   part[2*seg] = c, part[2*seg + 1] = sum 2^expo(h, c)
+// (floats, in a [positions][2*nseg] array).  A segment is NCH windows of 64 16-byte
+// chunks, one chunk per lane per window.  The first and the last chunk of the row may hold
+// elements of neighbouring rows: their slots outside the row are masked.  A task makes one
+// round trip to memory (plus the utterance's lengths, scalar loads).  It is split into its
+// index arithmetic (row_task_load), its loads (row_task_issue) and its reductions
+// (row_task_finish), so that a wave can issue the loads of two tasks before reducing
+// either.
 template <typename TI, int NCH>
 struct RowTask {
   bool ok;  // a node of its utterance's lattice (wave-uniform)
-  int seg, c0, nwin, nch;
-  int64_t pos;      // workspace position of the node
+  int seg, c0, nch, head;
+  int64_t pos;  // workspace position of the node
+  __amdgpu_buffer_rsrc_t rsrc;
   uint4 v[NCH];
-  float xe;
 };
 
+// Index arithmetic, lengths, label and buffer resource of a task.
 template <typename TI, int NCH>
 __device__ __forceinline__ void row_task_load(const Params& p, uint32_t g, uint32_t total, int lane,
                                               RowTask<TI, NCH>& tk) {
   constexpr int EPC = TI::kEpc;
   using ET = typename TI::T;
   tk.ok = false;
+  // a task that is no node of its utterance loads nothing: an empty buffer range
+  tk.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.tok, (short)0, 0, 0x00020000);
+  tk.c0 = 0;
   if (g >= total) return;
   const uint32_t nseg = (uint32_t)p.nseg;
   const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
@@ -299,36 +180,23 @@ __device__ __forceinline__ void row_task_load(const Params& p, uint32_t g, uint3
   const RowCover rc = row_cover<TI>(row, V);
   const int nch = rc.nch;
   const int c0 = seg * 64 * NCH;
-  const int nwin = (nch - c0 + 63) >> 6;
   tk.nch = nch;
   tk.c0 = c0;
-  tk.nwin = nwin;
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)rc.base, (short)0, nch * 16, 0x00020000);
+  tk.head = rc.head;
+  // range-checked loads (row_task_issue): chunks at or past the end of the row's cover
+  // read as zero bits without a memory access (and are masked in row_task_finish)
+  tk.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)rc.base, (short)0, nch * 16, 0x00020000);
+}
+
+// The chunk loads of a task; every window is loaded, with no branch (a task without a
+// node has an empty range and reads zeros without a memory access), so the loads of
+// consecutive tasks issue back to back.
+template <typename TI, int NCH>
+__device__ __forceinline__ void row_task_issue(int lane, RowTask<TI, NCH>& tk) {
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
-    if (j < nwin) {
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (c0 + lane + 64 * j) * 16, 0, 0);
-      tk.v[j] = make_uint4(x.x, x.y, x.z, x.w);
-    }
-  }
-  const int eh = c0 == 0 ? min(V, EPC - rc.head) : 0;
-  const bool tail_here = nch > 1 && nch - 1 >= c0 && nch - 1 < c0 + 64 * NCH;
-  const int et = tail_here ? V - ((nch - 1) * EPC - rc.head) : 0;
-  tk.xe = -__builtin_inff();
-  if (lane < eh) tk.xe = TI::load(row, lane);
-  else if (lane - eh < et) tk.xe = TI::load(row, V - et + (lane - eh));
-  const int seg_span = 64 * NCH;
-  float* rs = (float*)(p.stat + tk.pos);
-  if (lane == 0) {
-    if ((rc.head + p.blank) / EPC / seg_span == seg) rs[0] = TI::load(row, p.blank);
-    int y = -1;
-    if (u < U) {
-      const int64_t yy = p.labels[(int64_t)b * p.lab_stride + u];
-      if (yy >= 0 && yy < V) y = (int)yy;
-    }
-    if (y >= 0 ? (rc.head + y) / EPC / seg_span == seg : seg == 0)
-      rs[1] = y >= 0 ? TI::load(row, y) : -__builtin_inff();
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(tk.rsrc, (tk.c0 + lane + 64 * j) * 16, 0, 0);
+    tk.v[j] = make_uint4(x.x, x.y, x.z, x.w);
   }
 }
 
@@ -336,61 +204,66 @@ template <typename TI, int NCH>
 __device__ __forceinline__ void row_task_finish(const Params& p, int lane, RowTask<TI, NCH>& tk) {
   constexpr int EPC = TI::kEpc;
   if (!tk.ok) return;
-  const int c0 = tk.c0, nwin = tk.nwin, nch = tk.nch;
+  const int c0 = tk.c0, nch = tk.nch, head = tk.head;
+  // slots outside the row: before it in chunk 0, after it in chunk nch-1, and every
+  // chunk past the row's cover.  Every window takes part below, also those past the row
+  // (all -inf then): a loaded value left unused would make the next loop iteration wait
+  // for every load in flight before reusing its register.
+  const int tailn = head + p.V - (nch - 1) * EPC;  // slots of chunk nch-1 inside the row
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int cw = c0 + 64 * j;
-    if (j < nwin && (cw == 0 || cw + 63 >= nch - 1)) {
+    if (cw == 0 || cw + 63 >= nch - 1) {
       const int c = cw + lane;
-      if (c == 0 || c >= nch - 1) tk.v[j] = neg_inf_chunk<TI>();
+      if (c >= nch) {
+        tk.v[j] = neg_inf_chunk<TI>();
+      } else {
+        const int lo = c == 0 ? head : 0, hi = c == nch - 1 ? tailn : EPC;
+        if (lo > 0 || hi < EPC) tk.v[j] = mask_slots<TI>(tk.v[j], lo, hi);
+      }
     }
   }
   MaxAcc<TI> mx;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
-    if (j < nwin) {
-      mx.add(tk.v[j].x);
-      mx.add(tk.v[j].y);
-      mx.add(tk.v[j].z);
-      mx.add(tk.v[j].w);
-    }
+    mx.add(tk.v[j].x);
+    mx.add(tk.v[j].y);
+    mx.add(tk.v[j].z);
+    mx.add(tk.v[j].w);
   }
-  const float xe = tk.xe;
-  float mw = wave_max_dpp(fmaxf(mx.value(), xe));
+  float mw = wave_max_dpp(mx.value());
   if constexpr (__is_same(TI, BF16)) {
-    if (!(mw >= 0.f)) {
+    if (!(mw >= 0.f)) {  // no non-negative value in the segment: exact maximum from keys
       KeyMaxBF16 km;
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
-        if (j < nwin) {
-          km.add(tk.v[j].x);
-          km.add(tk.v[j].y);
-          km.add(tk.v[j].z);
-          km.add(tk.v[j].w);
-        }
+        km.add(tk.v[j].x);
+        km.add(tk.v[j].y);
+        km.add(tk.v[j].z);
+        km.add(tk.v[j].w);
       }
-      mw = wave_max_dpp(fmaxf(km.value(), xe));
+      mw = wave_max_dpp(km.value());
     }
   }
+  // the shift: the maximum itself (fp32) or maximum * log2e rounded to float (16-bit)
   const float c = EPC == 4 ? mw : mw * kLog2e;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
-    if (j < nwin) {
 #pragma unroll
-      for (int s = 0; s < EPC; ++s) {
-        const float e2 = __builtin_amdgcn_exp2f(expo<TI>(TI::get(tk.v[j], s), c));
-        if ((s & 3) == 0) a0 += e2;
-        else if ((s & 3) == 1) a1 += e2;
-        else if ((s & 3) == 2) a2 += e2;
-        else a3 += e2;
-      }
+    for (int s = 0; s < EPC; ++s) {
+      const float e2 = __builtin_amdgcn_exp2f(expo<TI>(TI::get(tk.v[j], s), c));
+      if ((s & 3) == 0) a0 += e2;
+      else if ((s & 3) == 1) a1 += e2;
+      else if ((s & 3) == 2) a2 += e2;
+      else a3 += e2;
     }
   }
-  float acc = ((a0 + a1) + (a2 + a3)) + __builtin_amdgcn_exp2f(expo<TI>(xe, c));
-  const bool empty = !(mw > -__builtin_inff());
+  float acc = (a0 + a1) + (a2 + a3);
+  const bool empty = !(mw > -__builtin_inff());  // every slot masked: an empty segment
   if (empty) acc = 0.f;
   double S = wave_sum_dpp((double)acc);
+  // 16-bit logits beyond about 2.3e38 in magnitude leave no float shift: NaN partial
   if (!empty && !(__builtin_fabsf(c) < __builtin_inff())) S = __builtin_nan("");
   if (lane == 0) {
     float* part = p.part + (tk.pos * p.nseg + tk.seg) * 2;
@@ -399,6 +272,28 @@ __device__ __forceinline__ void row_task_finish(const Params& p, int lane, RowTa
   }
 }
 
+// Row statistics, one task at a time (long segments: 5 to 8 windows).  A persistent grid
+// of waves walks the (node, segment) space of the padded [B, Tmax, U1max] rows in memory
+// order, skipping nodes outside their utterance in a few instructions (ragged batches
+// leave most of the padded space empty); the host keeps this space below 2^31.
+template <typename TI, int NCH>
+__global__ __launch_bounds__(256) void k_row_partial(const Params p) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (blockIdx.x == 0)  // the flags the node-weight kernel of this call sets
+    for (int i = threadIdx.x; i < p.B; i += blockDim.x) p.xflag[i] = 0;
+  const uint32_t total = (uint32_t)p.B * (uint32_t)p.Tmax * (uint32_t)p.U1max * (uint32_t)p.nseg;
+  const uint32_t stride = gridDim.x * kWavesPerBlock;
+  for (uint32_t g = xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv; g < total; g += stride) {
+    RowTask<TI, NCH> t0;
+    row_task_load<TI, NCH>(p, g, total, lane, t0);
+    row_task_issue<TI, NCH>(lane, t0);
+    row_task_finish<TI, NCH>(p, lane, t0);
+  }
+}
+
+// Row statistics for short segments (at most 4 windows): two tasks per loop iteration,
+// the loads of both issued before either is reduced.
 template <typename TI, int NCH>
 __global__ __launch_bounds__(256) void k_row_partial2(const Params p) {
   const int lane = threadIdx.x & 63;
@@ -411,8 +306,143 @@ __global__ __launch_bounds__(256) void k_row_partial2(const Params p) {
     RowTask<TI, NCH> t0, t1;
     row_task_load<TI, NCH>(p, g, total, lane, t0);
     row_task_load<TI, NCH>(p, g + stride, total, lane, t1);
+    row_task_issue<TI, NCH>(lane, t0);
+    row_task_issue<TI, NCH>(lane, t1);
     row_task_finish<TI, NCH>(p, lane, t0);
     row_task_finish<TI, NCH>(p, lane, t1);
+  }
+}
+
+// ---- short rows: a quarter wave per row ----
+// Rows of at most 16 CPL chunks (CPL <= 16) take 16 lanes each: lane l of the quarter
+// holds chunks l, l + 16, ..., l + 16 (CPL - 1) of its row, so a wave holds four rows and a
+// 256-thread block sixteen consecutive nodes of the padded [B, Tmax, U1max] space (one
+// contiguous stretch of the joint tensor).  Index arithmetic, masks and reductions (over
+// the 16 lanes of a row, DPP within a row of the wave) are shared by the four rows, and a
+// row of 130 chunks fills 90% of its lanes (against 68% for 64-chunk windows).
+
+// Lengths of the utterances of a block's 16 nodes (first node n0): scalar loads for the
+// first and the last node's utterance; when one utterance's box is smaller than 16 nodes
+// (a block may span more than two utterances) every lane loads its own.
+struct RowLens {
+  int64_t T, U;
+};
+__device__ __forceinline__ RowLens row_lens(const Params& p, uint32_t n0, uint32_t nodes, uint32_t b) {
+  const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
+  if (per >= 16) {
+    const uint32_t bl = fdiv(n0, p.fd_tu1);
+    const uint32_t bh = fdiv(min(n0 + 15u, nodes - 1u), p.fd_tu1);
+    const int64_t Tl = p.Tlen[bl], Ul = p.Ulen[bl], Th = p.Tlen[bh], Uh = p.Ulen[bh];
+    return b == bl ? RowLens{Tl, Ul} : RowLens{Th, Uh};
+  }
+  return RowLens{p.Tlen[b], p.Ulen[b]};
+}
+
+// 16-lane reductions (every lane of a 16-lane row of the wave gets its row's result; the
+// sum is taken in the same order on lane 0 of every row)
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+  return fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+}
+__device__ __forceinline__ double row16_sum(double x) {
+  x += dpp_d<0xB1>(x);
+  x += dpp_d<0x4E>(x);
+  x += dpp_d<0x141>(x);
+  return x + dpp_d<0x140>(x);
+}
+
+template <typename TI, int CPL>
+__global__ __launch_bounds__(256) void k_row_short(const Params p) {
+  constexpr int EPC = TI::kEpc;
+  using ET = typename TI::T;
+  const int l16 = threadIdx.x & 15;
+  if (blockIdx.x == 0)  // the flags the node-weight kernel of this call sets
+    for (int i = threadIdx.x; i < p.B; i += blockDim.x) p.xflag[i] = 0;
+  const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
+  const uint32_t nodes = (uint32_t)p.B * per;
+  const uint32_t n0 = blockIdx.x * 16u;
+  const uint32_t node = n0 + (threadIdx.x >> 4);
+  const uint32_t nd = min(node, nodes - 1u);
+  const uint32_t b = fdiv(nd, p.fd_tu1);
+  const uint32_t rem = nd - b * per;
+  const int t = (int)fdiv(rem, p.fd_u1);
+  const int u = (int)(rem - (uint32_t)t * (uint32_t)p.U1max);
+  const RowLens ln = row_lens(p, n0, nodes, b);
+  // a row of its utterance's lattice (the same for the 16 lanes of the row)
+  const bool valid = node < nodes && utt_dims_ok(p, ln.T, ln.U) && t < (int)ln.T && u <= (int)ln.U;
+  const int V = p.V;
+  const ET* row = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
+  const RowCover rc = row_cover<TI>(row, V);
+  const int head = rc.head, nch = rc.nch;
+  // chunk loads: addresses clamped into the row's cover (chunks past it are masked below);
+  // rows outside their utterance load nothing
+  uint4 v[CPL];
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = min(l16 + 16 * j, nch - 1);
+      const u32x4 x = *(const TDT_GLOBAL u32x4*)(rc.base + c);
+      v[j] = make_uint4(x.x, x.y, x.z, x.w);
+    }
+  }
+  // slots outside the row: before it in chunk 0, after it in chunk nch-1, every chunk past
+  const int tailn = head + V - (nch - 1) * EPC;  // slots of chunk nch-1 inside the row
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = l16 + 16 * j;
+    if (c >= nch) {
+      v[j] = neg_inf_chunk<TI>();
+    } else if (c == 0 || c == nch - 1) {
+      const int lo = c == 0 ? head : 0, hi = c == nch - 1 ? tailn : EPC;
+      v[j] = mask_slots<TI>(v[j], lo, hi);
+    }
+  }
+  MaxAcc<TI> mx;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    mx.add(v[j].x);
+    mx.add(v[j].y);
+    mx.add(v[j].z);
+    mx.add(v[j].w);
+  }
+  float mw = row16_max(mx.value());
+  if constexpr (__is_same(TI, BF16)) {
+    if (!(mw >= 0.f)) {  // no non-negative value in the row: exact maximum from keys
+      KeyMaxBF16 km;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        km.add(v[j].x);
+        km.add(v[j].y);
+        km.add(v[j].z);
+        km.add(v[j].w);
+      }
+      mw = row16_max(km.value());
+    }
+  }
+  const float c = EPC == 4 ? mw : mw * kLog2e;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+#pragma unroll
+    for (int s = 0; s < EPC; ++s) {
+      const float e2 = __builtin_amdgcn_exp2f(expo<TI>(TI::get(v[j], s), c));
+      if ((s & 3) == 0) a0 += e2;
+      else if ((s & 3) == 1) a1 += e2;
+      else if ((s & 3) == 2) a2 += e2;
+      else a3 += e2;
+    }
+  }
+  float acc = (a0 + a1) + (a2 + a3);
+  const bool empty = !(mw > -__builtin_inff());  // every element -inf
+  if (empty) acc = 0.f;
+  double S = row16_sum((double)acc);
+  if (!empty && !(__builtin_fabsf(c) < __builtin_inff())) S = __builtin_nan("");  // see row_task_finish
+  if (valid && l16 == 0) {
+    float* part = p.part + node_pos(p, (int)b, t, u) * 2;  // one segment per row
+    part[0] = empty ? -__builtin_inff() : c;
+    part[1] = (float)S;
   }
 }
 
@@ -478,10 +508,15 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
   const ET* irow = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
 
   if (ALIGNED) {
-    const RowCover oc = row_cover<TI>(orow, V);
-    uint4* obase = (uint4*)oc.base;
-    const uint4* ibase = (const uint4*)(((uintptr_t)irow) & ~(uintptr_t)15);
-    const int head = oc.head, nch = oc.nch;
+    // chunks counted from the gradient row's 128-byte line, so that a window's store
+    // instruction writes whole lines except at the row's ends; the logits are read at the
+    // same offsets (the rows are equal modulo 16 bytes)
+    const uintptr_t oa = (uintptr_t)orow;
+    uint4* obase = (uint4*)(oa & ~(uintptr_t)127);
+    const int head = (int)((oa & 127) / sizeof(ET));  // elements of the line before the row
+    const int nch = (head + V + EPC - 1) / EPC;       // chunks from the line start to the row end
+    const int cfirst = head / EPC;                    // the chunk holding the row's first element
+    const uint4* ibase = (const uint4*)((const char*)obase + ((const char*)irow - (const char*)orow));
     const int cb = (head + p.blank) / EPC, sb = (head + p.blank) % EPC;
     const int cy = ycol >= 0 ? (head + ycol) / EPC : -1, sy = ycol >= 0 ? (head + ycol) % EPC : 0;
     const int c0 = seg * 64 * NCH;
@@ -490,8 +525,8 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int c = c0 + lane + 64 * j;
-        if (c < nch) {
-          const u32x4 x = __builtin_nontemporal_load((const u32x4*)(ibase + c));
+        if (c >= cfirst && c < nch) {
+          const u32x4 x = __builtin_nontemporal_load((const TDT_GLOBAL u32x4*)(ibase + c));
           v[j] = make_uint4(x.x, x.y, x.z, x.w);
         }
       }
@@ -501,7 +536,7 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
       const int cw = c0 + 64 * j;  // first chunk of the window
       if (cw >= nch) break;
       const int c = cw + lane;
-      if (c >= nch) continue;
+      if (c < cfirst || c >= nch) continue;
       float o[EPC];
       if (valid) {
 #pragma unroll
@@ -526,9 +561,9 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
       }
       const int e0 = c * EPC - head;
       // windows away from the row's first and last chunk store whole chunks
-      if ((cw > 0 && cw + 63 < nch - 1) || (e0 >= 0 && e0 + EPC <= V)) {
+      if ((cw > cfirst && cw + 63 < nch - 1) || (e0 >= 0 && e0 + EPC <= V)) {
         const uint4 q = TI::pack(o);
-        __builtin_nontemporal_store(u32x4{q.x, q.y, q.z, q.w}, (u32x4*)(obase + c));
+        __builtin_nontemporal_store(u32x4{q.x, q.y, q.z, q.w}, (TDT_GLOBAL u32x4*)(obase + c));
       } else {
         ET* oe = (ET*)(obase + c);
 #pragma unroll
@@ -558,6 +593,103 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
   }
 }
 
+// Gradient of short rows (as k_row_short: a quarter wave per row, sixteen consecutive
+// nodes per block, natural order), for logits and gradient rows with the same address
+// modulo 16 bytes.  The chunks are counted from the gradient row's 128-byte line, so each
+// store instruction writes whole lines (16 lanes x 16 bytes, line-aligned) except at the
+// row's ends; the logits are read at the same offsets.  Whole chunks inside the row are
+// stored as 16-byte nontemporal stores, the row's first and last chunk element by element.
+// The blank and label columns are then overwritten by the lane that stored their chunk
+// (same thread, so the element store lands after the chunk store).
+template <typename TI, int CPL>
+__global__ __launch_bounds__(256) void k_grad_short(const Params p) {
+  constexpr int EPC = TI::kEpc;
+  using ET = typename TI::T;
+  const int l16 = threadIdx.x & 15;
+  const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
+  const uint32_t nodes = (uint32_t)p.B * per;
+  const uint32_t n0 = blockIdx.x * 16u;
+  const uint32_t node = n0 + (threadIdx.x >> 4);
+  const uint32_t nd = min(node, nodes - 1u);
+  const uint32_t b = fdiv(nd, p.fd_tu1);
+  const uint32_t rem = nd - b * per;
+  const int t = (int)fdiv(rem, p.fd_u1);
+  const int u = (int)(rem - (uint32_t)t * (uint32_t)p.U1max);
+  const int ok = p.uok[b];  // an ok utterance has valid lengths
+  const RowLens ln = row_lens(p, n0, nodes, b);
+  const bool valid = node < nodes && ok && t < (int)ln.T && u <= (int)ln.U;
+  const int V = p.V;
+  float A = 0.f, m = 0.f, Gb = 0.f, Gy = 0.f;
+  int ycol = -1;
+  const float* rec = nullptr;
+  if (valid) {
+    rec = (const float*)(p.lg + node_pos(p, (int)b, t, u) * p.LG);
+    A = rec[0];
+    m = rec[1];
+    Gb = rec[2];
+    Gy = rec[3];
+    ycol = __float_as_int(rec[4]);
+  }
+  ET* orow = (ET*)p.gtok + ((int64_t)b * p.gs0 + (int64_t)t * p.gs1 + (int64_t)u * p.gs2);
+  const ET* irow = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
+  const uintptr_t oa = (uintptr_t)orow;
+  uint4* obase = (uint4*)(oa & ~(uintptr_t)127);
+  const int head = (int)((oa & 127) / sizeof(ET));     // elements of the line before the row
+  const int nch = (head + V + EPC - 1) / EPC;          // chunks from the line start to the row end
+  const int cfirst = head / EPC;                       // the chunk holding the row's first element
+  // logits chunk at the offset of gradient chunk c (rows equal modulo 16 bytes)
+  const uint4* ibase = (const uint4*)((const char*)obase + ((const char*)irow - (const char*)orow));
+  uint4 v[CPL];
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = min(max(l16 + 16 * j, cfirst), nch - 1);  // inside the row's chunks
+      const u32x4 x = __builtin_nontemporal_load((const TDT_GLOBAL u32x4*)(ibase + c));
+      v[j] = make_uint4(x.x, x.y, x.z, x.w);
+    }
+  }
+  if (node < nodes) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = l16 + 16 * j;
+      if (c >= cfirst && c < nch) {
+        float o[EPC];
+        if (valid) {
+#pragma unroll
+          for (int s = 0; s < EPC; ++s) o[s] = grad_val<TI>(TI::get(v[j], s), A, m);
+          if (EPC == 8 && A < 0.f) {  // 16-bit: a negative w O (upstream gradient)
+#pragma unroll
+            for (int s = 0; s < EPC; ++s) o[s] = -o[s];
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < EPC; ++s) o[s] = 0.f;
+        }
+        const int e0 = c * EPC - head;
+        if (e0 >= 0 && e0 + EPC <= V) {
+          const uint4 q = TI::pack(o);
+          __builtin_nontemporal_store(u32x4{q.x, q.y, q.z, q.w}, (TDT_GLOBAL u32x4*)(obase + c));
+        } else {
+          ET* oe = (ET*)(obase + c);
+#pragma unroll
+          for (int s = 0; s < EPC; ++s) {
+            const int e = e0 + s;
+            if (e >= 0 && e < V) TI::store(oe, s, o[s]);
+          }
+        }
+      }
+    }
+    if (valid) {
+      if (((head + p.blank) / EPC & 15) == l16) TI::store(orow, p.blank, Gb);
+      if (ycol >= 0 && ((head + ycol) / EPC & 15) == l16) TI::store(orow, ycol, Gy);
+    }
+    if (l16 < p.D) {
+      const float gd = valid ? rec[5 + l16] : 0.f;
+      TI::store(p.gdur, (int64_t)b * p.gds0 + (int64_t)t * p.gds1 + (int64_t)u * p.gds2 + l16, gd);
+    }
+  }
+}
+
 // Segment split of a row of V elements: nseg segments of 64 x nch chunks, nch <= maxw
 // (<= 8).  The row-statistics pass takes segments of up to 8 windows of 64 chunks, the
 // gradient pass of up to 4.  Measured (ms per step, gradient pass us) for a maximum of
@@ -568,16 +700,42 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
 constexpr int kRowWindows = 8;
 constexpr int kGradWindows = 4;
 
-inline void pick_segments(int64_t V, int epc, int maxw, int* nch, int* nseg) {
-  const int64_t chunks = (V + epc - 1) / epc + 1;
+inline void pick_segments(int64_t V, int epc, int maxw, int extra, int* nch, int* nseg) {
+  const int64_t chunks = (V + epc - 1) / epc + extra;
   int64_t s = (chunks + 64 * maxw - 1) / (64 * maxw);
   int64_t n = (chunks + 64 * s - 1) / (64 * s);
   *nseg = (int)s;
   *nch = (int)n;
 }
 
+// Rows whose cover has at most this many 16-byte chunks take the quarter-wave kernels.
+constexpr int kShortRowChunks = 256;
+
+template <typename TI>
+hipError_t launch_short_rows(const Params& p, bool aligned, hipStream_t st, int which, int cpl) {
+  const int64_t nodes = (int64_t)p.B * p.Tmax * p.U1max;
+  const dim3 grid((unsigned)((nodes + 15) / 16));
+#define TDT_SR(N)                                                                                \
+  case N:                                                                                        \
+    if (which == 0) hipLaunchKernelGGL((k_row_short<TI, N>), grid, dim3(256), 0, st, p);         \
+    else hipLaunchKernelGGL((k_grad_short<TI, N>), grid, dim3(256), 0, st, p);                   \
+    break;
+  switch (cpl) {
+    TDT_SR(1) TDT_SR(2) TDT_SR(3) TDT_SR(4) TDT_SR(5) TDT_SR(6) TDT_SR(7) TDT_SR(8)
+    TDT_SR(9) TDT_SR(10) TDT_SR(11) TDT_SR(12) TDT_SR(13) TDT_SR(14) TDT_SR(15) default: TDT_SR(16)
+  }
+#undef TDT_SR
+  (void)aligned;
+  return hipGetLastError();
+}
+
 template <typename TI>
 hipError_t launch_rows_t(const Params& p, bool aligned, hipStream_t st, int which) {
+  // chunks of a row's cover: from its 16-byte chunk (row statistics) or from its 128-byte
+  // line (gradient)
+  const int64_t chunks = ((int64_t)p.V + TI::kEpc - 1) / TI::kEpc + (which == 0 ? 1 : 8);
+  if (chunks <= kShortRowChunks && (which == 0 || aligned))
+    return launch_short_rows<TI>(p, aligned, st, which, (int)((chunks + 15) / 16));
   const int nch = which == 0 ? p.nch : p.gnch;
   const int64_t nodes = (int64_t)p.B * p.Tmax * p.U1max;  // both passes walk the padded rows
   const int64_t waves = nodes * (which == 0 ? p.nseg : p.gnseg);
