@@ -3,6 +3,7 @@
 //   row partials -> node weights -> lattice (alpha || beta) -> coefficients and loss
 //   reduction -> gradient  (forward only: ... -> lattice -> loss reduction; a later
 //   backward call on the same workspace: coefficients -> gradient).
+#include <algorithm>
 #include <math.h>
 #include <string.h>
 
@@ -17,7 +18,7 @@ namespace {
 using tdt::Params;
 
 struct Layout {
-  int KD, A, Bb, DM, NW, NP, LG, RS, R, nT, nU, TT, nseg, nch, gnseg, gnch;
+  int KD, A, Bb, DM, NW, NP, LG, RS, R, nT, nU, TT, link, nseg, nch, gnseg, gnch;
   int64_t box;
   size_t pw_bytes;
   size_t off_part, off_stat, off_lg, off_pw, off_ar, off_br, off_lx;
@@ -68,18 +69,20 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
   L->NP = L->DM + 1;
   L->LG = 2 + D;
   L->RS = 5 + D;
-  // lattice tiles: one tile of 64 R labels (R = 2 only for durations up to 4) holding
-  // every frame, or bands of 64-label x 64-frame tiles for longer label sequences
-  if (U1max <= 64 || (L->DM == 4 && U1max <= 128)) {
-    L->R = U1max <= 64 ? 1 : 2;
+  // lattice tiles of 64 labels (one per lane): up to 256 labels, tiles holding every frame
+  // swept at once by the waves of one work-group (linked through LDS); longer label
+  // sequences, bands of 64-label x 64-frame tiles
+  L->R = 1;
+  if (U1max <= 256) {
     L->TT = (int)Tmax;
     L->nT = 1;
-    L->nU = 1;
+    L->nU = (int)((U1max + 63) / 64);
+    L->link = L->nU > 1 ? 1 : 0;
   } else {
-    L->R = 1;
     L->TT = 64;
     L->nT = (int)((Tmax + 63) / 64);
     L->nU = (int)((U1max + 63) / 64);
+    L->link = 0;
   }
   // a row's chunks: from its own 16-byte chunk (row statistics, one more chunk than V
   // fills) or from its 128-byte line (gradient pass, up to 8 more)
@@ -244,6 +247,7 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   p.LG = L.LG;
   p.RS = L.RS;
   p.R = L.R;
+  p.link = L.link;
   p.nT = L.nT;
   p.nU = L.nU;
   p.TT = L.TT;
@@ -341,6 +345,19 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
   auto rec = [&](int i) {
     if (events && i < num_events && events[i]) (void)hipEventRecord((hipEvent_t)events[i], st);
   };
+  // with gradients, extra work-groups of the first lattice launch zero the padding rows
+  // of the gradient while the sweeps run (one wave each, about eight per CU)
+  // (only for a gradient that is one contiguous joint tensor [B, Tmax, U1max, V + D]: its
+  // padding rows of a frame are then one byte range)
+  if (grads) {
+    const size_t elt = dtype == 0 ? 4 : 2;
+    const int64_t* g = grad_strides;
+    const int64_t* gd = grad_dur_strides;
+    const bool joint = g[2] == V + num_durations && g[1] == U1_max * g[2] && g[0] == T_max * g[1] &&
+                       gd[0] == g[0] && gd[1] == g[1] && gd[2] == g[2] &&
+                       (const char*)grad_dur_logits == (const char*)grad_logits + V * elt;
+    if (joint) p.zrows = (int)std::min<int64_t>(2048, B * T_max);
+  }
   rec(0);
   if (launch_rows(p, aligned, st, 0) != hipSuccess) return TDT_ERR_HIP;
   if (phases) rec(1);

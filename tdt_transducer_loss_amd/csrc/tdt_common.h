@@ -56,8 +56,9 @@ struct Params {
   int DM, NW, NP;    // duration bound of the kernels, move slots 2 DM + 1, slot pairs DM + 1
   int LG;            // doubles per node in lg: 2 + D
   int RS;            // floats of the gradient-pass record: 5 + D
-  int R;             // labels per lane of the lattice sweep (1 or 2)
+  int R;             // labels per lane of the lattice sweep (1)
   int nT, nU, TT;    // lattice tiles: nT rows of TT frames, nU columns of 64 R labels
+  int link;          // 1: one work-group of nU waves sweeps an utterance's nU label tiles at once
   int nseg, nch;     // row-statistics pass: segments per row, 64-chunk windows per segment
   int gnseg, gnch;   // the same for the gradient pass
   FastDiv fd_nseg, fd_gnseg, fd_u1, fd_tu1, fd_a;  // by nseg, gnseg, U1max, Tmax*U1max, A
@@ -98,6 +99,10 @@ struct Params {
   int* pe;
   int* uok;       // 1: gradients are written from the lattice, 0: zeros
   int* xflag;     // 1: some move weight lies outside [2^-300, 2^300] (extended-range sweep only)
+  // gradient rows outside every utterance's lattice (padding): 0 = written (zeros) by the
+  // gradient pass; > 0 = zeroed by that many extra work-groups of the first lattice launch
+  // (they overlap the sweeps) and skipped by the gradient pass
+  int zrows;
 };
 
 // ---- padded-box diagonal layout ----

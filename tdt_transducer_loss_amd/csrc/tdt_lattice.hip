@@ -354,15 +354,63 @@ __device__ __forceinline__ int dpp_shift_i32(int x, bool right) {
   return right ? __builtin_amdgcn_mov_dpp(x, 0x138, 0xf, 0xf, true) : __builtin_amdgcn_mov_dpp(x, 0x130, 0xf, 0xf, true);
 }
 
+// Links between the waves of one work-group that sweep neighbouring label tiles of one
+// utterance at the same time: per link an LDS ring of (value, scale) slots indexed by a
+// sequence number that grows along the sweep (alpha: the diagonal; beta: T + U minus the
+// diagonal), the producer's progress (every slot below it written) and the consumer's
+// (every slot below it read).  Waits are bounded: a wait that runs out marks the link
+// broken, and the work-group then redoes the utterance with the extended-range sweeps,
+// which exchange through memory.
+constexpr int kLinkRing = 256;
+struct LinkSlot {
+  double v;
+  int e, pad;
+};
+struct LinkShared {
+  LinkSlot ring[3][kLinkRing];
+  int prod[3], cons[3];
+  int redo;
+};
+// the links of a work-group (LDS, used by the linked-tile kernel only)
+__shared__ LinkShared g_link;
+struct LinkCtx {
+  int in, out;    // link read (lane 0 for alpha, lane 63 for beta), link written; -1: none
+  int in_last;    // the last sequence number the producer of `in` writes a value for
+  int broken;     // a wait ran out
+};
+// Ring slots and progress words are accessed as volatile LDS words: the compiler keeps
+// their order, and the LDS performs the accesses of one wave in order, so a consumer that
+// reads a progress value sees every slot written before it.  (A memory-model fence would
+// also wait for every global load in flight, stalling the weight prefetch.)
+#define TDT_LDS __attribute__((address_space(3)))
+__device__ __forceinline__ int link_load(const int* c) {
+  return __builtin_amdgcn_readfirstlane(*(const TDT_LDS volatile int*)c);
+}
+__device__ __forceinline__ void link_store(int* c, int v) { *(TDT_LDS volatile int*)c = v; }
+// the slot of sequence number sq on link i (volatile: see above)
+__device__ __forceinline__ TDT_LDS volatile LinkSlot* link_slot(int i, int sq) {
+  return (TDT_LDS volatile LinkSlot*)&g_link.ring[i][sq & (kLinkRing - 1)];
+}
+// wait until *c >= target (about 0.1 s at most)
+__device__ __forceinline__ void link_wait(const int* c, int target, LinkCtx& lk) {
+  if (lk.broken) return;
+  for (int it = 0; it < (1 << 20); ++it) {
+    if (link_load(c) >= target) return;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  lk.broken = 1;
+}
+
 // Plain alpha sweep of a tile.  Returns true when some value left [2^-700, 2^700] (the
 // tile is then redone in extended range).
-template <int DM, int R, bool BOUND>
-__device__ bool alpha_plain(const Params& p, const Tile& tl, int lane) {
+template <int DM, int R, bool BOUND, bool LINK>
+__device__ bool alpha_plain(const Params& p, const Tile& tl, int lane, LinkCtx& lk) {
   constexpr int S = ring_size<DM>();
   constexpr int NB = plain_buffers<DM, R>();
   static_assert(NB >= 2 && S % NB == 0, "prefetch buffers must divide the ring");
   static_assert(S >= DM + 2, "ring slots: DM + 1 pending frames and one in flight");
   static_assert(!BOUND || R == 1, "band tiles hold one label per lane");
+  static_assert(!LINK || (R == 1 && !BOUND), "linked tiles hold every frame, one label per lane");
   const int b = tl.b;
   const int trl = tl.below ? max(0, tl.t0 - DM) : tl.t0;  // first frame swept (replayed below t0)
   const int kb = trl + tl.u0;
@@ -398,6 +446,8 @@ __device__ bool alpha_plain(const Params& p, const Tile& tl, int lane) {
   }
   RangeTrack rt;
   double lin = 0.0;  // label contribution into this lane's first label for the coming step
+  double lv[LINK ? S : 1], ov[LINK ? S : 1];  // a block's link inputs and outputs
+  int le[LINK ? S : 1], oe[LINK ? S : 1];
   WPlain<DM, R> wb[NB];
   DiagCursor cl;  // the diagonal being loaded, NB - 1 steps ahead
   cl.init(p, kb);
@@ -426,6 +476,16 @@ __device__ bool alpha_plain(const Params& p, const Tile& tl, int lane) {
 #pragma unroll
     for (int ph = 0; ph < S; ++ph) {  // steps past the last diagonal touch no node
       const int q = q0 + ph;
+      if (LINK && ph == 0 && lk.in >= 0) {
+        // this block's inputs (slots up to kb + q0 + S - 2) written: read them all at once
+        link_wait(&g_link.prod[lk.in], min(kb + q0 + S - 1, lk.in_last + 1), lk);
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+          TDT_LDS volatile LinkSlot* sl = link_slot(lk.in, kb + q0 + j - 1);
+          lv[j] = sl->v;
+          le[j] = sl->e;
+        }
+      }
       if (ph == 0) {  // keep the lane's pending values near 1 (a zero lane shifts by 0)
         const double big = fmax(fmax(fabs(lin), fabs(bacc[0][0])), fmax(fabs(bacc[0][1]), fabs(lacc[R - 1][0])));
         const int ex = __builtin_amdgcn_frexp_exp(big);
@@ -445,6 +505,10 @@ __device__ bool alpha_plain(const Params& p, const Tile& tl, int lane) {
         const Ext x = rec_ext(w.x1);
         const double e1 = enter(x.m, x.e, sc, started, rt);
         lin = (lane == 0 && tl.left) ? e1 : lin;
+      }
+      if (LINK && lk.in >= 0) {  // lane 0: the left wave's label move of diagonal kb + q - 1
+        const double e1 = enter((lane == 0 && kb + q - 1 <= lk.in_last) ? lv[ph] : 0.0, le[ph], sc, started, rt);
+        lin = lane == 0 ? e1 : lin;
       }
       double a[R];
 #pragma unroll
@@ -480,7 +544,26 @@ __device__ bool alpha_plain(const Params& p, const Tile& tl, int lane) {
         __builtin_amdgcn_raw_buffer_store_b128(plain_rec(out, sc), xr, edge ? xoff + p.Tmax * 16 + 16 * (kb + q) : kBadOff,
                                                0, 0);
       }
+      if (LINK) {  // for the right wave (lane 63's values, written at the block's end)
+        ov[ph] = out;
+        oe[ph] = sc;
+      }
       lin = enter(dpp_shift_f64(out, true), dpp_shift_i32(sc, true), sc, started, rt);
+    }
+    if (LINK) {
+      if (lk.out >= 0) {
+        link_wait(&g_link.cons[lk.out], kb + q0 + S - kLinkRing, lk);  // the slots are free
+        if (lane == 63) {
+#pragma unroll
+          for (int j = 0; j < S; ++j) {
+            TDT_LDS volatile LinkSlot* sl = link_slot(lk.out, kb + q0 + j);
+            sl->v = ov[j];
+            sl->e = oe[j];
+          }
+        }
+        link_store(&g_link.prod[lk.out], kb + q0 + S);
+      }
+      if (lk.in >= 0) link_store(&g_link.cons[lk.in], kb + q0 + S - 1);
     }
   }
   return rt.bad();
@@ -488,8 +571,8 @@ __device__ bool alpha_plain(const Params& p, const Tile& tl, int lane) {
 
 // Plain beta sweep of a tile (pull form).  *P00 receives beta(0, 0) when the tile holds
 // node (0, 0) (lane 0).  Returns true when some value left [2^-700, 2^700].
-template <int DM, int R, bool BOUND>
-__device__ bool beta_plain(const Params& p, const Tile& tl, int lane, Ext* P00) {
+template <int DM, int R, bool BOUND, bool LINK>
+__device__ bool beta_plain(const Params& p, const Tile& tl, int lane, Ext* P00, LinkCtx& lk) {
   constexpr int S = ring_size<DM>();
   constexpr int NB = plain_buffers<DM, R>();
   static_assert(NB >= 2 && S % NB == 0, "prefetch buffers must divide the ring");
@@ -528,6 +611,8 @@ __device__ bool beta_plain(const Params& p, const Tile& tl, int lane, Ext* P00) 
 #pragma unroll
   for (int r = 0; r < R; ++r) started = term[r] ? -1 : started;  // the terminal starts its lane at scale 0
   RangeTrack rt;
+  double lv[LINK ? S : 1], ov[LINK ? S : 1];  // a block's link inputs and outputs
+  int le[LINK ? S : 1], oe[LINK ? S : 1];
   WPlain<DM, R> wb[NB];
   // the diagonal being loaded, NB - 1 steps ahead (kb may be one past the box's last
   // diagonal: the terminal of an utterance as long as the box; the closed forms hold there)
@@ -558,6 +643,16 @@ __device__ bool beta_plain(const Params& p, const Tile& tl, int lane, Ext* P00) 
 #pragma unroll
     for (int ph = 0; ph < S; ++ph) {  // steps past the last diagonal touch no node
       const int q = q0 + ph;
+      const int sq = U - tl.ulast + q;  // link sequence number of this step's diagonal kb - q
+      if (LINK && ph == 0 && lk.in >= 0) {  // this block's inputs written: read them at once
+        link_wait(&g_link.prod[lk.in], min(sq + S, lk.in_last + 1), lk);
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+          TDT_LDS volatile LinkSlot* sl = link_slot(lk.in, sq + j);
+          lv[j] = sl->v;
+          le[j] = sl->e;
+        }
+      }
       if (ph == 0) {  // keep the lane's newest values near 1
         const double big = fmax(fabs(h[0][S - 1]), fabs(nb[S - 1]));
         const int ex = __builtin_amdgcn_frexp_exp(big);
@@ -612,7 +707,32 @@ __device__ bool beta_plain(const Params& p, const Tile& tl, int lane, Ext* P00) 
         m = lane == 63 ? x.m : m;
         e = lane == 63 ? x.e : e;
       }
+      if (LINK && lk.in >= 0) {  // lane 63: the right wave's first label on this diagonal
+        const int tn = kb - q - un;
+        m = lane == 63 ? ((tn >= 0 && tn < T) ? lv[ph] : 0.0) : m;
+        e = lane == 63 ? le[ph] : e;
+      }
+      if (LINK) {  // for the left wave (lane 0's values, written at the block's end)
+        ov[ph] = a[0];
+        oe[ph] = sc;
+      }
       nb[ph] = enter(m, e, sc, started, rt);
+    }
+    if (LINK) {
+      const int sq0 = U - tl.ulast + q0;
+      if (lk.out >= 0) {
+        link_wait(&g_link.cons[lk.out], sq0 + S - kLinkRing, lk);  // the slots are free
+        if (lane == 0) {
+#pragma unroll
+          for (int j = 0; j < S; ++j) {
+            TDT_LDS volatile LinkSlot* sl = link_slot(lk.out, sq0 + j);
+            sl->v = ov[j];
+            sl->e = oe[j];
+          }
+        }
+        link_store(&g_link.prod[lk.out], sq0 + S);
+      }
+      if (lk.in >= 0) link_store(&g_link.cons[lk.in], sq0 + S);
     }
   }
   if (lane == 0 && tl.t0 == 0 && tl.u0 == 0) {  // beta(0, 0): the last step's value of lane 0
@@ -817,6 +937,38 @@ __device__ void finish_utterance(const Params& p, int b, Ext P, int lane) {
   if (p.ustatus) p.ustatus[b] = (P.m > 0.0 || lp != lp) ? 0 : 8;
 }
 
+// Zero the gradient rows of the padded box that lie outside their utterance's lattice
+// (t >= T, u > U, or lengths out of range), for a gradient laid out as one contiguous
+// joint tensor [B, Tmax, U1max, V + D] (the host checks the strides): the padding rows of
+// frame (b, t) are then one contiguous byte range, zeroed with 16-byte nontemporal stores
+// (elements at its two ends one by one).  Work-group w of nw takes the frames w, w + nw, ...
+__device__ void zero_padded_rows(const Params& p, uint32_t w, uint32_t nw, int lane) {
+  const uint32_t frames = (uint32_t)p.B * (uint32_t)p.Tmax;
+  const int elt = p.dtype == 0 ? 4 : 2;
+  const int64_t rowb = (int64_t)p.gs2 * elt;  // bytes of one joint row (V + D elements)
+  for (uint32_t f = w; f < frames; f += nw) {
+    const uint32_t b = f / (uint32_t)p.Tmax;
+    const int t = (int)(f - b * (uint32_t)p.Tmax);
+    const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
+    const int ulo = (utt_dims_ok(p, T64, U64) && t < (int)T64) ? (int)U64 + 1 : 0;  // first padding row
+    if (ulo >= p.U1max) continue;
+    char* lo = (char*)p.gtok + ((int64_t)b * p.gs0 + (int64_t)t * p.gs1 + (int64_t)ulo * p.gs2) * elt;
+    char* hi = lo + (p.U1max - ulo) * rowb;
+    char* a16 = (char*)(((uintptr_t)lo + 15) & ~(uintptr_t)15);
+    char* b16 = (char*)((uintptr_t)hi & ~(uintptr_t)15);
+    if (a16 > b16) a16 = b16 = hi;  // a range inside one chunk: elements only
+    for (char* c = a16 + 16 * lane; c < b16; c += 16 * 64)
+      __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, (TDT_GLOBAL u32x4*)c);
+    // the ends: at most 15 bytes before a16 and after b16
+    char* e = lane < 8 ? lo + lane * elt : b16 + (lane - 8) * elt;
+    const bool in = lane < 8 ? e < a16 : (lane < 16 && e < hi && e >= b16 && b16 >= a16);
+    if (in) {
+      if (elt == 4) *(TDT_GLOBAL uint32_t*)e = 0u;
+      else *(TDT_GLOBAL uint16_t*)e = (uint16_t)0;
+    }
+  }
+}
+
 // Tiles of band `band` (i + j = band for alpha, counted from the far corner for beta):
 // one 64-lane work-group per (tile, utterance, direction).  R labels per lane (R = 2 only
 // for a single tile); BOUND: tiles with neighbours (band tiles of 64 labels).  The plain
@@ -828,6 +980,11 @@ __global__ __launch_bounds__(64) void k_tiles(const Params p, int band) {
   const int lane = threadIdx.x;
   const int ilo = max(0, band - (p.nU - 1)), ihi = min(band, p.nT - 1);
   const int ntile = ihi - ilo + 1;
+  const uint32_t tile_blocks = (uint32_t)ntile * 2u * (uint32_t)p.B;
+  if (blockIdx.x >= tile_blocks) {  // the first band's launch also zeroes the padding rows
+    zero_padded_rows(p, blockIdx.x - tile_blocks, gridDim.x - tile_blocks, lane);
+    return;
+  }
   const int m = blockIdx.x % ntile, rest = blockIdx.x / ntile;
   const int dir = rest & 1, b = rest >> 1;
   int i = ilo + m, j = band - i;
@@ -843,8 +1000,9 @@ __global__ __launch_bounds__(64) void k_tiles(const Params p, int band) {
     if (make_tile(p, b, T, U, i, j, 64 * R, tl)) {
       bool redo = true;
       if constexpr (plain_buffers<DM, R>() >= 2) {
-        if (p.pw && !p.xflag[b]) redo = dir == 0 ? alpha_plain<DM, R, BOUND>(p, tl, lane)
-                                                 : beta_plain<DM, R, BOUND>(p, tl, lane, &P);
+        LinkCtx none{-1, -1, 0, 0};
+        if (p.pw && !p.xflag[b]) redo = dir == 0 ? alpha_plain<DM, R, BOUND, false>(p, tl, lane, none)
+                                                 : beta_plain<DM, R, BOUND, false>(p, tl, lane, &P, none);
       }
       // the sweeps run as one wavefront across the lanes: the whole wave redoes the tile
       // when any lane saw a value out of range
@@ -868,6 +1026,81 @@ __global__ __launch_bounds__(64) void k_tiles(const Params p, int band) {
     }
   }
   if (dir == 1 && i == 0 && j == 0) finish_utterance(p, b, P, lane);
+}
+
+// Linked tiles: one work-group of nU <= 4 waves per (utterance, direction), wave w sweeping
+// labels 64 w .. 64 w + 63 over every frame; for alpha wave w takes the label moves into
+// its first label from wave w - 1, for beta its last lane takes the beta of label 64 w + 64
+// from wave w + 1, both through the LDS links, so the waves run at once, each behind its
+// producer by about 64 diagonals, and the utterance takes about T + U steps.  A wave whose
+// plain sweep went out of range (or a link wait that ran out) makes wave 0 redo the whole
+// utterance in extended range, strip after strip.  Extra work-groups zero the gradient's
+// padding rows (as in k_tiles).
+template <int DM>
+__global__ __launch_bounds__(256) void k_tiles_link(const Params p) {
+  LinkShared& sh = g_link;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int W = (int)(blockDim.x >> 6);
+  const uint32_t tile_blocks = 2u * (uint32_t)p.B;
+  if (blockIdx.x >= tile_blocks) {
+    zero_padded_rows(p, (blockIdx.x - tile_blocks) * W + w, (gridDim.x - tile_blocks) * W, lane);
+    return;
+  }
+  const int dir = blockIdx.x & 1, b = blockIdx.x >> 1;
+  const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
+  const bool dims = utt_dims_ok(p, T64, U64);
+  const int T = dims ? (int)T64 : 0, U = dims ? (int)U64 : 0;
+  const int nw = dims ? min(W, U / 64 + 1) : 0;  // waves holding labels
+  if (threadIdx.x == 0) {
+    sh.redo = 0;
+    for (int i = 0; i < 3; ++i) {
+      // nothing written yet; every slot before the consumer's first one consumed
+      sh.prod[i] = -(1 << 30);
+      sh.cons[i] = dir == 0 ? 64 * (i + 1) - 1 : U - min(64 * i + 63, U);
+    }
+  }
+  __syncthreads();
+  Ext P = ext_zero();
+  Tile tl;
+  const bool have = w < nw && make_tile(p, b, T, U, 0, w, 64, tl);
+  bool redo = false;
+  if (have) {
+    redo = true;
+    if constexpr (plain_buffers<DM, 1>() >= 2) {
+      if (p.pw && !p.xflag[b]) {
+        LinkCtx lk{-1, -1, 0, 0};
+        if (dir == 0) {
+          lk.in = w > 0 ? w - 1 : -1;
+          lk.out = w + 1 < nw ? w : -1;
+          lk.in_last = T + tl.u0 - 2;
+          redo = alpha_plain<DM, 1, false, true>(p, tl, lane, lk);
+        } else {
+          lk.in = w + 1 < nw ? w : -1;
+          lk.out = w > 0 ? w - 1 : -1;
+          lk.in_last = T + U - (tl.u0 + 64);
+          redo = beta_plain<DM, 1, false, true>(p, tl, lane, &P, lk);
+        }
+        redo = redo || lk.broken;
+      }
+    }
+  }
+  if (__any(redo) && lane == 0) __hip_atomic_store(&sh.redo, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __syncthreads();
+  if (sh.redo && w == 0 && nw > 0) {
+    // extended range, 64-label strips in dependency order (the strips exchange through lx
+    // / br within this wave: stores complete before the next strip's loads, which bypass
+    // the vector L1)
+    for (int s = 0; s < nw; ++s) {
+      const int sj = dir == 0 ? s : nw - 1 - s;
+      Tile st;
+      if (!make_tile(p, b, T, U, 0, sj, 64, st)) continue;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (dir == 0) alpha_ext<DM>(p, st, lane);
+      else beta_ext<DM>(p, st, lane, &P);
+    }
+  }
+  if (dir == 1 && w == 0) finish_utterance(p, b, P, lane);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1000,13 +1233,17 @@ __global__ void k_reduce(const Params p) {
 // Launchers
 template <int DM>
 static hipError_t launch_bands(const Params& p, hipStream_t st) {
+  if (p.link) {
+    const int zb = (p.zrows + p.nU - 1) / p.nU;  // zeroing waves, nU per work-group
+    hipLaunchKernelGGL((k_tiles_link<DM>), dim3((unsigned)(2 * p.B + zb)), dim3(64 * p.nU), 0, st, p);
+    return hipGetLastError();
+  }
   const bool banded = p.nT > 1 || p.nU > 1;
   for (int band = 0; band < p.nT + p.nU - 1; ++band) {
     const int ilo = band - (p.nU - 1) > 0 ? band - (p.nU - 1) : 0;
     const int ihi = band < p.nT - 1 ? band : p.nT - 1;
-    const dim3 grid((unsigned)((ihi - ilo + 1) * 2 * p.B));
+    const dim3 grid((unsigned)((ihi - ilo + 1) * 2 * p.B + (band == 0 ? p.zrows : 0)));
     if (banded) hipLaunchKernelGGL((k_tiles<DM, 1, true>), grid, dim3(64), 0, st, p, band);
-    else if (DM == 4 && p.R == 2) hipLaunchKernelGGL((k_tiles<4, 2, false>), grid, dim3(64), 0, st, p, band);
     else hipLaunchKernelGGL((k_tiles<DM, 1, false>), grid, dim3(64), 0, st, p, band);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -492,7 +492,10 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
   const float* rec = nullptr;
   // the three per-utterance words in one round trip (an ok utterance has valid lengths)
   const int ok = p.uok[b];
-  const int T = (int)p.Tlen[b], U = (int)p.Ulen[b];
+  const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
+  const int T = (int)T64, U = (int)U64;
+  // rows outside the utterance's lattice, when the lattice launch has zeroed them
+  if (p.zrows && !(utt_dims_ok(p, T64, U64) && t < T && u <= U)) return;
   if (ok) {
     if (t < T && u <= U) {
       valid = true;
@@ -617,7 +620,10 @@ __global__ __launch_bounds__(256) void k_grad_short(const Params p) {
   const int u = (int)(rem - (uint32_t)t * (uint32_t)p.U1max);
   const int ok = p.uok[b];  // an ok utterance has valid lengths
   const RowLens ln = row_lens(p, n0, nodes, b);
-  const bool valid = node < nodes && ok && t < (int)ln.T && u <= (int)ln.U;
+  const bool inside = utt_dims_ok(p, ln.T, ln.U) && t < (int)ln.T && u <= (int)ln.U;
+  const bool valid = node < nodes && ok && inside;
+  // rows outside the utterance's lattice are skipped when the lattice launch has zeroed them
+  const bool write = node < nodes && (inside || p.zrows == 0);
   const int V = p.V;
   float A = 0.f, m = 0.f, Gb = 0.f, Gy = 0.f;
   int ycol = -1;
@@ -648,7 +654,7 @@ __global__ __launch_bounds__(256) void k_grad_short(const Params p) {
       v[j] = make_uint4(x.x, x.y, x.z, x.w);
     }
   }
-  if (node < nodes) {
+  if (write) {
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = l16 + 16 * j;
