@@ -71,7 +71,8 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
   L->RS = 5 + D;
   // lattice tiles of 64 labels (one per lane): up to 256 labels, tiles holding every frame
   // swept at once by the waves of one work-group (linked through LDS); longer label
-  // sequences, bands of 64-label x 64-frame tiles
+  // sequences, bands of 64-label x 48-frame tiles (B2 T1000 U1500 durations 0..8: 32 / 40
+  // / 48 / 64 / 96 / 128 frames, lattice 3.42 / 3.25 / 3.06 / 3.14 / 3.26 / 3.55 ms)
   L->R = 1;
   if (U1max <= 256) {
     L->TT = (int)Tmax;
@@ -79,8 +80,8 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
     L->nU = (int)((U1max + 63) / 64);
     L->link = L->nU > 1 ? 1 : 0;
   } else {
-    L->TT = 64;
-    L->nT = (int)((Tmax + 63) / 64);
+    L->TT = 48;
+    L->nT = (int)((Tmax + 47) / 48);
     L->nU = (int)((U1max + 63) / 64);
     L->link = 0;
   }

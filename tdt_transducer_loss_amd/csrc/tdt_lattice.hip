@@ -5,10 +5,12 @@
 //   lattice tiles — float64 alpha and beta sweeps over the T x (U+1) lattice (the
 //                   alpha/beta passes of the page "tdt-loss: add TDT loss kernel", comment
 //                   "What's in it": float64, no 1024-label limit), as an anti-diagonal
-//                   wavefront with the label index across the lanes of one wave; label
-//                   sequences longer than one wave holds are cut into tiles of 64 labels x
-//                   64 frames swept band after band (one launch per band of tiles), so
-//                   there is no limit on the label count and no work-group waits for another;
+//                   wavefront with the label index across the lanes of one wave; up to
+//                   256 labels the waves of one work-group sweep 64-label tiles at once,
+//                   linked through LDS; longer label sequences are cut into tiles of 64
+//                   labels x 48 frames swept band after band (one launch per band of
+//                   tiles), so there is no limit on the label count and no work-group
+//                   waits for another;
 //   coefficients  — posteriors of the moves out of each node and the per-node record of
 //                   the gradient pass, plus the loss reduction.
 //
@@ -578,7 +580,9 @@ __device__ bool beta_plain(const Params& p, const Tile& tl, int lane, Ext* P00, 
   static_assert(NB >= 2 && S % NB == 0, "prefetch buffers must divide the ring");
   const int b = tl.b, T = tl.T, U = tl.U;
   const int rtop = min(tl.t1 + DM - 1, T);  // highest frame swept (replayed above t1, or the terminal)
-  const int kb = rtop + tl.ulast;
+  // the sweep starts one diagonal higher when a tile lies to the right and frames above:
+  // the label move of duration DM out of the top-right node lands on that diagonal
+  const int kb = rtop + tl.ulast + (tl.right && rtop < T ? 1 : 0);
   const int nsteps = kb - (tl.t0 + tl.u0) + 1;
   const int64_t pwe = pw_utt_entries(p.NP, p.box, p.KD);
   const __amdgpu_buffer_rsrc_t wr = rsrc(p.pw + (int64_t)b * pwe * 2, pwe * 16);
@@ -643,7 +647,7 @@ __device__ bool beta_plain(const Params& p, const Tile& tl, int lane, Ext* P00, 
 #pragma unroll
     for (int ph = 0; ph < S; ++ph) {  // steps past the last diagonal touch no node
       const int q = q0 + ph;
-      const int sq = U - tl.ulast + q;  // link sequence number of this step's diagonal kb - q
+      const int sq = T + U - (kb - q);  // link sequence number of this step's diagonal kb - q
       if (LINK && ph == 0 && lk.in >= 0) {  // this block's inputs written: read them at once
         link_wait(&g_link.prod[lk.in], min(sq + S, lk.in_last + 1), lk);
 #pragma unroll
@@ -719,7 +723,7 @@ __device__ bool beta_plain(const Params& p, const Tile& tl, int lane, Ext* P00, 
       nb[ph] = enter(m, e, sc, started, rt);
     }
     if (LINK) {
-      const int sq0 = U - tl.ulast + q0;
+      const int sq0 = T + U - (kb - q0);
       if (lk.out >= 0) {
         link_wait(&g_link.cons[lk.out], sq0 + S - kLinkRing, lk);  // the slots are free
         if (lane == 0) {
@@ -849,7 +853,7 @@ __device__ void beta_ext(const Params& p, const Tile& tl, int lane, Ext* P00) {
   constexpr int NW = 2 * DM + 1;
   const int b = tl.b, T = tl.T, U = tl.U;
   const int rtop = min(tl.t1 + DM - 1, T);
-  const int kb = rtop + tl.ulast;
+  const int kb = rtop + tl.ulast + (tl.right && rtop < T ? 1 : 0);  // as in beta_plain
   const int nsteps = kb - (tl.t0 + tl.u0) + 1;
   const __amdgpu_buffer_rsrc_t br = rsrc(p.br + (int64_t)b * p.box * 16, p.box * 16);
   const int u = tl.u0 + lane, un = tl.u0 + 64;

@@ -3,13 +3,15 @@
 The lattice launcher picks a kernel by the largest duration value (templates for
 durations up to 4, 8 and 16; durations beyond 8 run the extended-range sweep only) and by
 the padded label count U1_max = U + 1: one tile holding every frame with one label per
-lane (U1_max <= 64), one tile with two labels per lane (durations up to 4, U1_max <= 128),
-or bands of 64-label x 64-frame tiles (everything longer).  This matrix gives each
-(duration bound, label count) pair a small case whose loss and every gradient element are
-compared with the oracle, plus a case per label count whose logits (standard deviation
-400) put the move weights far below 2^-300, which forces the extended-range sweep.  Frames are few (24-40) so that the oracle
-and the GPU run in well under a second per case; durations include 0 so that utterances
-with more labels than frames have alignments.
+lane (U1_max <= 64), two to four such tiles swept at once by the waves of one work-group
+and linked through LDS (U1_max <= 256), or bands of 64-label x 48-frame tiles (everything
+longer).  This matrix gives each (duration bound, label count) pair a small case whose
+loss and every gradient element are compared with the oracle, plus a case per label count
+whose logits (standard deviation 400) put the move weights far below 2^-300, which forces
+the extended-range sweep.  Frames are few (24-40) so that the oracle and the GPU run in
+well under a second per case; durations include 0 so that utterances with more labels
+than frames have alignments.  A linked case with 600 frames runs the LDS rings (256
+slots) through several turns.
 """
 import pytest
 
@@ -20,8 +22,8 @@ pytestmark = pytest.mark.gpu
 
 # duration sets by their largest value (the kernel template bound)
 DURATIONS = {4: [0, 1, 2, 3, 4], 8: [0, 1, 3, 8], 16: [0, 1, 2, 7, 16]}
-# label counts: one tile (51), one tile of two labels per lane or two bands (101), then
-# 4 to 79 bands of tiles
+# label counts: one tile (51), two and four linked tiles (101, 221), then 8 to 79 bands
+# of tiles
 LABELS = [50, 100, 220, 500, 1200, 2500, 5000]
 
 
@@ -54,4 +56,30 @@ def test_lattice_variant_extended_range(U):
 def test_more_than_8192_labels():
     """9000 labels in 12 frames (label moves of duration 0): 141 bands of 64-label tiles."""
     case = make_case(2, [12, 9], [9000, 8100], 9, [0, 1, 2], "f32", seed=300, sigma=0.02, reduction="mean")
+    _parity(case.to("cuda"))
+
+
+@pytest.mark.parametrize("dm", [4, 8])
+def test_linked_tiles_long_frames(dm):
+    """Three linked 64-label tiles over 600 frames: each link's ring turns over twice."""
+    case = make_case(2, [600, 410], [180, 150], 11, DURATIONS[dm], "f32", seed=310 + dm, sigma=0.05,
+                     reduction="mean")
+    _parity(case.to("cuda"))
+
+
+@pytest.mark.parametrize("dm", [4, 8])
+@pytest.mark.parametrize("T,U", [(200, 300), (150, 400)])
+def test_banded_tiles_many_frames(dm, T, U):
+    """Bands of tiles several frame tiles high: each tile's top-right node has a label move of
+    the longest duration into the tile above and to the right (a float32 case, so that a
+    missing move shows far above rounding)."""
+    case = make_case(1, [T], [U], 9, list(range(dm + 1)), "f32", seed=7 + T + dm, sigma=0.05, reduction="sum",
+                     name=f"bands_dm{dm}_T{T}_U{U}")
+    _parity(case.to("cuda"))
+
+
+def test_banded_tiles_many_frames_extended_range():
+    """The same geometry with weights far below 2^-300 (extended-range sweeps in every tile)."""
+    case = make_case(1, [150], [300], 9, [0, 1, 2, 3, 4], "f32", seed=401, scale=400.0, sigma=0.05,
+                     reduction="sum", name="bands_extended")
     _parity(case.to("cuda"))
