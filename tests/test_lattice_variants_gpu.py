@@ -83,3 +83,26 @@ def test_banded_tiles_many_frames_extended_range():
     case = make_case(1, [150], [300], 9, [0, 1, 2, 3, 4], "f32", seed=401, scale=400.0, sigma=0.05,
                      reduction="sum", name="bands_extended")
     _parity(case.to("cuda"))
+
+
+# ragged batches over every tile layout, with duration sets that have gaps, lack 0 or go
+# beyond 8 (B, T per utterance, U per utterance, T_max, U1_max, durations)
+SHAPES = {
+    "bands_gaps_ragged": (3, [255, 115, 211], [101, 57, 60], 255, 102, [0, 2, 5, 7]),
+    "bands_no_zero": (3, [206, 163, 92], [396, 326, 32], 206, 397, [1, 3, 8]),
+    "bands_dm16": (2, [246, 237], [298, 60], 246, 299, [0, 1, 9, 13]),
+    "bands_short_frames_long_labels": (3, [112, 91, 77], [323, 299, 232], 112, 324, [0, 1, 2, 3, 4]),
+    "linked_ragged_dm8": (3, [224, 149, 104], [120, 42, 114], 224, 121, [0, 1, 2, 3, 4, 5, 6, 7, 8]),
+    "linked_no_zero_dm16": (1, [253], [244], 253, 245, [1, 16]),
+}
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_lattice_shapes(name):
+    B, Ts, Us, Tmax, U1max, durs = SHAPES[name]
+    case = make_case(B, Ts, Us, 7, durs, "f32", seed=1000 + len(name), sigma=0.05, reduction="none", Tmax=Tmax,
+                     U1max=U1max, name=name)
+    loss, gt, gd, st = gpu_run(case.to("cuda"))
+    orc = oracle_run(case.to("cpu"))
+    check_loss(loss, orc, case.reduction, case.joint.dtype)
+    check_grads(gt, gd, orc, case.joint.dtype)
