@@ -100,8 +100,8 @@ struct Params {
   int* uok;       // 1: gradients are written from the lattice, 0: zeros
   int* xflag;     // 1: some move weight lies outside [2^-300, 2^300] (extended-range sweep only)
   // gradient rows outside every utterance's lattice (padding): 0 = written (zeros) by the
-  // gradient pass; > 0 = zeroed by that many extra work-groups of the first lattice launch
-  // (they overlap the sweeps) and skipped by the gradient pass
+  // gradient pass; > 0 = zeroed by that many extra waves of the first lattice launch (they
+  // overlap the sweeps) and skipped by the gradient pass
   int zrows;
 };
 

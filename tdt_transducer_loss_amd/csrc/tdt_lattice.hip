@@ -941,11 +941,28 @@ __device__ void finish_utterance(const Params& p, int b, Ext P, int lane) {
   if (p.ustatus) p.ustatus[b] = (P.m > 0.0 || lp != lp) ? 0 : 8;
 }
 
+// Zero bytes [x, y) of a range shorter than 128 bytes (x, y multiples of the element size
+// elt) by 24 lanes, l = 0 .. 23: whole 16-byte chunks by l < 8, the elements before the
+// first chunk by l = 8 .. 15 and those after the last one by l = 16 .. 23.
+__device__ __forceinline__ void zero_short(char* x, char* y, int elt, int l) {
+  char* x16 = (char*)(((uintptr_t)x + 15) & ~(uintptr_t)15);
+  char* y16 = (char*)((uintptr_t)y & ~(uintptr_t)15);
+  char* c = l < 8 ? x16 + 16 * l : (l < 16 ? x + (l - 8) * elt : (x16 > y16 ? x16 : y16) + (l - 16) * elt);
+  if (l < 8) {
+    if (c < y16) __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, (TDT_GLOBAL u32x4*)c);
+  } else if (c < (l < 16 ? (x16 < y ? x16 : y) : y)) {
+    if (elt == 4) *(TDT_GLOBAL uint32_t*)c = 0u;
+    else *(TDT_GLOBAL uint16_t*)c = (uint16_t)0;
+  }
+}
+
 // Zero the gradient rows of the padded box that lie outside their utterance's lattice
 // (t >= T, u > U, or lengths out of range), for a gradient laid out as one contiguous
 // joint tensor [B, Tmax, U1max, V + D] (the host checks the strides): the padding rows of
-// frame (b, t) are then one contiguous byte range, zeroed with 16-byte nontemporal stores
-// (elements at its two ends one by one).  Work-group w of nw takes the frames w, w + nw, ...
+// frame (b, t) are then one contiguous byte range.  Its whole 128-byte lines are zeroed
+// with 16-byte nontemporal stores, eight lines per wave store (a partly written line costs
+// the memory a read-modify-write), its two ends of under 128 bytes piece by piece.  Wave w
+// of nw takes the frames w, w + nw, ...
 __device__ void zero_padded_rows(const Params& p, uint32_t w, uint32_t nw, int lane) {
   const uint32_t frames = (uint32_t)p.B * (uint32_t)p.Tmax;
   const int elt = p.dtype == 0 ? 4 : 2;
@@ -958,18 +975,13 @@ __device__ void zero_padded_rows(const Params& p, uint32_t w, uint32_t nw, int l
     if (ulo >= p.U1max) continue;
     char* lo = (char*)p.gtok + ((int64_t)b * p.gs0 + (int64_t)t * p.gs1 + (int64_t)ulo * p.gs2) * elt;
     char* hi = lo + (p.U1max - ulo) * rowb;
-    char* a16 = (char*)(((uintptr_t)lo + 15) & ~(uintptr_t)15);
-    char* b16 = (char*)((uintptr_t)hi & ~(uintptr_t)15);
-    if (a16 > b16) a16 = b16 = hi;  // a range inside one chunk: elements only
-    for (char* c = a16 + 16 * lane; c < b16; c += 16 * 64)
+    char* a = (char*)(((uintptr_t)lo + 127) & ~(uintptr_t)127);
+    char* e = (char*)((uintptr_t)hi & ~(uintptr_t)127);
+    if (a > e) a = e = hi;  // inside one line: the head is the whole range
+    for (char* c = a + 16 * lane; c < e; c += 16 * 64)
       __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, (TDT_GLOBAL u32x4*)c);
-    // the ends: at most 15 bytes before a16 and after b16
-    char* e = lane < 8 ? lo + lane * elt : b16 + (lane - 8) * elt;
-    const bool in = lane < 8 ? e < a16 : (lane < 16 && e < hi && e >= b16 && b16 >= a16);
-    if (in) {
-      if (elt == 4) *(TDT_GLOBAL uint32_t*)e = 0u;
-      else *(TDT_GLOBAL uint16_t*)e = (uint16_t)0;
-    }
+    if (lane < 24) zero_short(lo, a, elt, lane);
+    else if (lane < 48) zero_short(e, hi, elt, lane - 24);
   }
 }
 
