@@ -18,11 +18,11 @@ namespace {
 using tdt::Params;
 
 struct Layout {
-  int KD, A, Bb, DM, NW, NP, LG, RS, R, nT, nU, TT, link, nseg, nch, gnseg, gnch;
+  int KD, A, Bb, DM, NW, NP, LG, RS, R, nT, nU, TT, link, xns, nseg, nch, gnseg, gnch;
   int64_t box;
   size_t pw_bytes;
   size_t off_part, off_stat, off_lg, off_pw, off_ar, off_br, off_lx;
-  size_t off_logp, off_wts, off_pm, off_pe, off_uok, off_xflag;
+  size_t off_logp, off_wts, off_pm, off_pe, off_uok, off_xflag, off_xctl, off_xprod, off_xring;
   size_t total;
 };
 
@@ -71,9 +71,12 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
   L->RS = 5 + D;
   // lattice tiles of 64 labels (one per lane): up to 256 labels, tiles holding every frame
   // swept at once by the waves of one work-group (linked through LDS); longer label
-  // sequences, bands of 64-label x 48-frame tiles (B2 T1000 U1500 durations 0..8: 32 / 40
-  // / 48 / 64 / 96 / 128 frames, lattice 3.42 / 3.25 / 3.06 / 3.14 / 3.26 / 3.55 ms)
+  // sequences, columns of 64 labels and every frame in work-groups of their own, linked
+  // through global memory (durations up to 8 and at most kMaxColBlocks work-groups), else
+  // bands of 64-label x 48-frame tiles (B2 T1000 U1500 durations 0..8: 32 / 40 / 48 / 64 /
+  // 96 / 128 frames, lattice 3.42 / 3.25 / 3.06 / 3.14 / 3.26 / 3.55 ms)
   L->R = 1;
+  L->xns = 0;
   if (U1max <= 256) {
     L->TT = (int)Tmax;
     L->nT = 1;
@@ -84,6 +87,7 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
     L->nT = (int)((Tmax + 47) / 48);
     L->nU = (int)((U1max + 63) / 64);
     L->link = 0;
+    if (L->DM <= 8 && 2 * B * L->nU <= tdt::kMaxColBlocks) L->xns = (int)(Tmax + U1max + 64);
   }
   // a row's chunks: from its own 16-byte chunk (row statistics, one more chunk than V
   // fills) or from its 128-byte line (gradient pass, up to 8 more)
@@ -118,6 +122,9 @@ int make_layout(int32_t dtype, int64_t B, int64_t Tmax, int64_t U1max, int64_t V
   L->off_pe = take((size_t)B * 4);
   L->off_uok = take((size_t)B * 4);
   L->off_xflag = take((size_t)B * 4);
+  L->off_xctl = take(L->xns ? (size_t)B * 2 * sizeof(tdt::XCtl) : 0);
+  L->off_xprod = take(L->xns ? (size_t)B * 2 * (size_t)L->nU * 4 : 0);
+  L->off_xring = take(L->xns ? (size_t)B * 2 * (size_t)(L->nU - 1) * (size_t)L->xns * 16 : 0);
   L->total = o;
   return TDT_OK;
 }
@@ -249,6 +256,7 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   p.RS = L.RS;
   p.R = L.R;
   p.link = L.link;
+  p.xns = L.xns;
   p.nT = L.nT;
   p.nU = L.nU;
   p.TT = L.TT;
@@ -305,6 +313,9 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   p.pe = (int*)(ws + L.off_pe);
   p.uok = (int*)(ws + L.off_uok);
   p.xflag = (int*)(ws + L.off_xflag);
+  p.xctl = L.xns ? (tdt::XCtl*)(ws + L.off_xctl) : nullptr;
+  p.xprod = L.xns ? (int*)(ws + L.off_xprod) : nullptr;
+  p.xring = L.xns ? ws + L.off_xring : nullptr;
 
   // Row and gradient chunks coincide when the logits and gradient rows share their
   // address modulo 16 bytes for every node.

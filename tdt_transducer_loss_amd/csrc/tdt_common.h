@@ -59,6 +59,8 @@ struct Params {
   int R;             // labels per lane of the lattice sweep (1)
   int nT, nU, TT;    // lattice tiles: nT rows of TT frames, nU columns of 64 R labels
   int link;          // 1: one work-group of nU waves sweeps an utterance's nU label tiles at once
+  int xns;           // > 0: label columns linked across work-groups are possible (cross-column
+                     //   workspace present); slots per link ring
   int nseg, nch;     // row-statistics pass: segments per row, 64-chunk windows per segment
   int gnseg, gnch;   // the same for the gradient pass
   FastDiv fd_nseg, fd_gnseg, fd_u1, fd_tu1, fd_a;  // by nseg, gnseg, U1max, Tmax*U1max, A
@@ -99,10 +101,28 @@ struct Params {
   int* pe;
   int* uok;       // 1: gradients are written from the lattice, 0: zeros
   int* xflag;     // 1: some move weight lies outside [2^-300, 2^300] (extended-range sweep only)
+  // workspace of label columns linked across work-groups (when xns > 0), reset by the node
+  // weights: per (utterance, direction) a control word, per (utterance, direction, column)
+  // the progress of the link it writes, per (utterance, direction, link) a ring of xns
+  // 16-byte slots
+  struct XCtl* xctl;
+  int* xprod;
+  char* xring;
   // gradient rows outside every utterance's lattice (padding): 0 = written (zeros) by the
   // gradient pass; > 0 = zeroed by that many extra waves of the first lattice launch (they
   // overlap the sweeps) and skipped by the gradient pass
   int zrows;
+};
+
+// Column work-groups (2 B nU) up to which long label sequences run as linked columns: they
+// must all be resident at once (about four two-wave work-groups per CU)
+constexpr int kMaxColBlocks = 768;
+
+// Control word of one (utterance, direction) of the linked columns: columns finished,
+// a column asked for the extended-range redo, and beta(0, 0) from the first column.
+struct XCtl {
+  int done, redo, pe, pad;
+  double pm;
 };
 
 // ---- padded-box diagonal layout ----

@@ -58,6 +58,11 @@ __device__ double reduction_weight(const Params& p, int b, int64_t sumU) {
 // blank and label logits from the token view.
 template <int DM>
 __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
+  if (p.xns && blockIdx.x == 0 && blockIdx.y == 0) {
+    // the linked columns' control words and link progress (nothing written yet)
+    for (int i = threadIdx.x; i < 2 * p.B; i += 256) p.xctl[i] = XCtl{0, 0, 0, 0, 0.0};
+    for (int i = threadIdx.x; i < 2 * p.B * p.nU; i += 256) p.xprod[i] = -(1 << 30);
+  }
   const int q = (int)(blockIdx.x * 256 + threadIdx.x);
   if (q >= p.box) return;
   int k, i;
@@ -1119,6 +1124,208 @@ __global__ __launch_bounds__(256) void k_tiles_link(const Params p) {
   if (dir == 1 && w == 0) finish_utterance(p, b, P, lane);
 }
 
+// ---- label columns linked across work-groups ----
+// Device-scope loads and stores: on this GPU they bypass the L2 of the XCD that issues
+// them, so work-groups on different XCDs see each other's values.
+__device__ __forceinline__ int xload_i32(const int* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void xstore_i32(int* a, int v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double xload_f64(const double* a) {
+  return __longlong_as_double(
+      (long long)__hip_atomic_load((const unsigned long long*)a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void xstore_f64(double* a, double v) {
+  __hip_atomic_store((unsigned long long*)a, (unsigned long long)__double_as_longlong(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave 1 of a column work-group: carries the column's LDS links to and from its
+// neighbours' work-groups.  In: slots the neighbour published (ring in global memory,
+// progress word) are copied into LDS ring 0 once the sweep has freed their places, then
+// LDS progress 0 is raised.  Out: slots the sweep wrote into LDS ring 1 are copied to
+// the global ring, and once every one of those stores has completed (s_waitcnt) the
+// progress word is raised, then LDS ring 1's places are freed.  The global rings hold
+// every sequence number of a link, so they need no flow control.  Returns false when no
+// slot moved for about 0.1 s (a neighbour that never ran).
+__device__ bool column_bridge(const Params& p, int b, int dir, int j, int ncol, int T, int U, int lane) {
+  const int in_link = dir == 0 ? (j > 0 ? j - 1 : -1) : (j + 1 < ncol ? j : -1);
+  const int out_link = dir == 0 ? (j + 1 < ncol ? j : -1) : (j > 0 ? j - 1 : -1);
+  const int bd = b * 2 + dir;
+  // the first sequence number the consumer of link i reads, and the last
+  auto first = [&](int i) { return dir == 0 ? 64 * (i + 1) - 1 : U - min(64 * i + 63, U); };
+  auto last = [&](int i) { return dir == 0 ? T + 64 * (i + 1) - 2 : T + U - (64 * i + 64); };
+  int in_next = 0, in_end = 0, out_next = 0, out_end = 0;
+  const int* gin = nullptr;
+  int* gout = nullptr;
+  const char* rin = nullptr;
+  char* rout = nullptr;
+  if (in_link >= 0) {
+    in_next = first(in_link);
+    in_end = last(in_link) + 1;
+    gin = p.xprod + bd * p.nU + in_link;
+    rin = p.xring + ((int64_t)bd * (p.nU - 1) + in_link) * p.xns * 16;
+  }
+  if (out_link >= 0) {
+    out_next = first(out_link);
+    out_end = last(out_link) + 1;
+    gout = p.xprod + bd * p.nU + out_link;
+    rout = p.xring + ((int64_t)bd * (p.nU - 1) + out_link) * p.xns * 16;
+  }
+  int idle = 0;
+  while (in_next < in_end || out_next < out_end) {
+    bool moved = false;
+    if (in_next < in_end) {
+      const int pub = __builtin_amdgcn_readfirstlane(xload_i32(gin));
+      const int avail = min(min(pub, in_end), link_load(&g_link.cons[0]) + kLinkRing);
+      if (avail > in_next) {
+        const int n = min(avail - in_next, 64);
+        if (lane < n) {  // the loads follow the progress load they depend on
+          const int sq = in_next + lane;
+          const double v = xload_f64((const double*)(rin + (int64_t)sq * 16));
+          const int e = xload_i32((const int*)(rin + (int64_t)sq * 16 + 8));
+          TDT_LDS volatile LinkSlot* sl = link_slot(0, sq);
+          sl->v = v;
+          sl->e = e;
+        }
+        in_next += n;
+        link_store(&g_link.prod[0], in_next);
+        moved = true;
+      }
+    }
+    if (out_next < out_end) {
+      const int avail = min(link_load(&g_link.prod[1]), out_end);
+      if (avail > out_next) {
+        const int n = min(avail - out_next, 64);
+        if (lane < n) {
+          const int sq = out_next + lane;
+          TDT_LDS volatile LinkSlot* sl = link_slot(1, sq);
+          xstore_f64((double*)(rout + (int64_t)sq * 16), sl->v);
+          xstore_i32((int*)(rout + (int64_t)sq * 16 + 8), sl->e);
+        }
+        out_next += n;
+        // every slot store complete before the progress store
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) xstore_i32(gout, out_next);
+        link_store(&g_link.cons[1], out_next);
+        moved = true;
+      }
+    }
+    if (moved) {
+      idle = 0;
+    } else {
+      if (++idle > (1 << 20)) return false;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  return true;
+}
+
+// Long label sequences: one work-group of two waves per (utterance, direction, column of
+// 64 labels over every frame), all resident at once (cooperative launch).  Wave 0 sweeps
+// the column as a wave of k_tiles_link does, through LDS links (ring 0 in, ring 1 out);
+// wave 1 carries those links to the neighbouring columns' work-groups (column_bridge), so
+// the columns run at once, each behind its producer by about 64 diagonals plus the
+// bridge, and the utterance takes about T + U steps instead of one launch per band of
+// tiles.  A column whose plain sweep went out of range, or whose links stalled, flags its
+// (utterance, direction); the last of the columns to finish redoes it in extended range,
+// strip after strip, and for beta finishes the utterance.  Extra work-groups zero the
+// gradient's padding rows (as in k_tiles).  The tiles hold every frame (p.TT = Tmax).
+__shared__ int g_col_last;
+template <int DM>
+__global__ __launch_bounds__(128) void k_cols(const Params p) {
+  LinkShared& sh = g_link;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const uint32_t col_blocks = 2u * (uint32_t)p.B * (uint32_t)p.nU;
+  if (blockIdx.x >= col_blocks) {
+    zero_padded_rows(p, (blockIdx.x - col_blocks) * 2 + w, (gridDim.x - col_blocks) * 2, lane);
+    return;
+  }
+  const int j = (int)(blockIdx.x % (uint32_t)p.nU), rest = (int)(blockIdx.x / (uint32_t)p.nU);
+  const int dir = rest & 1, b = rest >> 1;
+  const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
+  const bool dims = utt_dims_ok(p, T64, U64);
+  const int T = dims ? (int)T64 : 0, U = dims ? (int)U64 : 0;
+  const int ncol = dims ? U / 64 + 1 : 1;  // column 0 finishes an utterance with bad lengths
+  if (j >= ncol) return;
+  XCtl* ctl = p.xctl + (b * 2 + dir);
+  Tile tl;
+  const bool have = dims && make_tile(p, b, T, U, 0, j, 64, tl);
+  const bool plain = have && p.pw && !p.xflag[b];
+  if (threadIdx.x == 0) {
+    sh.redo = 0;
+    for (int i = 0; i < 2; ++i) {
+      // ring 0: the link read, ring 1: the link written (i: its lower column)
+      const int li = i == 0 ? (dir == 0 ? j - 1 : j) : (dir == 0 ? j : j - 1);
+      sh.prod[i] = -(1 << 30);
+      sh.cons[i] = dir == 0 ? 64 * (li + 1) - 1 : U - min(64 * li + 63, U);
+    }
+  }
+  __syncthreads();
+  Ext P = ext_zero();
+  bool redo = false;
+  if (w == 0) {
+    if (have) {
+      redo = true;
+      if constexpr (plain_buffers<DM, 1>() >= 2) {
+        if (plain) {
+          LinkCtx lk{-1, -1, 0, 0};
+          if (dir == 0) {
+            lk.in = j > 0 ? 0 : -1;
+            lk.out = j + 1 < ncol ? 1 : -1;
+            lk.in_last = T + tl.u0 - 2;
+            redo = alpha_plain<DM, 1, false, true>(p, tl, lane, lk);
+          } else {
+            lk.in = j + 1 < ncol ? 0 : -1;
+            lk.out = j > 0 ? 1 : -1;
+            lk.in_last = T + U - (tl.u0 + 64);
+            redo = beta_plain<DM, 1, false, true>(p, tl, lane, &P, lk);
+          }
+          redo = redo || lk.broken;
+        }
+      }
+    }
+  } else if (plain) {
+    redo = !column_bridge(p, b, dir, j, ncol, T, U, lane);
+  }
+  if (__any(redo) && lane == 0) __hip_atomic_store(&sh.redo, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __syncthreads();
+  if (threadIdx.x == 0) {  // (lane 0 of wave 0: it holds beta(0, 0) of column 0)
+    if (sh.redo) __hip_atomic_fetch_or(&ctl->redo, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (dir == 1 && j == 0) {
+      xstore_f64(&ctl->pm, P.m);
+      xstore_i32(&ctl->pe, P.e);
+    }
+    // release: this column's records and words before the count; acquire: the last one
+    // sees every column's
+    const int old = __hip_atomic_fetch_add(&ctl->done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int lastc = old == ncol - 1 ? 1 : 0;
+    g_col_last = lastc | (lastc && xload_i32(&ctl->redo) ? 2 : 0);
+  }
+  __syncthreads();
+  const int fin = g_col_last;
+  if (!(fin & 1) || w != 0) return;
+  if (fin & 2) {
+    // extended range, 64-label strips in dependency order (as in k_tiles_link)
+    for (int s2 = 0; s2 < ncol; ++s2) {
+      const int sj = dir == 0 ? s2 : ncol - 1 - s2;
+      Tile st;
+      if (!make_tile(p, b, T, U, 0, sj, 64, st)) continue;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (dir == 0) alpha_ext<DM>(p, st, lane);
+      else beta_ext<DM>(p, st, lane, &P);
+    }
+  } else if (dir == 1) {
+    P = Ext{xload_f64(&ctl->pm), xload_i32(&ctl->pe)};
+  }
+  if (dir == 1) finish_utterance(p, b, P, lane);
+}
+
 // ------------------------------------------------------------------------------------
 // Posteriors and the per-node record of the gradient pass:
 //   gamma(e) = alpha(n) W(e) beta(dest e) / P,   O(n) = sum over moves out of n,
@@ -1253,6 +1460,19 @@ static hipError_t launch_bands(const Params& p, hipStream_t st) {
     const int zb = (p.zrows + p.nU - 1) / p.nU;  // zeroing waves, nU per work-group
     hipLaunchKernelGGL((k_tiles_link<DM>), dim3((unsigned)(2 * p.B + zb)), dim3(64 * p.nU), 0, st, p);
     return hipGetLastError();
+  }
+  if constexpr (plain_buffers<DM, 1>() >= 2) {
+    if (p.xns) {  // linked columns, when every work-group can be resident at once
+      Params q = p;
+      q.TT = p.Tmax;
+      q.nT = 1;
+      const int zb = (p.zrows + 1) / 2;  // zeroing waves, two per work-group
+      void* args[] = {&q};
+      const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_cols<DM>),
+                                                      dim3((unsigned)(2 * p.B * p.nU + zb)), dim3(128), args, 0, st);
+      if (e == hipSuccess) return hipSuccess;
+      (void)hipGetLastError();  // too many to be resident: bands of tiles
+    }
   }
   const bool banded = p.nT > 1 || p.nU > 1;
   for (int band = 0; band < p.nT + p.nU - 1; ++band) {

@@ -4,8 +4,9 @@ The lattice launcher picks a kernel by the largest duration value (templates for
 durations up to 4, 8 and 16; durations beyond 8 run the extended-range sweep only) and by
 the padded label count U1_max = U + 1: one tile holding every frame with one label per
 lane (U1_max <= 64), two to four such tiles swept at once by the waves of one work-group
-and linked through LDS (U1_max <= 256), or bands of 64-label x 48-frame tiles (everything
-longer).  This matrix gives each (duration bound, label count) pair a small case whose
+and linked through LDS (U1_max <= 256), and beyond that columns of 64 labels over every
+frame in work-groups of their own, linked through global memory (durations up to 8, when
+all of them can be resident at once), else bands of 64-label x 48-frame tiles.  This matrix gives each (duration bound, label count) pair a small case whose
 loss and every gradient element are compared with the oracle, plus a case per label count
 whose logits (standard deviation 400) put the move weights far below 2^-300, which forces
 the extended-range sweep.  Frames are few (24-40) so that the oracle and the GPU run in
@@ -106,3 +107,41 @@ def test_lattice_shapes(name):
     orc = oracle_run(case.to("cpu"))
     check_loss(loss, orc, case.reduction, case.joint.dtype)
     check_grads(gt, gd, orc, case.joint.dtype)
+
+
+def test_columns_data_errors():
+    """Linked columns (301 padded labels) with an infeasible utterance, a label out of range,
+    a logit length beyond T_max and zero frames: statuses, losses and zero gradients as the
+    oracle has them (the first column finishes utterances with bad lengths)."""
+    case = make_case(5, [20, 19, 20, 20, 20], [290, 200, 250, 120, 260], 9, [0, 2, 4], "f32", seed=71,
+                     sigma=0.05, reduction="none", Tmax=20, U1max=301, name="columns_errors")
+    case.labels[2, 100] = 9
+    case.logit_lengths[3] = 21
+    case.logit_lengths[4] = 0
+    loss, gt, gd, st = gpu_run(case.to("cuda"))
+    orc = oracle_run(case.to("cpu"))
+    check_loss(loss, orc, "none", case.joint.dtype)
+    check_grads(gt, gd, orc, case.joint.dtype)
+    s = st.cpu().numpy()
+    assert list(s) == list(orc["status"])
+    assert s[0] == 0 and s[1] != 0 and s[2] != 0 and s[3] != 0 and s[4] != 0
+
+
+@pytest.mark.parametrize("dm,B", [(4, 80), (8, 60)])
+def test_many_utterances_long_labels(dm, B):
+    """Long label sequences in batches too large for every column work-group to be resident
+    at once: 80 x 5 columns x 2 directions exceed the column limit (bands of tiles), and
+    with durations up to 8 the 600 column work-groups are more than the GPU holds at the
+    register count of that sweep (the cooperative launch is refused and bands run)."""
+    import random
+
+    rnd = random.Random(dm)
+    Ts = [rnd.randint(3, 12) for _ in range(B)]
+    Us = [rnd.randint(200, 300) for _ in range(B)]
+    case = make_case(B, Ts, Us, 5, DURATIONS[dm], "f32", seed=72 + dm, sigma=0.05, reduction="mean", Tmax=12,
+                     U1max=301, name=f"many_long_dm{dm}")
+    loss, gt, gd, st = gpu_run(case.to("cuda"))
+    orc = oracle_run(case.to("cpu"))
+    check_loss(loss, orc, case.reduction, case.joint.dtype)
+    check_grads(gt, gd, orc, case.joint.dtype)
+    assert list(st.cpu().numpy()) == list(orc["status"])
