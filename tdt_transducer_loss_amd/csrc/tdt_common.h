@@ -114,8 +114,9 @@ struct Params {
   int zrows;
 };
 
-// Column work-groups (2 B nU) up to which long label sequences run as linked columns: they
-// must all be resident at once (about four two-wave work-groups per CU)
+// Column work-groups (2 B nU) up to which the workspace holds the links of long label
+// sequences run as linked columns (the launch also checks that the GPU holds them all at
+// once: about two to four two-wave work-groups per CU)
 constexpr int kMaxColBlocks = 768;
 
 // Control word of one (utterance, direction) of the linked columns: columns finished,

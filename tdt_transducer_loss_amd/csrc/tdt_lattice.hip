@@ -1149,7 +1149,7 @@ __device__ __forceinline__ void xstore_f64(double* a, double v) {
 // the global ring, and once every one of those stores has completed (s_waitcnt) the
 // progress word is raised, then LDS ring 1's places are freed.  The global rings hold
 // every sequence number of a link, so they need no flow control.  Returns false when no
-// slot moved for about 0.1 s (a neighbour that never ran).
+// slot moved for about 0.1 s (a neighbour that did not run).
 __device__ bool column_bridge(const Params& p, int b, int dir, int j, int ncol, int T, int U, int lane) {
   const int in_link = dir == 0 ? (j > 0 ? j - 1 : -1) : (j + 1 < ncol ? j : -1);
   const int out_link = dir == 0 ? (j + 1 < ncol ? j : -1) : (j > 0 ? j - 1 : -1);
@@ -1226,7 +1226,8 @@ __device__ bool column_bridge(const Params& p, int b, int dir, int j, int ncol, 
 }
 
 // Long label sequences: one work-group of two waves per (utterance, direction, column of
-// 64 labels over every frame), all resident at once (cooperative launch).  Wave 0 sweeps
+// 64 labels over every frame), launched only when the GPU holds all of them at once (so a
+// column never waits for a neighbour that has not started; the waits are bounded anyway).  Wave 0 sweeps
 // the column as a wave of k_tiles_link does, through LDS links (ring 0 in, ring 1 out);
 // wave 1 carries those links to the neighbouring columns' work-groups (column_bridge), so
 // the columns run at once, each behind its producer by about 64 diagonals plus the
@@ -1454,6 +1455,27 @@ __global__ void k_reduce(const Params p) {
 
 // ------------------------------------------------------------------------------------
 // Launchers
+// Work-groups of k_cols<DM> that the GPU running `st` holds at once (0 when unknown),
+// from the occupancy of one CU times the CUs; kept per device.
+template <int DM>
+static int col_capacity(hipStream_t st) {
+  constexpr int kDevices = 64;
+  static int cache[kDevices] = {};
+  int dev = -1;
+  if (st ? hipStreamGetDevice(st, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= kDevices) return 0;
+  int cap = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (cap == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_cols<DM>, 128, 0) != hipSuccess)
+      return 0;
+    cap = cus * per;
+    __atomic_store_n(&cache[dev], cap, __ATOMIC_RELAXED);
+  }
+  return cap;
+}
+
 template <int DM>
 static hipError_t launch_bands(const Params& p, hipStream_t st) {
   if (p.link) {
@@ -1463,15 +1485,15 @@ static hipError_t launch_bands(const Params& p, hipStream_t st) {
   }
   if constexpr (plain_buffers<DM, 1>() >= 2) {
     if (p.xns) {  // linked columns, when every work-group can be resident at once
-      Params q = p;
-      q.TT = p.Tmax;
-      q.nT = 1;
       const int zb = (p.zrows + 1) / 2;  // zeroing waves, two per work-group
-      void* args[] = {&q};
-      const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_cols<DM>),
-                                                      dim3((unsigned)(2 * p.B * p.nU + zb)), dim3(128), args, 0, st);
-      if (e == hipSuccess) return hipSuccess;
-      (void)hipGetLastError();  // too many to be resident: bands of tiles
+      const int grid = 2 * p.B * p.nU + zb;
+      if (grid <= col_capacity<DM>(st)) {
+        Params q = p;
+        q.TT = p.Tmax;
+        q.nT = 1;
+        hipLaunchKernelGGL((k_cols<DM>), dim3((unsigned)grid), dim3(128), 0, st, q);
+        return hipGetLastError();
+      }
     }
   }
   const bool banded = p.nT > 1 || p.nU > 1;

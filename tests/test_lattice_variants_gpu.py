@@ -132,7 +132,7 @@ def test_many_utterances_long_labels(dm, B):
     """Long label sequences in batches too large for every column work-group to be resident
     at once: 80 x 5 columns x 2 directions exceed the column limit (bands of tiles), and
     with durations up to 8 the 600 column work-groups are more than the GPU holds at the
-    register count of that sweep (the cooperative launch is refused and bands run)."""
+    register count of that sweep (the occupancy check sends them to bands)."""
     import random
 
     rnd = random.Random(dm)
