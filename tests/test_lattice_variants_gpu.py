@@ -70,29 +70,29 @@ def test_linked_tiles_long_frames(dm):
 
 @pytest.mark.parametrize("dm", [4, 8])
 @pytest.mark.parametrize("T,U", [(200, 300), (150, 400)])
-def test_banded_tiles_many_frames(dm, T, U):
-    """Bands of tiles several frame tiles high: each tile's top-right node has a label move of
-    the longest duration into the tile above and to the right (a float32 case, so that a
-    missing move shows far above rounding)."""
+def test_long_labels_many_frames(dm, T, U):
+    """Linked columns over 150-200 frames (a float32 case, so that a lost move shows far
+    above rounding)."""
     case = make_case(1, [T], [U], 9, list(range(dm + 1)), "f32", seed=7 + T + dm, sigma=0.05, reduction="sum",
                      name=f"bands_dm{dm}_T{T}_U{U}")
     _parity(case.to("cuda"))
 
 
-def test_banded_tiles_many_frames_extended_range():
-    """The same geometry with weights far below 2^-300 (extended-range sweeps in every tile)."""
+def test_long_labels_many_frames_extended_range():
+    """The same geometry with weights far below 2^-300 (the extended-range redo)."""
     case = make_case(1, [150], [300], 9, [0, 1, 2, 3, 4], "f32", seed=401, scale=400.0, sigma=0.05,
                      reduction="sum", name="bands_extended")
     _parity(case.to("cuda"))
 
 
-# ragged batches over every tile layout, with duration sets that have gaps, lack 0 or go
-# beyond 8 (B, T per utterance, U per utterance, T_max, U1_max, durations)
+# ragged batches over every lattice layout, with duration sets that have gaps, lack 0 or go
+# beyond 8 (B, T per utterance, U per utterance, T_max, U1_max, durations); the seed
+# follows the name
 SHAPES = {
-    "bands_gaps_ragged": (3, [255, 115, 211], [101, 57, 60], 255, 102, [0, 2, 5, 7]),
-    "bands_no_zero": (3, [206, 163, 92], [396, 326, 32], 206, 397, [1, 3, 8]),
+    "linked_gaps_ragged": (3, [255, 115, 211], [101, 57, 60], 255, 102, [0, 2, 5, 7]),
+    "columns_no_zero_dm8": (3, [206, 163, 92], [396, 326, 32], 206, 397, [1, 3, 8]),
     "bands_dm16": (2, [246, 237], [298, 60], 246, 299, [0, 1, 9, 13]),
-    "bands_short_frames_long_labels": (3, [112, 91, 77], [323, 299, 232], 112, 324, [0, 1, 2, 3, 4]),
+    "columns_short_frames": (3, [112, 91, 77], [323, 299, 232], 112, 324, [0, 1, 2, 3, 4]),
     "linked_ragged_dm8": (3, [224, 149, 104], [120, 42, 114], 224, 121, [0, 1, 2, 3, 4, 5, 6, 7, 8]),
     "linked_no_zero_dm16": (1, [253], [244], 253, 245, [1, 16]),
 }
@@ -125,6 +125,45 @@ def test_columns_data_errors():
     s = st.cpu().numpy()
     assert list(s) == list(orc["status"])
     assert s[0] == 0 and s[1] != 0 and s[2] != 0 and s[3] != 0 and s[4] != 0
+
+
+@pytest.mark.parametrize("dm", [4, 8])
+def test_bands_many_frame_tiles(dm):
+    """80 utterances of 150-200 frames and 250-350 labels: more column work-groups than the
+    linked-column path takes, so bands of 64-label x 48-frame tiles run, each utterance
+    several frame tiles high; each tile's top-right node has a label move of the longest
+    duration into the tile above and to the right."""
+    import random
+
+    rnd = random.Random(10 + dm)
+    B = 80
+    Ts = [rnd.randint(150, 200) for _ in range(B)]
+    Us = [rnd.randint(250, 350) for _ in range(B)]
+    case = make_case(B, Ts, Us, 5, list(range(dm + 1)), "f32", seed=80 + dm, sigma=0.05, reduction="sum",
+                     Tmax=200, U1max=351, name=f"bands_frames_dm{dm}")
+    loss, gt, gd, st = gpu_run(case.to("cuda"))
+    orc = oracle_run(case.to("cpu"))
+    check_loss(loss, orc, case.reduction, case.joint.dtype)
+    check_grads(gt, gd, orc, case.joint.dtype)
+    assert list(st.cpu().numpy()) == list(orc["status"])
+
+
+def test_bands_extended_range():
+    """Bands (80 utterances of 250-300 labels) with weights far below 2^-300: the
+    extended-range sweep in every tile."""
+    import random
+
+    rnd = random.Random(3)
+    B = 80
+    Ts = [rnd.randint(3, 12) for _ in range(B)]
+    Us = [rnd.randint(250, 300) for _ in range(B)]
+    case = make_case(B, Ts, Us, 5, [0, 1, 2, 3, 4], "f32", seed=90, scale=400.0, sigma=0.05, reduction="mean",
+                     Tmax=12, U1max=301, name="bands_extended")
+    loss, gt, gd, st = gpu_run(case.to("cuda"))
+    orc = oracle_run(case.to("cpu"))
+    check_loss(loss, orc, case.reduction, case.joint.dtype)
+    check_grads(gt, gd, orc, case.joint.dtype)
+    assert list(st.cpu().numpy()) == list(orc["status"])
 
 
 @pytest.mark.parametrize("dm,B", [(4, 80), (8, 60)])

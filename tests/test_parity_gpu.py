@@ -124,9 +124,9 @@ EDGE = {
                                                  reduction="mean_volume"),
     "max_duration_16": lambda: make_case(2, [40, 33], [7, 5], 10, [0, 1, 5, 16, 9], "f32", seed=47,
                                          reduction="sum", sigma=0.05),
-    "duration_8_banded": lambda: make_case(1, [30], [300], 21, list(range(9)), "bf16", seed=48,
+    "duration_8_long_labels": lambda: make_case(1, [30], [300], 21, list(range(9)), "bf16", seed=48,
                                               reduction="sum"),
-    "long_labels_banded": lambda: make_case(1, [12], [1100], 7, [0, 1, 2], "f32", seed=49, reduction="sum"),
+    "long_labels_1100": lambda: make_case(1, [12], [1100], 7, [0, 1, 2], "f32", seed=49, reduction="sum"),
     "wide_vocab_multipass": lambda: make_case(1, [5], [2], 40000, [0, 1, 2, 3, 4], "bf16", seed=50,
                                               reduction="none"),
     "tiny_vocab": lambda: make_case(2, [8, 6], [3, 2], 2, [0, 1, 2], "f32", seed=51, reduction="none",
@@ -138,8 +138,8 @@ EDGE = {
     # standard deviation 400: weights far below 2^-300 (extended-range lattice path)
     "huge_logits_extended_range": lambda: make_case(2, [40, 31], [12, 9], 17, [0, 1, 2], "f32", seed=54,
                                                     scale=400.0, reduction="none"),
-    # 300 labels with weights far below 2^-300: banded tiles in the extended-range sweep
-    "huge_logits_banded": lambda: make_case(1, [24], [300], 9, [0, 1, 2], "f32", seed=55, scale=400.0,
+    # 300 labels with weights far below 2^-300: linked columns redone in extended range
+    "huge_logits_long_labels": lambda: make_case(1, [24], [300], 9, [0, 1, 2], "f32", seed=55, scale=400.0,
                                                reduction="sum"),
     "plain_sweep_underflow_redo": _plain_sweep_underflow,
     "all_negative_logits_bf16": lambda: _all_negative("bf16"),
