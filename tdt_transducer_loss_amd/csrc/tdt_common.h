@@ -112,6 +112,9 @@ struct Params {
   // gradient pass; > 0 = zeroed by that many extra waves of the first lattice launch (they
   // overlap the sweeps) and skipped by the gradient pass
   int zrows;
+  // 1: the short-row statistics read the logits with nontemporal loads (a padded batch of
+  // more than twice the 256 MB last-level cache, whose reuse by the gradient pass is small)
+  int rows_nt;
 };
 
 // Column work-groups (2 B nU) up to which the workspace holds the links of long label

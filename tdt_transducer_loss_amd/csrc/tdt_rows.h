@@ -355,7 +355,7 @@ __device__ __forceinline__ double row16_sum(double x) {
 
 // Row statistics of row (b, t, u) by the 16 lanes of its quarter wave (valid: a row of its
 // utterance's lattice; the others load nothing and store nothing).
-template <typename TI, int CPL>
+template <typename TI, int CPL, bool NT>
 __device__ __forceinline__ void row_short_task(const Params& p, int b, int t, int u, bool valid, int l16) {
   constexpr int EPC = TI::kEpc;
   using ET = typename TI::T;
@@ -370,7 +370,8 @@ __device__ __forceinline__ void row_short_task(const Params& p, int b, int t, in
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = min(l16 + 16 * j, nch - 1);
-      const u32x4 x = *(const TDT_GLOBAL u32x4*)(rc.base + c);
+      const TDT_GLOBAL u32x4* a = (const TDT_GLOBAL u32x4*)(rc.base + c);
+      const u32x4 x = NT ? __builtin_nontemporal_load(a) : *a;
       v[j] = make_uint4(x.x, x.y, x.z, x.w);
     }
   }
@@ -589,7 +590,7 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
 // utterance leave at once); otherwise sixteen consecutive nodes per work-group (long label
 // sequences: more work-groups in flight).  B16 T400 U1max 101 V1025 fp16: 132 vs 155 us;
 // B2 T1000 U1max 1501 V1025 bf16: 1.32 vs 1.28 ms.
-template <typename TI, int CPL, bool FRAMES>
+template <typename TI, int CPL, bool FRAMES, bool NT>
 __global__ __launch_bounds__(256) void k_row_short(const Params p) {
   if (blockIdx.x == 0)  // the flags the node-weight kernel of this call sets
     for (int i = threadIdx.x; i < p.B; i += blockDim.x) p.xflag[i] = 0;
@@ -602,7 +603,7 @@ __global__ __launch_bounds__(256) void k_row_short(const Params p) {
     const int nrows = (int)U64 + 1;
     for (int u0 = 0; u0 < nrows; u0 += 16) {
       const int u = u0 + (int)(threadIdx.x >> 4);
-      row_short_task<TI, CPL>(p, b, t, u, u < nrows, l16);
+      row_short_task<TI, CPL, NT>(p, b, t, u, u < nrows, l16);
     }
   } else {
     const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
@@ -616,7 +617,7 @@ __global__ __launch_bounds__(256) void k_row_short(const Params p) {
     const int u = (int)(rem - (uint32_t)t * (uint32_t)p.U1max);
     const RowLens ln = row_lens(p, n0, nodes, b);
     const bool valid = node < nodes && utt_dims_ok(p, ln.T, ln.U) && t < (int)ln.T && u <= (int)ln.U;
-    row_short_task<TI, CPL>(p, (int)b, t, u, valid, l16);
+    row_short_task<TI, CPL, NT>(p, (int)b, t, u, valid, l16);
   }
 }
 
@@ -635,7 +636,8 @@ __global__ __launch_bounds__(256) void k_grad_short(const Params p) {
   const int l16 = threadIdx.x & 15;
   const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
   const uint32_t nodes = (uint32_t)p.B * per;
-  const uint32_t n0 = blockIdx.x * 16u;
+  // nodes in reverse order: the row-statistics pass ended on the last rows
+  const uint32_t n0 = (gridDim.x - 1u - blockIdx.x) * 16u;
   const uint32_t node = n0 + (threadIdx.x >> 4);
   const uint32_t nd = min(node, nodes - 1u);
   const uint32_t b = fdiv(nd, p.fd_tu1);
@@ -750,8 +752,10 @@ hipError_t launch_short_rows(const Params& p, bool aligned, hipStream_t st, int 
   const dim3 grid((unsigned)(frames ? (int64_t)p.B * p.Tmax : (nodes + 15) / 16));
 #define TDT_SR(N)                                                                                 \
   case N:                                                                                         \
-    if (frames) hipLaunchKernelGGL((k_row_short<TI, N, true>), grid, dim3(256), 0, st, p);        \
-    else if (which == 0) hipLaunchKernelGGL((k_row_short<TI, N, false>), grid, dim3(256), 0, st, p); \
+    if (frames && p.rows_nt) hipLaunchKernelGGL((k_row_short<TI, N, true, true>), grid, dim3(256), 0, st, p);        \
+    else if (frames) hipLaunchKernelGGL((k_row_short<TI, N, true, false>), grid, dim3(256), 0, st, p);              \
+    else if (which == 0 && p.rows_nt) hipLaunchKernelGGL((k_row_short<TI, N, false, true>), grid, dim3(256), 0, st, p); \
+    else if (which == 0) hipLaunchKernelGGL((k_row_short<TI, N, false, false>), grid, dim3(256), 0, st, p);         \
     else hipLaunchKernelGGL((k_grad_short<TI, N>), grid, dim3(256), 0, st, p);                    \
     break;
   switch (cpl) {
