@@ -302,14 +302,18 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   // short rows of a batch far larger than the last-level cache are streamed past it (the
   // gradient pass re-reads little of it from there): B16 Tmax400 U1max101 V1025 fp16
   // 0.617 -> 0.596 ms per step, B2 T1000 U1500 V1025 bf16 about 1% (both with the
-  // short-row gradient pass in reverse node order).  Long rows keep ordinary loads: there
-  // the gradient pass, walking the rows in reverse, finds the last-read ones in that cache
-  // (B4 T200 U40 V8193 bf16: row pass 96 -> 83 us with nontemporal loads, gradient pass
-  // 159 -> 178 us).
-  p.rows_nt = (double)B * (double)T_max * (double)U1_max * (double)(V + num_durations) * (double)elt >
-                      (double)(512u << 20)
-                  ? 1
-                  : 0;
+  // short-row gradient pass in reverse node order).  (Every long row nontemporal: B4 T200
+  // U40 V8193 bf16 row pass 96 -> 83 us but gradient pass 159 -> 178 us.)
+  const double row_bytes = (double)(V + num_durations) * (double)elt;
+  const double padded_nodes = (double)B * (double)T_max * (double)U1_max;
+  p.rows_nt = padded_nodes * row_bytes > 2.0 * tdt::kLastLevelCacheBytes ? 1 : 0;
+  // long rows: every row but those of the last 256 MB is streamed past the last-level cache;
+  // the gradient pass, walking the rows in reverse, starts on the ones kept there (B4 T200
+  // U40 V8193 bf16: 0.328 -> 0.307 ms per step, row pass 96 -> 85 us and gradient pass
+  // 160 -> 151 us; keeping 192 / 128 / 320 MB: 0.306 / 0.314 / 0.317 ms; fp32 0.591 ->
+  // 0.568 ms)
+  const double keep = tdt::kLastLevelCacheBytes / row_bytes;
+  p.nt_nodes = padded_nodes > keep ? (uint32_t)(padded_nodes - keep) : 0u;
   char* ws = (char*)workspace;
   p.part = (float*)(ws + L.off_part);
   p.stat = (float2*)(ws + L.off_stat);

@@ -115,7 +115,14 @@ struct Params {
   // 1: the short-row statistics read the logits with nontemporal loads (a padded batch of
   // more than twice the 256 MB last-level cache, whose reuse by the gradient pass is small)
   int rows_nt;
+  // long-row statistics: the rows of nodes below nt_nodes (all but the last 256 MB of the
+  // padded batch in memory order) are read with nontemporal loads, the rest with ordinary
+  // ones, which leave them in the last-level cache for the gradient pass (it starts there)
+  uint32_t nt_nodes;
 };
+
+// bytes of the GPU's last-level cache (MI355X Infinity Cache)
+constexpr double kLastLevelCacheBytes = 256.0 * 1024 * 1024;
 
 // Column work-groups (2 B nU) up to which the workspace holds the links of long label
 // sequences run as linked columns (the launch also checks that the GPU holds them all at

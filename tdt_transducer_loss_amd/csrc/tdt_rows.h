@@ -143,6 +143,7 @@ __device__ __forceinline__ uint4 mask_slots(uint4 c, int lo, int hi) {
 template <typename TI, int NCH>
 struct RowTask {
   bool ok;  // a node of its utterance's lattice (wave-uniform)
+  bool nt;  // its row is read with nontemporal loads (node < nt_nodes)
   int seg, c0, nch, head;
   int64_t pos;  // workspace position of the node
   __amdgpu_buffer_rsrc_t rsrc;
@@ -156,6 +157,7 @@ __device__ __forceinline__ void row_task_load(const Params& p, uint32_t g, uint3
   constexpr int EPC = TI::kEpc;
   using ET = typename TI::T;
   tk.ok = false;
+  tk.nt = false;
   // a task that is no node of its utterance loads nothing: an empty buffer range
   tk.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.tok, (short)0, 0, 0x00020000);
   tk.c0 = 0;
@@ -173,6 +175,7 @@ __device__ __forceinline__ void row_task_load(const Params& p, uint32_t g, uint3
   const int T = (int)T64, U = (int)U64;
   if (t >= T || u > U) return;
   tk.ok = true;
+  tk.nt = node < p.nt_nodes;
   tk.seg = seg;
   tk.pos = node_pos(p, (int)b, t, u);
   const int V = p.V;
@@ -188,15 +191,24 @@ __device__ __forceinline__ void row_task_load(const Params& p, uint32_t g, uint3
   tk.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)rc.base, (short)0, nch * 16, 0x00020000);
 }
 
-// The chunk loads of a task; every window is loaded, with no branch (a task without a
-// node has an empty range and reads zeros without a memory access), so the loads of
-// consecutive tasks issue back to back.
+// The chunk loads of a task; every window is loaded (a task without a node has an empty
+// range and reads zeros without a memory access), so the loads of consecutive tasks issue
+// back to back.  Nontemporal or ordinary by the task's row (a wave-uniform branch; the
+// cache policy is an immediate operand, so the two loops stay apart).
 template <typename TI, int NCH>
 __device__ __forceinline__ void row_task_issue(int lane, RowTask<TI, NCH>& tk) {
+  if (tk.nt) {
 #pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(tk.rsrc, (tk.c0 + lane + 64 * j) * 16, 0, 0);
-    tk.v[j] = make_uint4(x.x, x.y, x.z, x.w);
+    for (int j = 0; j < NCH; ++j) {
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(tk.rsrc, (tk.c0 + lane + 64 * j) * 16, 0, 2);
+      tk.v[j] = make_uint4(x.x, x.y, x.z, x.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(tk.rsrc, (tk.c0 + lane + 64 * j) * 16, 0, 0);
+      tk.v[j] = make_uint4(x.x, x.y, x.z, x.w);
+    }
   }
 }
 
