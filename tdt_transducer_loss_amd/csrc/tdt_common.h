@@ -85,7 +85,9 @@ struct Params {
   void* gdur;
   int64_t gds0, gds1, gds2;
   // workspace, per node position
-  float* part;    // [nseg] float2 per row segment: its shift c and its sum 2^(x log2e - c), see k_row_partial
+  float* part;    // [nseg] float2 per row segment: its shift c and its sum 2^(x log2e - c), see
+                  //   k_row_partial; node-major order (b, t, u), unlike the other per-node
+                  //   arrays, so that the row passes write consecutive rows' records together
   float2* stat;   // row statistics (c, K) written by the node weights, lse = row_lse(c, K)
   double* lg;     // [LG]: l_blank - sigma, l_label - sigma, lambda[D] (log-softmax of the
                   //   durations); the coefficient kernel overwrites it with the RS floats

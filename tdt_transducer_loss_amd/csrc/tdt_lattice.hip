@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void k_node_weights(const Params p) {
     // their shifts in base-2 units (see k_row_partial).  Each float32 partial sum is
     // rescaled to the common shift in float32 and summed in float64.  A NaN partial
     // (logits beyond the float range of the shift) propagates.
-    const float* part = p.part + pos * 2 * p.nseg;
+    const float* part = p.part + (((int64_t)b * p.Tmax + t) * p.U1max + u) * 2 * p.nseg;  // node-major
     float mx = -__builtin_inff();
     for (int s2 = 0; s2 < p.nseg; ++s2)
       if (!(part[2 * s2 + 1] <= 0.f)) mx = fmaxf(mx, part[2 * s2]);

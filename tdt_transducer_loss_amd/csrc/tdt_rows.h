@@ -145,7 +145,7 @@ struct RowTask {
   bool ok;  // a node of its utterance's lattice (wave-uniform)
   bool nt;  // its row is read with nontemporal loads (node < nt_nodes)
   int seg, c0, nch, head;
-  int64_t pos;  // workspace position of the node
+  int64_t pos;  // node-major index (b, t, u) of the node: its row partials' place
   __amdgpu_buffer_rsrc_t rsrc;
   uint4 v[NCH];
 };
@@ -177,7 +177,7 @@ __device__ __forceinline__ void row_task_load(const Params& p, uint32_t g, uint3
   tk.ok = true;
   tk.nt = node < p.nt_nodes;
   tk.seg = seg;
-  tk.pos = node_pos(p, (int)b, t, u);
+  tk.pos = node;  // node-major index (b, t, u) of the padded box
   const int V = p.V;
   const ET* row = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
   const RowCover rc = row_cover<TI>(row, V);
@@ -440,7 +440,8 @@ __device__ __forceinline__ void row_short_task(const Params& p, int b, int t, in
   double S = row16_sum((double)acc);
   if (!empty && !(__builtin_fabsf(c) < __builtin_inff())) S = __builtin_nan("");  // see row_task_finish
   if (valid && l16 == 0) {
-    float* part = p.part + node_pos(p, (int)b, t, u) * 2;  // one segment per row
+    // one segment per row, in node-major order (consecutive rows, consecutive records)
+    float* part = p.part + (((int64_t)b * p.Tmax + t) * p.U1max + u) * 2;
     part[0] = empty ? -__builtin_inff() : c;
     part[1] = (float)S;
   }
