@@ -1398,18 +1398,24 @@ __global__ __launch_bounds__(256) void k_coef(const Params p) {
           Ext bt = ext_zero();
           if (t + d < T) bt = xrec_get(p.br, node_pos(p, b, t + d, u));
           else if (t + d == T && u == U) bt = ext_one();
+          // the plain weight is loaded whether or not the destination holds a beta, so that
+          // the loads of a node issue together
+          const int sl = d - 1;
+          const double wp = plain ? pw[(sl >> 1) * pstride + (sl & 1)] : 0.0;
           if (bt.m != 0.0) {
-            const int sl = d - 1;
-            const Ext w = plain ? Ext{pw[(sl >> 1) * pstride + (sl & 1)], 0} : ext_exp(lb + lam[d]);
+            const Ext w = plain ? Ext{wp, 0} : ext_exp(lb + lam[d]);
             gb = ext_to_double(Ext{a.m * w.m * bt.m * rP, a.e + w.e + bt.e - Pe});
           }
         }
-        if (u < U && t + d < T) {
-          const Ext bt = xrec_get(p.br, node_pos(p, b, t + d, u + 1));
-          if (bt.m != 0.0) {
-            const int sl = DM + d;
-            const Ext w = plain ? Ext{pw[(sl >> 1) * pstride + (sl & 1)], 0} : ext_exp(ly + lam[d]);
-            gy = ext_to_double(Ext{a.m * w.m * bt.m * rP, a.e + w.e + bt.e - Pe});
+        {
+          const int sl = DM + d;
+          const double wp = plain ? pw[(sl >> 1) * pstride + (sl & 1)] : 0.0;
+          if (u < U && t + d < T) {
+            const Ext bt = xrec_get(p.br, node_pos(p, b, t + d, u + 1));
+            if (bt.m != 0.0) {
+              const Ext w = plain ? Ext{wp, 0} : ext_exp(ly + lam[d]);
+              gy = ext_to_double(Ext{a.m * w.m * bt.m * rP, a.e + w.e + bt.e - Pe});
+            }
           }
         }
       }
