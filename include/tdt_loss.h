@@ -132,6 +132,13 @@ int tdt_loss_workspace_size(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_
  *                    256-byte aligned; its contents need no initialisation and are
  *                    overwritten.  Calls that share a workspace must not overlap.
  * Returns TDT_OK or a negative TDT_ERR_* code.
+ *
+ * Long label sequences run as label columns in work-groups that wait on each other; they
+ * are launched only when the GPU holds all of them at once, and every wait is bounded
+ * (about 0.1 s), after which the utterance is recomputed by the extended-range sweeps, so
+ * work on other streams can slow a call down but not stop it.  The environment variable
+ * TDT_LINK_SPIN_LIMIT (read at each call; for tests) lowers that bound to the given
+ * number of polls, forcing that recomputation.
  */
 int tdt_loss_fwd_bwd(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,
                      const void* logits, const int64_t* logits_strides, const void* dur_logits,

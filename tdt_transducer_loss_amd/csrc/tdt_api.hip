@@ -5,6 +5,7 @@
 //   backward call on the same workspace: coefficients -> gradient).
 #include <algorithm>
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -314,6 +315,11 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   // 0.568 ms)
   const double keep = tdt::kLastLevelCacheBytes / row_bytes;
   p.nt_nodes = padded_nodes > keep ? (uint32_t)(padded_nodes - keep) : 0u;
+  p.spin = 1 << 20;
+  if (const char* e = getenv("TDT_LINK_SPIN_LIMIT")) {  // tests: force the waits to give up
+    const long v = strtol(e, nullptr, 10);
+    if (v >= 1 && v < (1 << 20)) p.spin = (int)v;
+  }
   char* ws = (char*)workspace;
   p.part = (float*)(ws + L.off_part);
   p.stat = (float2*)(ws + L.off_stat);

@@ -121,6 +121,10 @@ struct Params {
   // padded batch in memory order) are read with nontemporal loads, the rest with ordinary
   // ones, which leave them in the last-level cache for the gradient pass (it starts there)
   uint32_t nt_nodes;
+  // iterations a wait between lattice waves or work-groups may take before it gives up and
+  // the utterance is redone in extended range (2^20, about 0.1 s; the environment variable
+  // TDT_LINK_SPIN_LIMIT lowers it, so that tests can force that path)
+  int spin;
 };
 
 // bytes of the GPU's last-level cache (MI355X Infinity Cache)

@@ -384,6 +384,7 @@ struct LinkCtx {
   int in, out;    // link read (lane 0 for alpha, lane 63 for beta), link written; -1: none
   int in_last;    // the last sequence number the producer of `in` writes a value for
   int broken;     // a wait ran out
+  int spin;       // iterations a wait may take (Params::spin)
 };
 // Ring slots and progress words are accessed as volatile LDS words: the compiler keeps
 // their order, and the LDS performs the accesses of one wave in order, so a consumer that
@@ -398,10 +399,10 @@ __device__ __forceinline__ void link_store(int* c, int v) { *(TDT_LDS volatile i
 __device__ __forceinline__ TDT_LDS volatile LinkSlot* link_slot(int i, int sq) {
   return (TDT_LDS volatile LinkSlot*)&g_link.ring[i][sq & (kLinkRing - 1)];
 }
-// wait until *c >= target (about 0.1 s at most)
+// wait until *c >= target (at most lk.spin iterations: about 0.1 s by default)
 __device__ __forceinline__ void link_wait(const int* c, int target, LinkCtx& lk) {
   if (lk.broken) return;
-  for (int it = 0; it < (1 << 20); ++it) {
+  for (int it = 0; it < lk.spin; ++it) {
     if (link_load(c) >= target) return;
     __builtin_amdgcn_s_sleep(2);
   }
@@ -1021,7 +1022,7 @@ __global__ __launch_bounds__(64) void k_tiles(const Params p, int band) {
     if (make_tile(p, b, T, U, i, j, 64 * R, tl)) {
       bool redo = true;
       if constexpr (plain_buffers<DM, R>() >= 2) {
-        LinkCtx none{-1, -1, 0, 0};
+        LinkCtx none{-1, -1, 0, 0, p.spin};
         if (p.pw && !p.xflag[b]) redo = dir == 0 ? alpha_plain<DM, R, BOUND, false>(p, tl, lane, none)
                                                  : beta_plain<DM, R, BOUND, false>(p, tl, lane, &P, none);
       }
@@ -1090,7 +1091,7 @@ __global__ __launch_bounds__(256) void k_tiles_link(const Params p) {
     redo = true;
     if constexpr (plain_buffers<DM, 1>() >= 2) {
       if (p.pw && !p.xflag[b]) {
-        LinkCtx lk{-1, -1, 0, 0};
+        LinkCtx lk{-1, -1, 0, 0, p.spin};
         if (dir == 0) {
           lk.in = w > 0 ? w - 1 : -1;
           lk.out = w + 1 < nw ? w : -1;
@@ -1149,7 +1150,7 @@ __device__ __forceinline__ void xstore_f64(double* a, double v) {
 // the global ring, and once every one of those stores has completed (s_waitcnt) the
 // progress word is raised, then LDS ring 1's places are freed.  The global rings hold
 // every sequence number of a link, so they need no flow control.  Returns false when no
-// slot moved for about 0.1 s (a neighbour that did not run).
+// slot moved for p.spin polls (about 0.1 s by default: a neighbour that did not run).
 __device__ bool column_bridge(const Params& p, int b, int dir, int j, int ncol, int T, int U, int lane) {
   const int in_link = dir == 0 ? (j > 0 ? j - 1 : -1) : (j + 1 < ncol ? j : -1);
   const int out_link = dir == 0 ? (j + 1 < ncol ? j : -1) : (j > 0 ? j - 1 : -1);
@@ -1218,7 +1219,7 @@ __device__ bool column_bridge(const Params& p, int b, int dir, int j, int ncol, 
     if (moved) {
       idle = 0;
     } else {
-      if (++idle > (1 << 20)) return false;
+      if (++idle > p.spin) return false;
       __builtin_amdgcn_s_sleep(2);
     }
   }
@@ -1275,7 +1276,7 @@ __global__ __launch_bounds__(128) void k_cols(const Params p) {
       redo = true;
       if constexpr (plain_buffers<DM, 1>() >= 2) {
         if (plain) {
-          LinkCtx lk{-1, -1, 0, 0};
+          LinkCtx lk{-1, -1, 0, 0, p.spin};
           if (dir == 0) {
             lk.in = j > 0 ? 0 : -1;
             lk.out = j + 1 < ncol ? 1 : -1;

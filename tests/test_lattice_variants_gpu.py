@@ -184,3 +184,14 @@ def test_many_utterances_long_labels(dm, B):
     check_loss(loss, orc, case.reduction, case.joint.dtype)
     check_grads(gt, gd, orc, case.joint.dtype)
     assert list(st.cpu().numpy()) == list(orc["status"])
+
+
+@pytest.mark.parametrize("dm", [4, 8])
+@pytest.mark.parametrize("U", [100, 220, 500, 1200])
+def test_link_waits_give_up(dm, U, monkeypatch):
+    """Every wait between linked waves or column work-groups bounded to one poll (set from
+    the host through TDT_LINK_SPIN_LIMIT): links break, the plain sweeps' results are
+    dropped, and the extended-range redo (wave 0 of the work-group, or the last column of
+    the utterance to finish) must still give the oracle's loss and gradients."""
+    monkeypatch.setenv("TDT_LINK_SPIN_LIMIT", "1")
+    _parity(_case(dm, U, "f32", seed=500 + U + dm).to("cuda"))
