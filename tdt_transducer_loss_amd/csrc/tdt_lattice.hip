@@ -1228,12 +1228,12 @@ __device__ bool column_bridge(const Params& p, int b, int dir, int j, int ncol, 
 
 // Long label sequences: one work-group of two waves per (utterance, direction, column of
 // 64 labels over every frame), launched only when the GPU holds all of them at once (so a
-// column never waits for a neighbour that has not started; the waits are bounded anyway).  Wave 0 sweeps
-// the column as a wave of k_tiles_link does, through LDS links (ring 0 in, ring 1 out);
-// wave 1 carries those links to the neighbouring columns' work-groups (column_bridge), so
-// the columns run at once, each behind its producer by about 64 diagonals plus the
-// bridge, and the utterance takes about T + U steps instead of one launch per band of
-// tiles.  A column whose plain sweep went out of range, or whose links stalled, flags its
+// column never waits for a neighbour that has not started; the waits are bounded anyway).
+// Wave 0 sweeps the column as a wave of k_tiles_link does, through LDS links (ring 0 in,
+// ring 1 out); wave 1 carries those links to the neighbouring columns' work-groups
+// (column_bridge), so the columns run at once, each behind its producer by about 64
+// diagonals plus the bridge, and the utterance takes about T + U steps instead of one
+// launch per band of tiles.  A column whose plain sweep went out of range, or whose links stalled, flags its
 // (utterance, direction); the last of the columns to finish redoes it in extended range,
 // strip after strip, and for beta finishes the utterance.  Extra work-groups zero the
 // gradient's padding rows (as in k_tiles).  The tiles hold every frame (p.TT = Tmax).
