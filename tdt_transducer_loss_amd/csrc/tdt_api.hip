@@ -1,8 +1,9 @@
 // Host side of the C ABI declared in include/tdt_loss.h: argument validation, workspace
 // layout and the launch sequence.  On the caller's stream the kernels run
 //   row partials -> node weights -> lattice (alpha || beta) -> coefficients and loss
-//   reduction -> gradient  (forward only: ... -> lattice -> loss reduction; a later
-//   backward call on the same workspace: coefficients -> gradient).
+//   reduction -> gradient  (short rows: the gradient pass computes the coefficients and
+//   reduces the loss itself; forward only: ... -> lattice -> loss reduction; a later
+//   backward call on the same workspace: [coefficients ->] gradient).
 #include <algorithm>
 #include <math.h>
 #include <stdlib.h>
@@ -399,11 +400,14 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
   if (phases) rec(2);
   if (tdt::launch_lattice_side(p, 1, st) != hipSuccess) return TDT_ERR_HIP;
   if (phases) rec(3);
-  if (grads && tdt::launch_lattice_side(p, 2, st) != hipSuccess) return TDT_ERR_HIP;
+  // coefficients (and the loss reduction) by a kernel of their own for long rows; the
+  // short-row gradient pass computes them itself
+  const bool coef = grads && !tdt::short_grad_rows(p, aligned);
+  if (coef && tdt::launch_lattice_side(p, 2, st) != hipSuccess) return TDT_ERR_HIP;
   rec(phases ? 4 : 2);
   if (grads && launch_rows(p, aligned, st, 1) != hipSuccess) return TDT_ERR_HIP;
   rec(phases ? 5 : 3);
-  // with gradients the coefficient kernel has reduced the loss already
+  // with gradients the coefficient kernel or the gradient pass has reduced the loss already
   if (!grads && tdt::launch_lattice_side(p, 3, st) != hipSuccess) return TDT_ERR_HIP;
   rec(phases ? 6 : 1);
   return TDT_OK;
@@ -459,7 +463,7 @@ extern "C" int tdt_loss_backward(int32_t dtype, int64_t B, int64_t T_max, int64_
   if (rc != TDT_OK) return rc;
   p.gscale = grad_loss;
   hipStream_t st = (hipStream_t)stream;
-  if (tdt::launch_lattice_side(p, 2, st) != hipSuccess) return TDT_ERR_HIP;
+  if (!tdt::short_grad_rows(p, aligned) && tdt::launch_lattice_side(p, 2, st) != hipSuccess) return TDT_ERR_HIP;
   if (launch_rows(p, aligned, st, 1) != hipSuccess) return TDT_ERR_HIP;
   return TDT_OK;
 }

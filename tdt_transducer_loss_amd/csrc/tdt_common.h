@@ -255,6 +255,25 @@ __device__ __forceinline__ double ext_to_double(Ext a) {
   return ldexp(a.m, e);
 }
 
+// alpha / beta record of a node, normalised (the plain sweeps store unnormalised values)
+__device__ __forceinline__ Ext xrec_get(const char* base, int64_t pos) {
+  const char* r = base + pos * 16;
+  return ext_norm(*(const double*)r, *(const int*)(r + 8));
+}
+
+// The reduced loss from every utterance's log P and reduction weight (one thread).
+__device__ inline void reduce_loss(const Params& p) {
+  double s = 0.0;
+  for (int b = 0; b < p.B; ++b) {
+    const double Lb = -p.logp[b];
+    if (p.red == 0)
+      p.loss[b] = (float)Lb;
+    else
+      s += p.wts[b] * Lb;
+  }
+  if (p.red != 0) p.loss[0] = (float)s;
+}
+
 // Sum of N extended values: align to the largest exponent, add, renormalise.
 template <int N>
 __device__ __forceinline__ Ext ext_sum(const Ext (&t)[N]) {

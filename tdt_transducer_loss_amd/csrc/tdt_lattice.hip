@@ -1334,23 +1334,6 @@ __global__ __launch_bounds__(128) void k_cols(const Params p) {
 //   c_blank, c_label = sums over blank / label moves, c_dur(d) = moves of duration d,
 //   grad h_blank = w (O softmax(h)_blank - c_blank), grad h_y = w (O softmax(h)_y - c_label),
 //   grad g_d = w (O softmax(g)_d - c_dur(d)),  other columns w O softmax(h)_v (streamed).
-__device__ void reduce_loss(const Params& p) {
-  double s = 0.0;
-  for (int b = 0; b < p.B; ++b) {
-    const double Lb = -p.logp[b];
-    if (p.red == 0)
-      p.loss[b] = (float)Lb;
-    else
-      s += p.wts[b] * Lb;
-  }
-  if (p.red != 0) p.loss[0] = (float)s;
-}
-
-// alpha / beta record of a node, normalised (the plain sweeps store unnormalised values)
-__device__ __forceinline__ Ext xrec_get(const char* base, int64_t pos) {
-  const char* r = base + pos * 16;
-  return ext_norm(*(const double*)r, *(const int*)(r + 8));
-}
 
 // One lane per position of the padded box (as in the node weights).  Utterances whose
 // move weights all lie in [2^-300, 2^300] read the plain weights the lattice read; the

@@ -634,9 +634,109 @@ __global__ __launch_bounds__(256) void k_row_short(const Params p) {
   }
 }
 
+// ---- gradient coefficients of a node, inside the short-row gradient pass ----
+// Node n = (t, u) of an utterance with a lattice, by the 16 lanes of its quarter wave:
+// lane i < D takes duration index i (value d) and the posteriors of the two moves of
+// duration d out of n, blank (d >= 1, to (t + d, u)) and label (to (t + d, u + 1)),
+//   gamma(e) = alpha(n) W(e) beta(dest e) / P
+// (W: the plain weight the lattice read, or, for an utterance whose weights left the
+// plain range, the weight rebuilt in extended range from its log-domain ingredients).
+// Sums over the quarter give c_blank, c_label and O = c_blank + c_label (every move out
+// of n); then
+//   grad h_blank = w (O softmax(h)_blank - c_blank),  grad h_y = w (O softmax(h)_y - c_label),
+//   grad g_d = w (O softmax(g)_d - c_d)   (lane i, its own duration),
+// and every other column w O softmax(h)_v, streamed from grad_val's A and m.  The long-row
+// gradient pass, whose waves each take one segment of a row, reads the same numbers from
+// the per-node record the coefficient kernel writes.  Every lane of the quarter calls it
+// (the sums run across the quarter); a node that is not `valid` gets zeros.
+struct NodeGrad {
+  float A, m, Gb, Gy;  // grad_val's scale and shift; the blank and label column gradients
+  int ycol;            // the label column (-1: none, or the label is the blank)
+  float gd;            // lane i < D: the gradient of duration logit i
+};
+
+__device__ __forceinline__ NodeGrad node_grad(const Params& p, int b, int t, int u, int T, int U, int li,
+                                              bool valid) {
+  const bool has = valid && li < p.D;
+  int d = 0;  // the lane's duration value (no dynamic index into the kernel arguments)
+#pragma unroll
+  for (int j = 0; j < kMaxD; ++j) d = li == j ? p.dval[j] : d;
+  const int64_t pos = node_pos(p, b, t, u);
+  double gb = 0.0, gy = 0.0, lb = 0.0, ly = 0.0, lam = -__builtin_inf();
+  if (valid) {
+    const double* lgp = p.lg + pos * p.LG;
+    lb = lgp[0];
+    ly = lgp[1];
+    if (has) lam = lgp[2 + li];
+  }
+  if (has) {
+    const bool plain = p.pw != nullptr && p.xflag[b] == 0;
+    const Ext a = xrec_get(p.ar, pos);
+    const double rP = 1.0 / p.pm[b];
+    const int Pe = p.pe[b];
+    // the node's plain weights: slot pairs len(k) + 3 entries apart in its diagonal's block
+    const int k = t + u, len = diag_len(p, k);
+    const double* pw =
+        plain ? p.pw + ((int64_t)b * pw_utt_entries(p.NP, p.box, p.KD) + pw_block(p, k) + (u - diag_ulo(p, k))) * 2
+              : nullptr;
+    const int64_t pstride = (int64_t)(len + 3) * 2;  // doubles between slot pairs
+    if (d >= 1) {
+      Ext bt = ext_zero();
+      if (t + d < T) bt = xrec_get(p.br, node_pos(p, b, t + d, u));
+      else if (t + d == T && u == U) bt = ext_one();
+      const int sl = d - 1;
+      const double wp = plain ? pw[(sl >> 1) * pstride + (sl & 1)] : 0.0;
+      if (bt.m != 0.0) {
+        const Ext w = plain ? Ext{wp, 0} : ext_exp(lb + lam);
+        gb = ext_to_double(Ext{a.m * w.m * bt.m * rP, a.e + w.e + bt.e - Pe});
+      }
+    }
+    const int sl = p.DM + d;
+    const double wp = plain ? pw[(sl >> 1) * pstride + (sl & 1)] : 0.0;
+    if (u < U && t + d < T) {
+      const Ext bt = xrec_get(p.br, node_pos(p, b, t + d, u + 1));
+      if (bt.m != 0.0) {
+        const Ext w = plain ? Ext{wp, 0} : ext_exp(ly + lam);
+        gy = ext_to_double(Ext{a.m * w.m * bt.m * rP, a.e + w.e + bt.e - Pe});
+      }
+    }
+  }
+  const double cb = row16_sum(gb), cl = row16_sum(gy);
+  NodeGrad g{0.f, 0.f, 0.f, 0.f, -1, 0.f};
+  if (valid) {
+    const double O = cb + cl;
+    const double wgt = p.gscale ? p.wts[b] * (double)p.gscale[p.red == 0 ? b : 0] : p.wts[b];
+    // softmax(h)_blank, softmax(h)_label (sigma added back)
+    const double sb = exp(lb + p.sigma), sy = exp(ly + p.sigma);
+    const float2 rs = p.stat[pos];
+    int y = -1;
+    if (u < U) y = (int)p.labels[(int64_t)b * p.lab_stride + u];
+    double Gb = wgt * (O * sb - cb);
+    const double Gy = wgt * (O * sy - cl);
+    if (y == p.blank) {  // both corrections land on the blank column
+      Gb -= wgt * cl;
+      y = -1;
+    }
+    const double wO = wgt * O;
+    if (p.dtype == 0) {  // A = w O 2^-K and the row maximum
+      g.A = (float)(wO * exp2(-(double)rs.y));
+      g.m = rs.x;
+    } else {  // the sign of w O and C = c + K - log2|w O| (base 2)
+      g.A = wO < 0.0 ? -1.f : 1.f;
+      g.m = (float)((double)rs.x + (double)rs.y - log2(fabs(wO)));
+    }
+    g.Gb = (float)Gb;
+    g.Gy = (float)Gy;
+    g.ycol = y;
+    if (has) g.gd = (float)(wgt * (O * exp(lam) - (gb + gy)));
+  }
+  return g;
+}
+
 // Gradient of short rows (as k_row_short: a quarter wave per row, sixteen consecutive
-// nodes per block, natural order), for logits and gradient rows with the same address
-// modulo 16 bytes.  The chunks are counted from the gradient row's 128-byte line, so each
+// nodes per block, the blocks in reverse order), for logits and gradient rows with the
+// same address modulo 16 bytes.  Each quarter computes its node's coefficients
+// (node_grad), and the first block reduces the loss.  The chunks are counted from the gradient row's 128-byte line, so each
 // store instruction writes whole lines (16 lanes x 16 bytes, line-aligned) except at the
 // row's ends; the logits are read at the same offsets.  Whole chunks inside the row are
 // stored as 16-byte nontemporal stores, the row's first and last chunk element by element.
@@ -646,6 +746,8 @@ template <typename TI, int CPL>
 __global__ __launch_bounds__(256) void k_grad_short(const Params p) {
   constexpr int EPC = TI::kEpc;
   using ET = typename TI::T;
+  // the loss of the batch (the lattice has finished every log P), unless the call writes none
+  if (p.loss && blockIdx.x == 0 && threadIdx.x == 0) reduce_loss(p);
   const int l16 = threadIdx.x & 15;
   const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
   const uint32_t nodes = (uint32_t)p.B * per;
@@ -664,17 +766,9 @@ __global__ __launch_bounds__(256) void k_grad_short(const Params p) {
   // rows outside the utterance's lattice are skipped when the lattice launch has zeroed them
   const bool write = node < nodes && (inside || p.zrows == 0);
   const int V = p.V;
-  float A = 0.f, m = 0.f, Gb = 0.f, Gy = 0.f;
-  int ycol = -1;
-  const float* rec = nullptr;
-  if (valid) {
-    rec = (const float*)(p.lg + node_pos(p, (int)b, t, u) * p.LG);
-    A = rec[0];
-    m = rec[1];
-    Gb = rec[2];
-    Gy = rec[3];
-    ycol = __float_as_int(rec[4]);
-  }
+  // the node's coefficients from the lattice (every lane of the quarter takes part)
+  const NodeGrad ng = node_grad(p, (int)b, t, u, (int)ln.T, (int)ln.U, l16, valid);
+  const float A = ng.A, m = ng.m;
   ET* orow = (ET*)p.gtok + ((int64_t)b * p.gs0 + (int64_t)t * p.gs1 + (int64_t)u * p.gs2);
   const ET* irow = (const ET*)p.tok + ((int64_t)b * p.ts0 + (int64_t)t * p.ts1 + (int64_t)u * p.ts2);
   const uintptr_t oa = (uintptr_t)orow;
@@ -725,13 +819,11 @@ __global__ __launch_bounds__(256) void k_grad_short(const Params p) {
       }
     }
     if (valid) {
-      if (((head + p.blank) / EPC & 15) == l16) TI::store(orow, p.blank, Gb);
-      if (ycol >= 0 && ((head + ycol) / EPC & 15) == l16) TI::store(orow, ycol, Gy);
+      if (((head + p.blank) / EPC & 15) == l16) TI::store(orow, p.blank, ng.Gb);
+      if (ng.ycol >= 0 && ((head + ng.ycol) / EPC & 15) == l16) TI::store(orow, ng.ycol, ng.Gy);
     }
-    if (l16 < p.D) {
-      const float gd = valid ? rec[5 + l16] : 0.f;
-      TI::store(p.gdur, (int64_t)b * p.gds0 + (int64_t)t * p.gds1 + (int64_t)u * p.gds2 + l16, gd);
-    }
+    if (l16 < p.D)
+      TI::store(p.gdur, (int64_t)b * p.gds0 + (int64_t)t * p.gds1 + (int64_t)u * p.gds2 + l16, ng.gd);
   }
 }
 
@@ -780,12 +872,20 @@ hipError_t launch_short_rows(const Params& p, bool aligned, hipStream_t st, int 
   return hipGetLastError();
 }
 
+// The gradient pass takes the short-row kernel, which computes the node coefficients
+// itself (the coefficient kernel is then left out): rows of at most kShortRowChunks
+// chunks counted from their 128-byte line, logits and gradient rows equal modulo 16 bytes.
+inline bool short_grad_rows(const Params& p, bool aligned) {
+  const int64_t epc = p.dtype == 0 ? 4 : 8;  // elements per 16-byte chunk
+  return aligned && ((int64_t)p.V + epc - 1) / epc + 8 <= kShortRowChunks;
+}
+
 template <typename TI>
 hipError_t launch_rows_t(const Params& p, bool aligned, hipStream_t st, int which) {
   // chunks of a row's cover: from its 16-byte chunk (row statistics) or from its 128-byte
   // line (gradient)
   const int64_t chunks = ((int64_t)p.V + TI::kEpc - 1) / TI::kEpc + (which == 0 ? 1 : 8);
-  if (chunks <= kShortRowChunks && (which == 0 || aligned))
+  if (which == 0 ? chunks <= kShortRowChunks : short_grad_rows(p, aligned))
     return launch_short_rows<TI>(p, aligned, st, which, (int)((chunks + 15) / 16));
   const int nch = which == 0 ? p.nch : p.gnch;
   const int64_t nodes = (int64_t)p.B * p.Tmax * p.U1max;  // both passes walk the padded rows
