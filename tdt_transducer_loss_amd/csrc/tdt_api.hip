@@ -381,9 +381,11 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
   };
   // with gradients, extra waves of the first lattice launch zero the padding rows of the
   // gradient while the sweeps run (only for a gradient that is one contiguous joint tensor
-  // [B, Tmax, U1max, V + D]: the padding rows of a frame are then one byte range).  128
-  // waves: with more, the sweeps (bound by the latency of their weight loads) slow down by
-  // more than the zeroing gains
+  // [B, Tmax, U1max, V + D]: the padding rows of a frame are then one byte range).  192
+  // waves: B16 Tmax400 U1max101 V1025 fp16 (774 MB of padding rows beside the sweeps)
+  // 0.603 / 0.575 / 0.546 / 0.558 / 0.556 / 0.591 ms per step with 128 / 160 / 192 / 256 /
+  // 384 / 512 waves (more waves slow the sweeps, bound by the latency of their weight
+  // loads, by more than the zeroing gains)
   if (grads) {
     const size_t elt = dtype == 0 ? 4 : 2;
     const int64_t* g = grad_strides;
@@ -391,7 +393,7 @@ int fwd_bwd_impl(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_
     const bool joint = g[2] == V + num_durations && g[1] == U1_max * g[2] && g[0] == T_max * g[1] &&
                        gd[0] == g[0] && gd[1] == g[1] && gd[2] == g[2] &&
                        (const char*)grad_dur_logits == (const char*)grad_logits + V * elt;
-    if (joint) p.zrows = (int)std::min<int64_t>(128, B * T_max);
+    if (joint) p.zrows = (int)std::min<int64_t>(192, B * T_max);
   }
   rec(0);
   if (launch_rows(p, aligned, st, 0) != hipSuccess) return TDT_ERR_HIP;
