@@ -597,27 +597,28 @@ __global__ __launch_bounds__(256) void k_grad(const Params p) {
   }
 }
 
-// Row statistics of short rows.  FRAMES: one work-group per frame (b, t) of the padded
-// box, its 256 lanes walking the frame's rows u = 0 .. U sixteen at a time (a quarter wave
-// per row), so that a ragged batch pays for its valid rows only (frames outside the
-// utterance leave at once); otherwise sixteen consecutive nodes per work-group (long label
-// sequences: more work-groups in flight).  B16 T400 U1max 101 V1025 fp16: 132 vs 155 us;
-// B2 T1000 U1max 1501 V1025 bf16: 1.32 vs 1.28 ms.
+// Row statistics of short rows, a quarter wave per row.  FRAMES (up to 256 labels): one
+// work-group per sixteen rows u = 16 c .. 16 c + 15 of a frame (b, t) of the padded box, so
+// that a ragged batch pays for its valid rows only (pieces outside the utterance leave at
+// once); otherwise sixteen consecutive nodes per work-group (long label sequences: more
+// work-groups in flight).  B16 T400 U1max 101 V1025 fp16: 92 us, against 104 us for one
+// work-group per frame walking its rows and 155 us for sixteen consecutive nodes; B2 T1000
+// U1max 1501 V1025 bf16 (sixteen nodes): 1.28 vs 1.32 ms for one work-group per frame.
 template <typename TI, int CPL, bool FRAMES, bool NT>
 __global__ __launch_bounds__(256) void k_row_short(const Params p) {
   if (blockIdx.x == 0)  // the flags the node-weight kernel of this call sets
     for (int i = threadIdx.x; i < p.B; i += blockDim.x) p.xflag[i] = 0;
   const int l16 = threadIdx.x & 15;
   if constexpr (FRAMES) {
-    const int b = (int)(blockIdx.x / (uint32_t)p.Tmax);
-    const int t = (int)(blockIdx.x - (uint32_t)b * (uint32_t)p.Tmax);
+    const uint32_t nc = ((uint32_t)p.U1max + 15u) >> 4;  // sixteen-row pieces per frame
+    const uint32_t f = blockIdx.x / nc;
+    const int c = (int)(blockIdx.x - f * nc);
+    const int b = (int)(f / (uint32_t)p.Tmax);
+    const int t = (int)(f - (uint32_t)b * (uint32_t)p.Tmax);
     const int64_t T64 = p.Tlen[b], U64 = p.Ulen[b];
-    if (!utt_dims_ok(p, T64, U64) || t >= (int)T64) return;
-    const int nrows = (int)U64 + 1;
-    for (int u0 = 0; u0 < nrows; u0 += 16) {
-      const int u = u0 + (int)(threadIdx.x >> 4);
-      row_short_task<TI, CPL, NT>(p, b, t, u, u < nrows, l16);
-    }
+    if (!utt_dims_ok(p, T64, U64) || t >= (int)T64 || 16 * c > (int)U64) return;
+    const int u = 16 * c + (int)(threadIdx.x >> 4);
+    row_short_task<TI, CPL, NT>(p, b, t, u, u <= (int)U64, l16);
   } else {
     const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
     const uint32_t nodes = (uint32_t)p.B * per;
@@ -733,38 +734,60 @@ __device__ __forceinline__ NodeGrad node_grad(const Params& p, int b, int t, int
   return g;
 }
 
-// Gradient of short rows (as k_row_short: a quarter wave per row, sixteen consecutive
-// nodes per block, the blocks in reverse order), for logits and gradient rows with the
-// same address modulo 16 bytes.  Each quarter computes its node's coefficients
-// (node_grad), and the first block reduces the loss.  The chunks are counted from the gradient row's 128-byte line, so each
+// Gradient of short rows (as k_row_short: a quarter wave per row; FRAMES, up to 256
+// labels: one work-group per sixteen rows of a frame, pieces outside the utterance leave
+// at once when the lattice launch has zeroed the padding rows, else sixteen consecutive
+// nodes per work-group; the work-groups in reverse order), for logits and gradient rows
+// with the same address modulo 16 bytes.  Each quarter computes its node's coefficients
+// (node_grad), and the first work-group reduces the loss.  B16 T400 U1max 101 V1025 fp16:
+// 218 us with frame pieces, 242 us with sixteen consecutive nodes.  The chunks are counted from the gradient row's 128-byte line, so each
 // store instruction writes whole lines (16 lanes x 16 bytes, line-aligned) except at the
 // row's ends; the logits are read at the same offsets.  Whole chunks inside the row are
 // stored as 16-byte nontemporal stores, the row's first and last chunk element by element.
 // The blank and label columns are then overwritten by the lane that stored their chunk
 // (same thread, so the element store lands after the chunk store).
-template <typename TI, int CPL>
+template <typename TI, int CPL, bool FRAMES>
 __global__ __launch_bounds__(256) void k_grad_short(const Params p) {
   constexpr int EPC = TI::kEpc;
   using ET = typename TI::T;
   // the loss of the batch (the lattice has finished every log P), unless the call writes none
   if (p.loss && blockIdx.x == 0 && threadIdx.x == 0) reduce_loss(p);
   const int l16 = threadIdx.x & 15;
-  const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
-  const uint32_t nodes = (uint32_t)p.B * per;
-  // nodes in reverse order: the row-statistics pass ended on the last rows
-  const uint32_t n0 = (gridDim.x - 1u - blockIdx.x) * 16u;
-  const uint32_t node = n0 + (threadIdx.x >> 4);
-  const uint32_t nd = min(node, nodes - 1u);
-  const uint32_t b = fdiv(nd, p.fd_tu1);
-  const uint32_t rem = nd - b * per;
-  const int t = (int)fdiv(rem, p.fd_u1);
-  const int u = (int)(rem - (uint32_t)t * (uint32_t)p.U1max);
+  // work-groups in reverse order: the row-statistics pass ended on the last rows
+  const uint32_t blk = gridDim.x - 1u - blockIdx.x;
+  uint32_t b;
+  int t, u;
+  bool in;
+  RowLens ln;
+  if constexpr (FRAMES) {
+    const uint32_t nc = ((uint32_t)p.U1max + 15u) >> 4;
+    const uint32_t f = blk / nc;
+    const int c = (int)(blk - f * nc);
+    b = f / (uint32_t)p.Tmax;
+    t = (int)(f - b * (uint32_t)p.Tmax);
+    u = 16 * c + (int)(threadIdx.x >> 4);
+    in = u < p.U1max;
+    ln = RowLens{p.Tlen[b], p.Ulen[b]};
+    // a piece outside the utterance's lattice: its rows are zeroed by the lattice launch
+    if (p.zrows && (!utt_dims_ok(p, ln.T, ln.U) || t >= (int)ln.T || 16 * c > (int)ln.U)) return;
+  } else {
+    const uint32_t per = (uint32_t)p.Tmax * (uint32_t)p.U1max;
+    const uint32_t nodes = (uint32_t)p.B * per;
+    const uint32_t n0 = blk * 16u;
+    const uint32_t node = n0 + (threadIdx.x >> 4);
+    const uint32_t nd = min(node, nodes - 1u);
+    b = fdiv(nd, p.fd_tu1);
+    const uint32_t rem = nd - b * per;
+    t = (int)fdiv(rem, p.fd_u1);
+    u = (int)(rem - (uint32_t)t * (uint32_t)p.U1max);
+    in = node < nodes;
+    ln = row_lens(p, n0, nodes, b);
+  }
   const int ok = p.uok[b];  // an ok utterance has valid lengths
-  const RowLens ln = row_lens(p, n0, nodes, b);
   const bool inside = utt_dims_ok(p, ln.T, ln.U) && t < (int)ln.T && u <= (int)ln.U;
-  const bool valid = node < nodes && ok && inside;
+  const bool valid = in && ok && inside;
   // rows outside the utterance's lattice are skipped when the lattice launch has zeroed them
-  const bool write = node < nodes && (inside || p.zrows == 0);
+  const bool write = in && (inside || p.zrows == 0);
   const int V = p.V;
   // the node's coefficients from the lattice (every lane of the quarter takes part)
   const NodeGrad ng = node_grad(p, (int)b, t, u, (int)ln.T, (int)ln.U, l16, valid);
@@ -851,17 +874,17 @@ constexpr int kShortRowChunks = 256;
 template <typename TI>
 hipError_t launch_short_rows(const Params& p, bool aligned, hipStream_t st, int which, int cpl) {
   const int64_t nodes = (int64_t)p.B * p.Tmax * p.U1max;
-  // row statistics: one work-group per frame (up to 256 labels) or sixteen nodes; gradient:
-  // sixteen nodes per work-group
-  const bool frames = which == 0 && p.U1max <= 256;
-  const dim3 grid((unsigned)(frames ? (int64_t)p.B * p.Tmax : (nodes + 15) / 16));
+  // one work-group per sixteen rows of a frame (up to 256 labels) or per sixteen nodes
+  const bool frames = p.U1max <= 256;
+  const dim3 grid((unsigned)(frames ? (int64_t)p.B * p.Tmax * ((p.U1max + 15) / 16) : (nodes + 15) / 16));
 #define TDT_SR(N)                                                                                 \
   case N:                                                                                         \
-    if (frames && p.rows_nt) hipLaunchKernelGGL((k_row_short<TI, N, true, true>), grid, dim3(256), 0, st, p);        \
-    else if (frames) hipLaunchKernelGGL((k_row_short<TI, N, true, false>), grid, dim3(256), 0, st, p);              \
+    if (which == 0 && frames && p.rows_nt) hipLaunchKernelGGL((k_row_short<TI, N, true, true>), grid, dim3(256), 0, st, p); \
+    else if (which == 0 && frames) hipLaunchKernelGGL((k_row_short<TI, N, true, false>), grid, dim3(256), 0, st, p); \
     else if (which == 0 && p.rows_nt) hipLaunchKernelGGL((k_row_short<TI, N, false, true>), grid, dim3(256), 0, st, p); \
-    else if (which == 0) hipLaunchKernelGGL((k_row_short<TI, N, false, false>), grid, dim3(256), 0, st, p);         \
-    else hipLaunchKernelGGL((k_grad_short<TI, N>), grid, dim3(256), 0, st, p);                    \
+    else if (which == 0) hipLaunchKernelGGL((k_row_short<TI, N, false, false>), grid, dim3(256), 0, st, p); \
+    else if (frames) hipLaunchKernelGGL((k_grad_short<TI, N, true>), grid, dim3(256), 0, st, p); \
+    else hipLaunchKernelGGL((k_grad_short<TI, N, false>), grid, dim3(256), 0, st, p); \
     break;
   switch (cpl) {
     TDT_SR(1) TDT_SR(2) TDT_SR(3) TDT_SR(4) TDT_SR(5) TDT_SR(6) TDT_SR(7) TDT_SR(8)

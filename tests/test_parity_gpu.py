@@ -211,6 +211,25 @@ def test_separate_gradient_buffers_unaligned_path():
     check_grads(gt, gdd, orc, case.joint.dtype)
 
 
+def test_padding_rows_written_by_gradient_pass():
+    """Gradient views with the logits' strides (rows co-aligned, the short-row gradient
+    pass) in two separate buffers, so not one joint tensor: the lattice launch zeroes no
+    padding rows and the gradient pass writes them itself (frame pieces outside the
+    utterances included).  Every element of both views is written (NaN canaries disappear)
+    and the result is bitwise that of the joint-buffer run."""
+    case = config_case(3, device="cuda")
+    loss_j, g_j, gd_j, _ = gpu_run(case)
+    snap = (loss_j.clone(), g_j.clone(), gd_j.clone())
+    n = case.joint.numel()
+    g = torch.full((n,), float("nan"), dtype=case.joint.dtype, device="cuda").as_strided(
+        case.tok.shape, case.tok.stride(), 0)
+    gd = torch.full((n,), float("nan"), dtype=case.joint.dtype, device="cuda").as_strided(
+        case.dur.shape, case.dur.stride(), 0)
+    loss, gt, gdd, _ = gpu_run(case, grads=(g, gd))
+    assert not torch.isnan(gt).any().item() and not torch.isnan(gdd).any().item()
+    assert torch.equal(loss, snap[0]) and torch.equal(gt, snap[1]) and torch.equal(gdd, snap[2])
+
+
 def test_padding_canary_and_determinism():
     """Every element of the gradient views is written (NaN canaries disappear) and two runs
     are bitwise identical."""
