@@ -152,8 +152,11 @@ int tdt_loss_fwd_bwd(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, in
 /*
  * Launch sequence, all on `stream`, in order: row partials (log-sum-exp partials of the
  * token-logit rows), node weights, lattice (alpha and beta sweeps), coefficients (which
- * also reduce the loss), gradient pass.  A forward-only call runs a loss-reduction
- * kernel in place of the coefficients and the gradient pass.
+ * also reduce the loss), gradient pass.  For rows of at most 256 16-byte chunks whose
+ * logits and gradient rows share their address modulo 16 bytes, the gradient pass
+ * computes the coefficients itself and reduces the loss (no coefficient kernel).  A
+ * forward-only call runs a loss-reduction kernel in place of the coefficients and the
+ * gradient pass.
  *
  * Same as tdt_loss_fwd_bwd, and additionally records caller-created events (hipEvent_t
  * handles on the device of `stream`; NULL entries are skipped) on `stream`, for tools
@@ -161,9 +164,9 @@ int tdt_loss_fwd_bwd(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, in
  *   num_events == 4: events[0] before the first kernel, [1] after the last one, [2]
  *     right before the gradient pass and [3] right after it;
  *   num_events == 7: events[0] before the row partials, [1] after them, [2] after the
- *     node weights, [3] after the lattice, [4] after the coefficients, [5] after the
- *     gradient pass, [6] after the loss reduction kernel (forward only; with gradients
- *     [6] directly follows [5]).
+ *     node weights, [3] after the lattice, [4] after the coefficients (directly after [3]
+ *     when the gradient pass computes them), [5] after the gradient pass, [6] after the
+ *     loss reduction kernel (forward only; with gradients [6] directly follows [5]).
  * Any other count (or events == NULL) returns TDT_ERR_INVALID_ARGUMENT.
  */
 int tdt_loss_fwd_bwd_timed(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V,
@@ -178,8 +181,8 @@ int tdt_loss_fwd_bwd_timed(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_m
 /*
  * Gradient of a loss computed earlier by a forward-only tdt_loss_fwd_bwd call (both
  * gradient pointers NULL), for autograd-style use where the upstream gradient is known
- * only later.  Stream-ordered on `stream`; runs the coefficient kernel and the gradient
- * pass (the last two kernels of the launch sequence above) on the state the forward call
+ * only later.  Stream-ordered on `stream`; runs the coefficient kernel (when the launch
+ * sequence above has one) and the gradient pass on the state the forward call
  * left in `workspace`, so between the two calls the workspace must be untouched, and
  * logits, dur_logits, labels, the two length arrays and every size, durations, blank,
  * sigma and reduction must be the same (contents included).  Nothing is checked on the
