@@ -195,3 +195,18 @@ def test_link_waits_give_up(dm, U, monkeypatch):
     the utterance to finish) must still give the oracle's loss and gradients."""
     monkeypatch.setenv("TDT_LINK_SPIN_LIMIT", "1")
     _parity(_case(dm, U, "f32", seed=500 + U + dm).to("cuda"))
+
+
+@pytest.mark.parametrize("U", [30, 150])
+def test_sixteen_durations(U):
+    """The most durations a call takes (16, values up to 16): the short-row gradient pass
+    gives each of its 16 lanes per node one duration's two moves, and the node weights
+    write every slot pair of the duration bound 16; one tile and two linked tiles."""
+    durations = list(range(15)) + [16]
+    case = make_case(2, [40, 33], [U, U - 7], 13, durations, "bf16" if U > 100 else "f32", seed=400 + U,
+                     sigma=0.05, reduction="mean", name=f"d16_U{U}")
+    loss, gt, gd, st = gpu_run(case.to("cuda"))
+    orc = oracle_run(case)
+    check_loss(loss, orc, case.reduction, case.joint.dtype)
+    check_grads(gt, gd, orc, case.joint.dtype)
+    assert st.cpu().tolist() == orc["status"].tolist()
