@@ -23,7 +23,7 @@ __device__ __forceinline__ float load_tok(const Params& p, int64_t off) {
 hipError_t launch_rows_f32(const Params& p, bool aligned, hipStream_t st, int which);
 hipError_t launch_rows_f16(const Params& p, bool aligned, hipStream_t st, int which);
 hipError_t launch_rows_bf16(const Params& p, bool aligned, hipStream_t st, int which);
-// which: 0 node weights, 1 lattice, 2 coefficients + loss, 3 loss only
+// which: 0 node weights, 1 lattice, 2 coefficients + loss (long rows), 3 loss only
 hipError_t launch_lattice_side(const Params& p, int which, hipStream_t st);
 
 }  // namespace tdt

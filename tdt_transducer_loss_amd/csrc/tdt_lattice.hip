@@ -1329,7 +1329,8 @@ __global__ __launch_bounds__(128) void k_cols(const Params p) {
 }
 
 // ------------------------------------------------------------------------------------
-// Posteriors and the per-node record of the gradient pass:
+// Posteriors and the per-node record of the long-row gradient pass (the short-row gradient
+// pass computes the same numbers itself, a quarter wave per node: node_grad):
 //   gamma(e) = alpha(n) W(e) beta(dest e) / P,   O(n) = sum over moves out of n,
 //   c_blank, c_label = sums over blank / label moves, c_dur(d) = moves of duration d,
 //   grad h_blank = w (O softmax(h)_blank - c_blank), grad h_y = w (O softmax(h)_y - c_label),
