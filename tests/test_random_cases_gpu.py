@@ -8,7 +8,8 @@ The draws straddle the thresholds the library switches on:
 - duration sets up to 16 (the kernel bounds 4, 8 and 16), unsorted, with or without 0;
 - every reduction, sigma, the blank anywhere in the vocabulary (labels may equal it);
 - ragged lengths (padding rows), and gradient buffers co-aligned with the logits (the
-  short-row passes) or in separate contiguous buffers (the per-element path).
+  short-row passes) or in separate contiguous buffers (the per-element path);
+- and, separately, long label sequences (65 to 1500 labels: linked columns, bands).
 """
 import random
 
@@ -69,6 +70,38 @@ def test_random_case(i):
         grads = (torch.full(gcase.tok.shape, float("nan"), dtype=gcase.joint.dtype, device="cuda"),
                  torch.full(gcase.dur.shape, float("nan"), dtype=gcase.joint.dtype, device="cuda"))
     loss, gt, gd, st = gpu_run(gcase, grads=grads)
+    orc = oracle_run(case)
+    check_loss(loss, orc, case.reduction, case.joint.dtype)
+    check_grads(gt, gd, orc, case.joint.dtype)
+    assert st.cpu().tolist() == orc["status"].tolist()
+
+
+N_LONG = 16
+
+
+def _draw_long(i):
+    """Long label sequences (65 to 1500 labels over few frames, duration 0 always allowed so
+    that more labels than frames align): linked columns (durations up to 8), bands (16)."""
+    r = random.Random(7000 + i)
+    dtype = r.choice(["f32", "bf16"])
+    V = r.randint(5, 40)
+    B = r.randint(1, 4)
+    T = [r.randint(4, 60) for _ in range(B)]
+    Umax = r.choice([r.randint(257, 600), r.randint(900, 1500)])
+    U = [r.randint(Umax // 2, Umax) for _ in range(B)]
+    maxd = r.choice([2, 4, 8, 16])
+    durs = [0] + r.sample(range(1, maxd + 1), r.randint(1, min(maxd, 6)))
+    r.shuffle(durs)
+    red = r.choice(["none", "sum", "mean", "mean_batch", "mean_volume"])
+    name = f"long{i}_{dtype}_U{Umax}_d{max(durs)}_{red}"
+    return make_case(B, T, U, V, durs, dtype, scale=r.choice([1.0, 2.0]), sigma=r.choice([0.0, 0.05]),
+                     reduction=red, seed=7000 + i, name=name)
+
+
+@pytest.mark.parametrize("i", range(N_LONG))
+def test_random_long_labels(i):
+    case = _draw_long(i)
+    loss, gt, gd, st = gpu_run(case.to("cuda"))
     orc = oracle_run(case)
     check_loss(loss, orc, case.reduction, case.joint.dtype)
     check_grads(gt, gd, orc, case.joint.dtype)
