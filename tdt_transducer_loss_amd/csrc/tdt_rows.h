@@ -640,8 +640,11 @@ __global__ __launch_bounds__(256) void k_row_short(const Params p) {
 // lane i < D takes duration index i (value d) and the posteriors of the two moves of
 // duration d out of n, blank (d >= 1, to (t + d, u)) and label (to (t + d, u + 1)),
 //   gamma(e) = alpha(n) W(e) beta(dest e) / P
-// (W: the plain weight the lattice read, or, for an utterance whose weights left the
-// plain range, the weight rebuilt in extended range from its log-domain ingredients).
+// (W rebuilt from the node's log-domain ingredients: exp(lb + lambda_d) in float64, the
+// plain weight the lattice read up to rounding, or in extended range for an utterance
+// whose weights left the plain range; rebuilding takes two exponentials per lane instead
+// of two gathers from the weight blocks: B2 T1000 U1500 V1025 bf16 gradient pass 2.49 ->
+// 2.30 ms).
 // Sums over the quarter give c_blank, c_label and O = c_blank + c_label (every move out
 // of n); then
 //   grad h_blank = w (O softmax(h)_blank - c_blank),  grad h_y = w (O softmax(h)_y - c_label),
@@ -675,29 +678,19 @@ __device__ __forceinline__ NodeGrad node_grad(const Params& p, int b, int t, int
     const Ext a = xrec_get(p.ar, pos);
     const double rP = 1.0 / p.pm[b];
     const int Pe = p.pe[b];
-    // the node's plain weights: slot pairs len(k) + 3 entries apart in its diagonal's block
-    const int k = t + u, len = diag_len(p, k);
-    const double* pw =
-        plain ? p.pw + ((int64_t)b * pw_utt_entries(p.NP, p.box, p.KD) + pw_block(p, k) + (u - diag_ulo(p, k))) * 2
-              : nullptr;
-    const int64_t pstride = (int64_t)(len + 3) * 2;  // doubles between slot pairs
     if (d >= 1) {
       Ext bt = ext_zero();
       if (t + d < T) bt = xrec_get(p.br, node_pos(p, b, t + d, u));
       else if (t + d == T && u == U) bt = ext_one();
-      const int sl = d - 1;
-      const double wp = plain ? pw[(sl >> 1) * pstride + (sl & 1)] : 0.0;
       if (bt.m != 0.0) {
-        const Ext w = plain ? Ext{wp, 0} : ext_exp(lb + lam);
+        const Ext w = plain ? Ext{exp(lb + lam), 0} : ext_exp(lb + lam);
         gb = ext_to_double(Ext{a.m * w.m * bt.m * rP, a.e + w.e + bt.e - Pe});
       }
     }
-    const int sl = p.DM + d;
-    const double wp = plain ? pw[(sl >> 1) * pstride + (sl & 1)] : 0.0;
     if (u < U && t + d < T) {
       const Ext bt = xrec_get(p.br, node_pos(p, b, t + d, u + 1));
       if (bt.m != 0.0) {
-        const Ext w = plain ? Ext{wp, 0} : ext_exp(ly + lam);
+        const Ext w = plain ? Ext{exp(ly + lam), 0} : ext_exp(ly + lam);
         gy = ext_to_double(Ext{a.m * w.m * bt.m * rP, a.e + w.e + bt.e - Pe});
       }
     }
