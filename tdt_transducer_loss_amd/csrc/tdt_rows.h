@@ -20,12 +20,12 @@
 namespace tdt {
 
 constexpr int kWavesPerBlock = 4;   // 256-thread work-groups
-// Grid of the persistent row-statistics pass: about two (node, segment) tasks per wave,
-// at most 12288 blocks (48K waves).  Measured at B4 T200 U40 V8193 bf16 (98,400 tasks):
-// 4096 blocks 109 us, 12288 (two tasks per wave) 102 us, 16384 (one or two) 118 us,
-// 32768 (one) 109 us.
-constexpr int kRowStatBlocks = 12288;
-constexpr int kRowStatTasksPerWave = 2;
+// Grid of the persistent row-statistics pass: one (node, segment) task per wave, at most
+// 65536 blocks (256K waves; larger batches loop).  Measured row pass, B4 T200 U40 V8193
+// bf16 (98,400 tasks) / fp32 (164,000 tasks): one task per wave 83.0 / 157.0 us; two
+// 84.5 / 161.7; three 87.5 / 163.9; two with at most 12288 blocks 84.6 / 177.0.
+constexpr int kRowStatBlocks = 65536;
+constexpr int kRowStatTasksPerWave = 1;
 static_assert(kRowStatBlocks % 8 == 0, "whole rounds of the eight XCDs");
 
 template <typename TI>
@@ -907,8 +907,9 @@ hipError_t launch_rows_t(const Params& p, bool aligned, hipStream_t st, int whic
   const int64_t nodes = (int64_t)p.B * p.Tmax * p.U1max;  // both passes walk the padded rows
   const int64_t waves = nodes * (which == 0 ? p.nseg : p.gnseg);
   int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (which == 0) {  // persistent row statistics
-    blocks = (waves + kRowStatTasksPerWave * kWavesPerBlock - 1) / (kRowStatTasksPerWave * kWavesPerBlock);
+  if (which == 0) {  // persistent row statistics (the two-task form: two tasks per wave)
+    const int64_t tpw = nch <= 4 ? 2 : kRowStatTasksPerWave;
+    blocks = (waves + tpw * kWavesPerBlock - 1) / (tpw * kWavesPerBlock);
     if (blocks > kRowStatBlocks) blocks = kRowStatBlocks;
   }
   const dim3 grid((unsigned)blocks);
