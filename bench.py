@@ -175,8 +175,8 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the loss shards by utterance with no exchange but a scalar all-reduce, not built here.",
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the loss shards by utterance with no exchange but a scalar all-reduce, which is not implemented.",
               file=sys.stderr)
         return 2
 

@@ -69,7 +69,7 @@ typedef enum {
 #define TDT_UTT_BAD_LABEL 4        /* a label y_1..y_U outside [0, V) */
 #define TDT_UTT_INFEASIBLE 8       /* no alignment exists */
 
-/* Limits of this build: 1 <= num_durations <= 16, duration values in [0, 16] with at
+/* Limits of the library: 1 <= num_durations <= 16, duration values in [0, 16] with at
  * least one > 0, T_max and U1_max below 2^24 with T_max * U1_max below 2^27, and fewer
  * than 2^31 (node, row segment) pairs per call, a row segment being up to 512 16-byte
  * chunks of a logits row (beyond these: TDT_ERR_UNSUPPORTED).  There is no other limit on
