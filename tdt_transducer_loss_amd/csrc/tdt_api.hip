@@ -309,12 +309,13 @@ int prepare(int32_t dtype, int64_t B, int64_t T_max, int64_t U1_max, int64_t V, 
   const double row_bytes = (double)(V + num_durations) * (double)elt;
   const double padded_nodes = (double)B * (double)T_max * (double)U1_max;
   p.rows_nt = padded_nodes * row_bytes > 2.0 * tdt::kLastLevelCacheBytes ? 1 : 0;
-  // long rows: every row but those of the last 256 MB is streamed past the last-level cache;
-  // the gradient pass, walking the rows in reverse, starts on the ones kept there (B4 T200
-  // U40 V8193 bf16: 0.328 -> 0.307 ms per step, row pass 96 -> 85 us and gradient pass
-  // 160 -> 151 us; keeping 192 / 128 / 320 MB: 0.306 / 0.314 / 0.317 ms; fp32 0.591 ->
-  // 0.568 ms)
-  const double keep = tdt::kLastLevelCacheBytes / row_bytes;
+  // long rows: every row but those of the last 224 MB (7/8 of the last-level cache) is
+  // streamed past it; the gradient pass, walking the rows in reverse, starts on the ones
+  // kept there (B4 T200 U40 V8193 bf16: 0.328 -> 0.307 ms per step when first measured,
+  // row pass 96 -> 85 us and gradient pass 160 -> 151 us; with one row task per wave,
+  // keeping 192 / 224 / 256 / 288 MB: 0.304 / 0.3003-0.3008 / 0.3027-0.3030 / 0.313 ms,
+  // fp32 0.552 / 0.549 / 0.548 / 0.551 ms)
+  const double keep = 0.875 * tdt::kLastLevelCacheBytes / row_bytes;
   p.nt_nodes = padded_nodes > keep ? (uint32_t)(padded_nodes - keep) : 0u;
   p.spin = 1 << 20;
   if (const char* e = getenv("TDT_LINK_SPIN_LIMIT")) {  // tests: force the waits to give up
